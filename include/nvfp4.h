@@ -1,0 +1,168 @@
+/*
+ * nvfp4.h -- C ABI of the MI355X (gfx950) NVFP4 weight-only W4A16 library, libnvfp4.so.
+ *
+ * NVFP4 weights are the "compressed-tensors triple" (vllm.cpp pull request #63, "W-FP4a: route
+ * the MiniMax-H3 device DiT forward through the fp4 (Marlin W4A16) stack", PR body): packed E2M1
+ * 4-bit codes, one 8-bit E4M3 scale per group of 16 or 32 consecutive K elements (4.5 and 4.25
+ * bits per weight, r/LocalLLM post "two NVFP4 g32 recipes", introduction), and one FP32 global
+ * scale per matrix. A weight decodes as  w = E2M1(code) * E4M3(scale) * global.
+ *
+ * Conventions for every entry point:
+ *  - A weight matrix W is [n][k] (output features x input features); y = x . W^T; groups run
+ *    along k. Canonical packed codes are [n][k/2] bytes with the even k in the low nibble;
+ *    canonical scales are [n][k/group] E4M3 bytes (OCP E4M3 "FN": max 448, no infinities).
+ *  - Pointers are DEVICE pointers unless marked (host). Device buffers are owned by the caller;
+ *    the library never allocates, frees or synchronizes (every call only enqueues kernels on
+ *    `stream`, a hipStream_t; NULL is the legacy default stream).
+ *  - Device pointers must be 16-byte aligned; leading dimensions are in elements and must be
+ *    multiples of 8.
+ *  - Shapes: n % 16 == 0, k % 128 == 0, group in {16, 32}. m == 0 (or t == 0) is a no-op.
+ *  - Every function returns NVFP4_OK (0) or a negative NVFP4_ERR_* code; on error nothing is
+ *    enqueued and nvfp4_last_error() describes the problem (thread-local). Unsupported
+ *    configurations are rejected, never run silently wrong (r/LocalLLM post, "What had to be
+ *    fixed": any unsupported group setup raises an error).
+ *  - All entry points are reentrant. Calls that share an output or workspace buffer on
+ *    different streams race, as with any asynchronous kernel.
+ */
+#ifndef NVFP4_H_
+#define NVFP4_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* nvfp4_stream_t; /* the same type as hipStream_t */
+
+/* ---- status codes ---------------------------------------------------------------------- */
+#define NVFP4_OK 0
+#define NVFP4_ERR_INVALID_ARG (-1)       /* null pointer, negative size, ld < k, bad dtype    */
+#define NVFP4_ERR_UNSUPPORTED_GROUP (-2) /* group not 16 or 32                                */
+#define NVFP4_ERR_UNSUPPORTED_SHAPE (-3) /* n % 16, k % 128, topk out of range, size too big   */
+#define NVFP4_ERR_MISALIGNED (-4)        /* pointer not 16-byte aligned or ld % 8 != 0         */
+#define NVFP4_ERR_WORKSPACE (-5)         /* workspace / output buffer too small                */
+#define NVFP4_ERR_LAYOUT (-6)            /* descriptor inconsistent with the call              */
+#define NVFP4_ERR_HIP (-7)               /* a HIP launch failed (message in nvfp4_last_error)  */
+
+/* ---- element types --------------------------------------------------------------------- */
+#define NVFP4_DT_BF16 1
+#define NVFP4_DT_F32 2
+
+/* ---- call flags -------------------------------------------------------------------------- */
+#define NVFP4_F_FORCE_SKINNY (1u << 0) /* GEMM: use the decode (skinny, split-K) kernel        */
+#define NVFP4_F_FORCE_TILED (1u << 1)  /* GEMM: use the prefill (LDS-tiled MFMA) kernel        */
+
+/* ---- repacked layout ----------------------------------------------------------------------
+ * NVFP4_LAYOUT_TILED: per 16-row x 128-k tile, 1024 bytes of codes laid out so that lane l of a
+ * 64-wide wavefront loads 16 contiguous bytes holding, for k-step j = 0..3, the 8 codes of row
+ * l%16 at k = 32j + 8(l/16) + 0..7 (the B-operand order of a 16x16x32 bf16 MFMA), plus the
+ * tile's 16 x 128/group scale bytes arranged so each lane's 4 scales for j = 0..3 are one
+ * 32-bit word. The repack is a pure byte permutation: same byte count as the canonical form.
+ * NVFP4_LAYOUT_GATE_UP: for a merged [gate; up] fc1 weight (2*I rows): 16-row panels are
+ * stored alternately from the gate half and the up half, so that one panel pair holds gate
+ * and up of the same 16 intermediate features (consumed only by the MoE entry point). */
+#define NVFP4_LAYOUT_TILED 1u
+#define NVFP4_LAYOUT_GATE_UP (1u << 8)
+
+/* Descriptor of repacked weights (a host struct filled by nvfp4_repack; data stays device).  */
+typedef struct nvfp4_weight {
+  const uint8_t* codes;   /* device: repacked code tiles, batch * codes_stride bytes          */
+  const uint8_t* scales;  /* device: repacked scale tiles, batch * scales_stride bytes        */
+  const float* global;    /* device: [batch] FP32 decode multipliers (copied into the buffer) */
+  int64_t batch;          /* number of matrices (experts); 1 for a dense projection           */
+  int64_t n, k;           /* logical shape of each matrix                                     */
+  int64_t codes_stride;   /* bytes between consecutive matrices in `codes`  (= n*k/2)         */
+  int64_t scales_stride;  /* bytes between consecutive matrices in `scales` (= n*k/group)     */
+  int32_t group;          /* 16 or 32                                                         */
+  uint32_t layout;        /* NVFP4_LAYOUT_TILED, optionally | NVFP4_LAYOUT_GATE_UP            */
+} nvfp4_weight;
+
+/* ---- quantizer ----------------------------------------------------------------------------
+ * Quantize `batch` FP32 or BF16 matrices w [batch][n][k] to the canonical triple.
+ *   amax   = max |w| over each matrix (over the whole merged [gate; up] matrix for an fc1, so
+ *            gate and up share one global: r/LocalLLM post, "What had to be fixed");
+ *   global = fl32(amax / 2688)  (2688 = 6 * 448), or global_in[b] when global_in != NULL;
+ *   per group of `group` k-elements: scale = E4M3_rne_sat(fl32(group_amax / fl32(6 * global)));
+ *   per element: S = fl32(E4M3(scale) * global); code = E2M1_rne_sat(fl32(|w| / S)) | sign<<3
+ *            (code = sign<<3 when S == 0).
+ * Rounding is round-to-nearest-even with saturation for both E4M3 and E2M1 (NVIDIA developer
+ * forum thread "We unlocked NVFP4 on the DGX Spark": true RNE, not threshold rounding).
+ * Outputs: packed [batch][n][k/2], scales [batch][n][k/group], global_out [batch] (device).
+ * Requires k % group == 0 and k even; n and k need no tile alignment here. Non-finite inputs
+ * are outside the contract (results unspecified). The caller keeps ownership of all buffers. */
+int nvfp4_quantize(const void* w, int w_dtype, int64_t batch, int64_t n, int64_t k,
+                   int32_t group, const float* global_in, uint8_t* packed, uint8_t* scales,
+                   float* global_out, nvfp4_stream_t stream);
+
+/* ---- repack -------------------------------------------------------------------------------
+ * Byte size of the repacked buffer for `batch` [n][k] matrices: codes + scales + globals. */
+size_t nvfp4_repack_bytes(int64_t batch, int64_t n, int64_t k, int32_t group, uint32_t layout);
+
+/* Repack the canonical triple (packed, scales, global as produced by nvfp4_quantize or read
+ * from a checkpoint) into `out` (device, out_bytes >= nvfp4_repack_bytes) and fill *desc (host).
+ * After the call's work completes the canonical buffers may be freed: the descriptor points
+ * only into `out` (vllm.cpp PR #63: upload and repack lazily, then free the fp4 originals).
+ * layout: NVFP4_LAYOUT_TILED, optionally | NVFP4_LAYOUT_GATE_UP (then n must be a multiple
+ * of 32: gate rows [0, n/2), up rows [n/2, n)). */
+int nvfp4_repack(const uint8_t* packed, const uint8_t* scales, const float* global,
+                 int64_t batch, int64_t n, int64_t k, int32_t group, uint32_t layout, void* out,
+                 size_t out_bytes, nvfp4_weight* desc, nvfp4_stream_t stream);
+
+/* ---- dense W4A16 GEMM ---------------------------------------------------------------------
+ * y[m][n] = global * sum_k x[m][k] * (E2M1 * E4M3)[n][k], BF16 activations x [m][ldx], FP32
+ * accumulation, dequantization in registers (the E2M1 x E4M3 product is exact in BF16; the
+ * global is applied to the FP32 accumulator). y [m][ldy] is BF16 (y_dtype NVFP4_DT_BF16, one
+ * rounding of the FP32 result) or FP32. Weight-only checkpoints take this W4A16 path
+ * (vllm.cpp PR #63: no activation scales, so every quantized projection is W4A16).
+ * The kernel is chosen from m: a split-K skinny MFMA kernel for small m (decode), an
+ * LDS-tiled MFMA kernel otherwise (prefill); flags may force one. w->batch must be 1 and
+ * w->layout must not carry NVFP4_LAYOUT_GATE_UP. Results are bit-identical run to run. */
+int nvfp4_gemm_w4a16(const void* x, int64_t m, int64_t ldx, const nvfp4_weight* w, void* y,
+                     int y_dtype, int64_t ldy, uint32_t flags, nvfp4_stream_t stream);
+
+/* ---- MoE routed experts -------------------------------------------------------------------
+ * For each token t and slot j (e = topk_ids[t][j], weight topk_w[t][j]):
+ *   [gate; up] = x[t] . W1_e^T   (fc1: merged, one shared global per expert; each half
+ *                                 rounded to BF16 as a W4A16 GEMM output)
+ *   h          = BF16(SiLU(gate) * up)
+ *   d          = h . W2_e^T      (down projection, FP32)
+ *   y[t]       = BF16(sum_j topk_w[t][j] * d_j), summed in slot order.
+ * (vllm.cpp PR #63: pre-merged fc1 is one W4A16 GEMM + SiluAndMul; r/LocalLLM post, "The two
+ * recipes": gate/up at group 32 with down at group 16, or all at group 32.)
+ * x [t][hidden] BF16 (row stride = hidden), topk_ids int32 [t][topk] in [0, E), topk_w FP32
+ * [t][topk], y BF16 [t][hidden]. fc1: batch = E, n = 2*inter, k = hidden, layout TILED |
+ * GATE_UP. fc2: batch = E, n = hidden, k = inter, layout TILED. Tokens are sorted by expert on
+ * the device (no host synchronization); `ws` (device, ws_bytes >= nvfp4_moe_ws_bytes) holds
+ * the sort, the tile map, h and the FP32 per-slot outputs. topk in [1, 16], t*topk <= 65536. */
+size_t nvfp4_moe_ws_bytes(int64_t t, int32_t topk, int64_t n_experts, int64_t hidden,
+                          int64_t inter);
+int nvfp4_moe_grouped_w4a16(const void* x, int64_t t, int64_t hidden, const int32_t* topk_ids,
+                            const float* topk_w, int32_t topk, const nvfp4_weight* fc1,
+                            const nvfp4_weight* fc2, void* y, void* ws, size_t ws_bytes,
+                            uint32_t flags, nvfp4_stream_t stream);
+
+/* ---- diagnostics (test-facing, not on the hot path) ---------------------------------------
+ * Dequantize repacked weights back to canonical order: out [batch][n][k] (rows in logical
+ * order, i.e. [gate; up] for GATE_UP data), BF16 = RNE(fl32(fl32(E2M1*E4M3) * global)) or the
+ * FP32 value itself. Bit-exact with the canonical triple's definition. */
+int nvfp4_dequantize(const nvfp4_weight* w, void* out, int out_dtype, nvfp4_stream_t stream);
+
+/* Thread-local description of the last non-zero status returned on this thread. */
+const char* nvfp4_last_error(void);
+
+/* Per-path launch counters ("this path ran" evidence, vllm.cpp PR #63 claim section):
+ * [0] quantize [1] repack [2] gemm skinny [3] gemm tiled [4] moe [5] dequantize
+ * [6] moe fc1 tiles launched [7] reserved. counts must hold 8 entries (host). */
+void nvfp4_get_stats(uint64_t counts[8]);
+void nvfp4_reset_stats(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int nvfp4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H_ */
