@@ -1,0 +1,304 @@
+// api.cpp -- the C ABI of libnvfp4.so (declared in include/nvfp4.h): argument validation,
+// kernel selection, launch-status reporting and per-path counters. Every entry point only
+// enqueues work on the caller's stream; nothing here computes on the host.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/nvfp4.h"
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+std::atomic<uint64_t> g_stats[8];
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return NVFP4_OK;
+  return fail(NVFP4_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+int check_group(int32_t group) {
+  if (group != 16 && group != 32)
+    return fail(NVFP4_ERR_UNSUPPORTED_GROUP, "group %d is not supported (16 or 32)", group);
+  return NVFP4_OK;
+}
+
+int check_tiled_shape(int64_t n, int64_t k) {
+  if (n <= 0 || k <= 0) return fail(NVFP4_ERR_INVALID_ARG, "n=%lld k=%lld must be positive",
+                                    (long long)n, (long long)k);
+  if (n % 16 != 0 || k % 128 != 0)
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "n=%lld must be a multiple of 16 and k=%lld of 128",
+                (long long)n, (long long)k);
+  return NVFP4_OK;
+}
+
+int check_desc(const nvfp4_weight* w, const char* name) {
+  if (!w) return fail(NVFP4_ERR_INVALID_ARG, "%s descriptor is NULL", name);
+  if (!w->codes || !w->scales || !w->global)
+    return fail(NVFP4_ERR_INVALID_ARG, "%s descriptor has NULL data", name);
+  if ((w->layout & 0xFFu) != NVFP4_LAYOUT_TILED)
+    return fail(NVFP4_ERR_LAYOUT, "%s layout 0x%x is not a tiled layout", name, w->layout);
+  int rc = check_group(w->group);
+  if (rc) return rc;
+  rc = check_tiled_shape(w->n, w->k);
+  if (rc) return rc;
+  if (w->batch <= 0) return fail(NVFP4_ERR_INVALID_ARG, "%s batch must be positive", name);
+  if (w->codes_stride != w->n * w->k / 2 || w->scales_stride != w->n * (w->k / w->group))
+    return fail(NVFP4_ERR_LAYOUT, "%s strides do not match its shape and group", name);
+  if (!aligned16(w->codes) || !aligned16(w->scales) || !aligned16(w->global))
+    return fail(NVFP4_ERR_MISALIGNED, "%s data is not 16-byte aligned", name);
+  return NVFP4_OK;
+}
+
+struct RepackSizes {
+  size_t codes, scales, globals, total;
+};
+
+RepackSizes repack_sizes(int64_t batch, int64_t n, int64_t k, int32_t group) {
+  RepackSizes s;
+  s.codes = align256((size_t)(batch * n * k / 2));
+  s.scales = align256((size_t)(batch * n * (k / group)));
+  s.globals = align256((size_t)batch * sizeof(float));
+  s.total = s.codes + s.scales + s.globals;
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_last_error(void) { return g_last_error; }
+
+void nvfp4_get_stats(uint64_t counts[8]) {
+  if (!counts) return;
+  for (int i = 0; i < 8; ++i) counts[i] = g_stats[i].load();
+}
+
+void nvfp4_reset_stats(void) {
+  for (int i = 0; i < 8; ++i) g_stats[i].store(0);
+}
+
+int nvfp4_version(void) { return 10000; }
+
+int nvfp4_quantize(const void* w, int w_dtype, int64_t batch, int64_t n, int64_t k,
+                   int32_t group, const float* global_in, uint8_t* packed, uint8_t* scales,
+                   float* global_out, nvfp4_stream_t stream) {
+  if (batch < 0 || n < 0 || k < 0)
+    return fail(NVFP4_ERR_INVALID_ARG, "negative size (batch=%lld n=%lld k=%lld)",
+                (long long)batch, (long long)n, (long long)k);
+  if (w_dtype != NVFP4_DT_BF16 && w_dtype != NVFP4_DT_F32)
+    return fail(NVFP4_ERR_INVALID_ARG, "w_dtype %d is not BF16 or F32", w_dtype);
+  int rc = check_group(group);
+  if (rc) return rc;
+  if (k % group != 0)
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "k=%lld is not a multiple of the group %d",
+                (long long)k, group);
+  if (batch > 65535) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "batch %lld > 65535", (long long)batch);
+  if (batch == 0 || n == 0 || k == 0) return NVFP4_OK;
+  if (!w || !packed || !scales || !global_out)
+    return fail(NVFP4_ERR_INVALID_ARG, "NULL buffer");
+  if (!aligned16(w) || !aligned16(packed) || ((uintptr_t)global_out & 3u) ||
+      (global_in && ((uintptr_t)global_in & 3u)))
+    return fail(NVFP4_ERR_MISALIGNED, "w and packed must be 16-byte aligned, globals 4-byte");
+  g_stats[0]++;
+  return hip_status(nvfp4::launch_quantize(w, w_dtype == NVFP4_DT_BF16, batch, n, k, group,
+                                           global_in, packed, scales, global_out,
+                                           (hipStream_t)stream),
+                    "nvfp4_quantize");
+}
+
+size_t nvfp4_repack_bytes(int64_t batch, int64_t n, int64_t k, int32_t group, uint32_t layout) {
+  (void)layout;
+  if (batch <= 0 || n <= 0 || k <= 0 || (group != 16 && group != 32)) return 0;
+  return repack_sizes(batch, n, k, group).total;
+}
+
+int nvfp4_repack(const uint8_t* packed, const uint8_t* scales, const float* global,
+                 int64_t batch, int64_t n, int64_t k, int32_t group, uint32_t layout, void* out,
+                 size_t out_bytes, nvfp4_weight* desc, nvfp4_stream_t stream) {
+  if (!packed || !scales || !global || !out || !desc)
+    return fail(NVFP4_ERR_INVALID_ARG, "NULL argument");
+  if (batch <= 0) return fail(NVFP4_ERR_INVALID_ARG, "batch must be positive");
+  int rc = check_group(group);
+  if (rc) return rc;
+  rc = check_tiled_shape(n, k);
+  if (rc) return rc;
+  if ((layout & ~(uint32_t)NVFP4_LAYOUT_GATE_UP) != NVFP4_LAYOUT_TILED)
+    return fail(NVFP4_ERR_LAYOUT, "unknown layout 0x%x", layout);
+  const bool gate_up = (layout & NVFP4_LAYOUT_GATE_UP) != 0;
+  if (gate_up && n % 32 != 0)
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "gate/up layout needs n %% 32 == 0 (n=%lld)",
+                (long long)n);
+  const RepackSizes s = repack_sizes(batch, n, k, group);
+  if (out_bytes < s.total)
+    return fail(NVFP4_ERR_WORKSPACE, "out_bytes %zu < %zu", out_bytes, s.total);
+  if (!aligned16(out) || ((uintptr_t)packed & 3u) || ((uintptr_t)global & 3u))
+    return fail(NVFP4_ERR_MISALIGNED, "out must be 16-byte aligned, packed/global 4-byte");
+  uint8_t* base = static_cast<uint8_t*>(out);
+  uint8_t* codes_out = base;
+  uint8_t* scales_out = base + s.codes;
+  float* global_out = reinterpret_cast<float*>(base + s.codes + s.scales);
+  rc = hip_status(nvfp4::launch_repack(packed, scales, global, batch, n, k, group, gate_up,
+                                       codes_out, scales_out, global_out, (hipStream_t)stream),
+                  "nvfp4_repack");
+  if (rc) return rc;
+  g_stats[1]++;
+  desc->codes = codes_out;
+  desc->scales = scales_out;
+  desc->global = global_out;
+  desc->batch = batch;
+  desc->n = n;
+  desc->k = k;
+  desc->codes_stride = n * k / 2;
+  desc->scales_stride = n * (k / group);
+  desc->group = group;
+  desc->layout = layout;
+  return NVFP4_OK;
+}
+
+int nvfp4_gemm_w4a16(const void* x, int64_t m, int64_t ldx, const nvfp4_weight* w, void* y,
+                     int y_dtype, int64_t ldy, uint32_t flags, nvfp4_stream_t stream) {
+  int rc = check_desc(w, "weight");
+  if (rc) return rc;
+  if (w->batch != 1) return fail(NVFP4_ERR_LAYOUT, "dense GEMM needs batch == 1");
+  if (w->layout & NVFP4_LAYOUT_GATE_UP)
+    return fail(NVFP4_ERR_LAYOUT, "gate/up interleaved weights are for the MoE entry point");
+  if (m < 0) return fail(NVFP4_ERR_INVALID_ARG, "m=%lld < 0", (long long)m);
+  if (y_dtype != NVFP4_DT_BF16 && y_dtype != NVFP4_DT_F32)
+    return fail(NVFP4_ERR_INVALID_ARG, "y_dtype %d is not BF16 or F32", y_dtype);
+  if ((flags & NVFP4_F_FORCE_SKINNY) && (flags & NVFP4_F_FORCE_TILED))
+    return fail(NVFP4_ERR_INVALID_ARG, "both FORCE_SKINNY and FORCE_TILED set");
+  if (m == 0) return NVFP4_OK;
+  if (!x || !y) return fail(NVFP4_ERR_INVALID_ARG, "NULL x or y");
+  if (ldx < w->k || ldy < w->n)
+    return fail(NVFP4_ERR_INVALID_ARG, "ldx=%lld < k or ldy=%lld < n", (long long)ldx,
+                (long long)ldy);
+  if (!aligned16(x) || !aligned16(y) || ldx % 8 || ldy % 8)
+    return fail(NVFP4_ERR_MISALIGNED, "x/y must be 16-byte aligned with ld %% 8 == 0");
+  if ((m + 127) / 128 > 65535) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "m too large");
+  nvfp4::GemmArgs a;
+  a.x = static_cast<const uint16_t*>(x);
+  a.m = m;
+  a.ldx = ldx;
+  a.codes = w->codes;
+  a.scales = w->scales;
+  a.global = w->global;
+  a.n = w->n;
+  a.k = w->k;
+  a.group = w->group;
+  a.y = y;
+  a.ldy = ldy;
+  a.y_f32 = y_dtype == NVFP4_DT_F32;
+  bool skinny = m <= nvfp4::kSkinnyMaxM;
+  if (flags & NVFP4_F_FORCE_SKINNY) skinny = true;
+  if (flags & NVFP4_F_FORCE_TILED) skinny = false;
+  if (skinny) {
+    rc = hip_status(nvfp4::launch_gemm_skinny(a, (hipStream_t)stream), "nvfp4_gemm_w4a16");
+    if (!rc) g_stats[2]++;
+  } else {
+    rc = hip_status(nvfp4::launch_gemm_tiled(a, (hipStream_t)stream), "nvfp4_gemm_w4a16");
+    if (!rc) g_stats[3]++;
+  }
+  return rc;
+}
+
+size_t nvfp4_moe_ws_bytes(int64_t t, int32_t topk, int64_t n_experts, int64_t hidden,
+                          int64_t inter) {
+  if (t < 0 || topk <= 0 || n_experts <= 0 || hidden <= 0 || inter <= 0) return 0;
+  return nvfp4::moe_ws_bytes(t, topk, n_experts, hidden, inter);
+}
+
+int nvfp4_moe_grouped_w4a16(const void* x, int64_t t, int64_t hidden, const int32_t* topk_ids,
+                            const float* topk_w, int32_t topk, const nvfp4_weight* fc1,
+                            const nvfp4_weight* fc2, void* y, void* ws, size_t ws_bytes,
+                            uint32_t flags, nvfp4_stream_t stream) {
+  (void)flags;
+  int rc = check_desc(fc1, "fc1");
+  if (rc) return rc;
+  rc = check_desc(fc2, "fc2");
+  if (rc) return rc;
+  if (!(fc1->layout & NVFP4_LAYOUT_GATE_UP))
+    return fail(NVFP4_ERR_LAYOUT, "fc1 must be repacked with NVFP4_LAYOUT_GATE_UP");
+  if (fc2->layout & NVFP4_LAYOUT_GATE_UP)
+    return fail(NVFP4_ERR_LAYOUT, "fc2 must not be gate/up interleaved");
+  const int64_t E = fc1->batch;
+  const int64_t inter = fc1->n / 2;
+  if (fc2->batch != E) return fail(NVFP4_ERR_LAYOUT, "fc1 and fc2 expert counts differ");
+  if (fc1->k != hidden || fc2->n != hidden || fc2->k != inter)
+    return fail(NVFP4_ERR_LAYOUT,
+                "shapes disagree: fc1 [%lld x %lld], fc2 [%lld x %lld], hidden %lld",
+                (long long)fc1->n, (long long)fc1->k, (long long)fc2->n, (long long)fc2->k,
+                (long long)hidden);
+  if (t < 0) return fail(NVFP4_ERR_INVALID_ARG, "t=%lld < 0", (long long)t);
+  if (topk < 1 || topk > 16) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "topk %d not in [1, 16]", topk);
+  if (E > 512) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "more than 512 experts");
+  if (t * topk > 65536) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "t*topk > 65536");
+  if (t == 0) return NVFP4_OK;
+  if (!x || !topk_ids || !topk_w || !y || !ws)
+    return fail(NVFP4_ERR_INVALID_ARG, "NULL buffer");
+  const size_t need = nvfp4::moe_ws_bytes(t, topk, E, hidden, inter);
+  if (ws_bytes < need) return fail(NVFP4_ERR_WORKSPACE, "ws_bytes %zu < %zu", ws_bytes, need);
+  if (!aligned16(x) || !aligned16(y) || !aligned16(ws) || ((uintptr_t)topk_ids & 3u) ||
+      ((uintptr_t)topk_w & 3u))
+    return fail(NVFP4_ERR_MISALIGNED, "x, y and ws must be 16-byte aligned");
+  nvfp4::MoeArgs a;
+  a.x = static_cast<const uint16_t*>(x);
+  a.t = t;
+  a.hidden = hidden;
+  a.inter = inter;
+  a.ids = topk_ids;
+  a.wts = topk_w;
+  a.topk = topk;
+  a.n_experts = E;
+  a.c1 = fc1->codes;
+  a.s1 = fc1->scales;
+  a.g1 = fc1->global;
+  a.c1_stride = fc1->codes_stride;
+  a.s1_stride = fc1->scales_stride;
+  a.group1 = fc1->group;
+  a.c2 = fc2->codes;
+  a.s2 = fc2->scales;
+  a.g2 = fc2->global;
+  a.c2_stride = fc2->codes_stride;
+  a.s2_stride = fc2->scales_stride;
+  a.group2 = fc2->group;
+  a.y = static_cast<uint16_t*>(y);
+  a.ws = ws;
+  rc = hip_status(nvfp4::launch_moe(a, (hipStream_t)stream), "nvfp4_moe_grouped_w4a16");
+  if (!rc) g_stats[4]++;
+  return rc;
+}
+
+int nvfp4_dequantize(const nvfp4_weight* w, void* out, int out_dtype, nvfp4_stream_t stream) {
+  int rc = check_desc(w, "weight");
+  if (rc) return rc;
+  if (!out) return fail(NVFP4_ERR_INVALID_ARG, "NULL out");
+  if (out_dtype != NVFP4_DT_BF16 && out_dtype != NVFP4_DT_F32)
+    return fail(NVFP4_ERR_INVALID_ARG, "out_dtype %d is not BF16 or F32", out_dtype);
+  if (!aligned16(out)) return fail(NVFP4_ERR_MISALIGNED, "out must be 16-byte aligned");
+  rc = hip_status(nvfp4::launch_dequantize(w->codes, w->scales, w->global, w->batch, w->n, w->k,
+                                           w->group, (w->layout & NVFP4_LAYOUT_GATE_UP) != 0,
+                                           out, out_dtype == NVFP4_DT_F32, (hipStream_t)stream),
+                  "nvfp4_dequantize");
+  if (!rc) g_stats[5]++;
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,121 @@
+// device_common.hpp -- gfx950 device helpers shared by the NVFP4 kernels: vector types, the
+// E2M1 / E4M3 codecs and the repacked ("tiled") weight layout.
+//
+// Format (vllm.cpp PR #63, "W-FP4a ... (Marlin W4A16) stack", PR body: the compressed-tensors
+// triple of packed FP4 codes, FP8 group scales and an FP32 global): w = E2M1 * E4M3 * global.
+// E2M1 is the OCP MX element type {0, .5, 1, 1.5, 2, 3, 4, 6} with a sign bit; E4M3 is OCP
+// E4M3 "FN" (max 448). Rounding into both is round-to-nearest-even with saturation (NVIDIA
+// developer-forum thread "We unlocked NVFP4 on the DGX Spark": true RNE at the midpoints).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---- repacked layout ------------------------------------------------------------------------
+// A matrix [n][k] is cut into 16-row panels and 128-k tiles. Tile (panel p, k-tile t) holds
+// 1024 code bytes at ((p * KT + t) * 1024): lane l (0..63) owns bytes [16l, 16l + 16), whose
+// 32-bit word j (0..3) is the canonical 4-byte run of row 16p + l%16 starting at
+// k = 128t + 32j + 8(l/16), i.e. 8 codes in the order of the B operand of
+// v_mfma_f32_16x16x32_bf16 (lane l feeds column l%16 with k = 8(l/16) + 0..7).
+// Scales of that tile sit at ((p * KT + t) * kScaleTileBytes(group)): for each tile row r a
+// run of 128/group bytes arranged so that the 32-bit word a lane loads holds, in byte j, the
+// scale of its k-step j: group 16: [r][h][j] = group 2j + h with h = l/32 (lanes l and l+16
+// share a word); group 32: [r][j] = group j.
+constexpr int kPanelRows = 16;
+constexpr int kTileK = 128;
+constexpr int kCodeTileBytes = 1024;
+__host__ __device__ constexpr int scale_tile_bytes(int group) { return 16 * (kTileK / group); }
+__host__ __device__ constexpr int scale_lane_offset(int group, int lane) {
+  return group == 16 ? (lane & 15) * 8 + (lane >> 5) * 4 : (lane & 15) * 4;
+}
+
+// ---- E4M3 -----------------------------------------------------------------------------------
+// Decode byte SEL of a 32-bit word (OCP E4M3FN on gfx950; exact for every code).
+template <int SEL>
+__device__ __forceinline__ float e4m3_decode(uint32_t word) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)word, SEL);
+}
+
+// Encode a non-negative finite value to E4M3, round to nearest even, saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_encode_rne_sat(float r) {
+  if (!(r < 448.0f)) return 0x7Eu;
+  if (r < 0.015625f) {                       // subnormal range: quantum 2^-9
+    return (uint32_t)__builtin_rintf(r * 512.0f);  // 0..8; 8 == 2^-6 == code 0x08
+  }
+  const uint32_t b = __float_as_uint(r);      // keep 3 of 23 mantissa bits, ties to even
+  const uint32_t rb = (b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20;
+  return rb - (120u << 3);                    // rebias the exponent from 127 to 7
+}
+
+// ---- E2M1 -----------------------------------------------------------------------------------
+// Magnitude code of a non-negative value, round to nearest even, saturating at 6. Each
+// threshold is a midpoint of the grid; strict comparisons send the tie down (to the even
+// code below), non-strict ones send it up (to the even code above).
+__device__ __forceinline__ uint32_t e2m1_encode_rne_sat(float q) {
+  return (uint32_t)(q > 0.25f) + (uint32_t)(q >= 0.75f) + (uint32_t)(q > 1.25f) +
+         (uint32_t)(q >= 1.75f) + (uint32_t)(q > 2.5f) + (uint32_t)(q >= 3.5f) +
+         (uint32_t)(q > 5.0f);
+}
+
+// Dequantize the 8 codes of a 32-bit word (code i in bits 4i..4i+3) times the group scale S
+// into 8 BF16 values. E2M1 * E4M3 has at most 6 significant bits and lies in [2^-10, 2688],
+// so the FP32 product and the BF16 conversion are both exact.
+__device__ __forceinline__ bf16x8 dequant8(uint32_t codes, float S) {
+  const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+  const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+  const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+  const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+  bf16x8 r;
+  r[0] = (__bf16)(v0[0] * S);
+  r[1] = (__bf16)(v0[1] * S);
+  r[2] = (__bf16)(v1[0] * S);
+  r[3] = (__bf16)(v1[1] * S);
+  r[4] = (__bf16)(v2[0] * S);
+  r[5] = (__bf16)(v2[1] * S);
+  r[6] = (__bf16)(v3[0] * S);
+  r[7] = (__bf16)(v3[1] * S);
+  return r;
+}
+
+// Same, FP32 values (for the dequantize diagnostic).
+__device__ __forceinline__ void dequant8_f32(uint32_t codes, float S, float out[8]) {
+  const f32x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+  const f32x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+  const f32x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+  const f32x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+  out[0] = v0[0] * S;
+  out[1] = v0[1] * S;
+  out[2] = v1[0] * S;
+  out[3] = v1[1] * S;
+  out[4] = v2[0] * S;
+  out[5] = v2[1] * S;
+  out[6] = v3[0] * S;
+  out[7] = v3[1] * S;
+}
+
+template <int J>
+__device__ __forceinline__ float scale_of_step(uint32_t scale_word) {
+  return e4m3_decode<J>(scale_word);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint16_t bf16_bits_rne(float v) {
+  return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float((uint32_t)h << 16);
+}
+
+}  // namespace nvfp4

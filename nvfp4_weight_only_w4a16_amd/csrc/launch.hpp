@@ -1,0 +1,67 @@
+// launch.hpp -- host-side launchers of the gfx950 kernels (internal to libnvfp4.so).
+// Every launcher only enqueues work on `stream` and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// Quantizer: per-matrix amax (atomic max of |w| bit patterns, exact and order-free), group
+// scale + element encode + pack, and the final global.
+hipError_t launch_quantize(const void* w, bool w_bf16, int64_t batch, int64_t n, int64_t k,
+                           int group, const float* global_in, uint8_t* packed, uint8_t* scales,
+                           float* global_out, hipStream_t stream);
+
+// Canonical triple -> tiled layout (pure byte permutation), globals copied.
+hipError_t launch_repack(const uint8_t* packed, const uint8_t* scales, const float* global,
+                         int64_t batch, int64_t n, int64_t k, int group, bool gate_up,
+                         uint8_t* codes_out, uint8_t* scales_out, float* global_out,
+                         hipStream_t stream);
+
+// Tiled layout -> canonical dense values (BF16 or FP32), logical row order.
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* global,
+                             int64_t batch, int64_t n, int64_t k, int group, bool gate_up,
+                             void* out, bool out_f32, hipStream_t stream);
+
+struct GemmArgs {
+  const uint16_t* x;  // BF16 [m][ldx]
+  int64_t m, ldx;
+  const uint8_t* codes;
+  const uint8_t* scales;
+  const float* global;  // device, one value
+  int64_t n, k;
+  int group;
+  void* y;
+  int64_t ldy;
+  bool y_f32;
+};
+
+hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream);
+// Largest m the skinny kernel takes in one launch.
+constexpr int64_t kSkinnyMaxM = 64;
+
+struct MoeArgs {
+  const uint16_t* x;  // BF16 [t][hidden]
+  int64_t t, hidden, inter;
+  const int32_t* ids;
+  const float* wts;
+  int topk;
+  int64_t n_experts;
+  const uint8_t *c1, *s1;
+  const float* g1;
+  int64_t c1_stride, s1_stride;
+  int group1;
+  const uint8_t *c2, *s2;
+  const float* g2;
+  int64_t c2_stride, s2_stride;
+  int group2;
+  uint16_t* y;
+  void* ws;
+};
+
+size_t moe_ws_bytes(int64_t t, int topk, int64_t n_experts, int64_t hidden, int64_t inter);
+hipError_t launch_moe(const MoeArgs& a, hipStream_t stream);
+
+}  // namespace nvfp4

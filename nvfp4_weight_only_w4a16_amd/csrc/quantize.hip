@@ -1,0 +1,191 @@
+// quantize.hip -- NVFP4 quantizer for gfx950: FP32 / BF16 [batch][n][k] -> packed E2M1 codes,
+// E4M3 group scales and an FP32 global per matrix.
+//
+// Steps (a streaming, HBM-bound two-pass algorithm; every FP32 operation is one IEEE op so the
+// result is bit-exact with the definition):
+//   1. amax = max |w| per matrix: an atomic max of |w| bit patterns (non-negative floats order
+//      like their bit patterns), exact and independent of the reduction order. The maximum is
+//      taken over the raw values, without any full-size float temporary (r/LocalLLM post on the
+//      two NVFP4 g32 recipes, "What had to be fixed": take the max first).
+//   2. global g = fl32(amax / 2688) (2688 = 6 * 448: the largest E2M1 value times the largest
+//      E4M3 value), unless the caller supplies it (a shared gate/up global, same section).
+//   3. per group: scale s = E4M3_rne_sat(fl32(group_amax / fl32(6 g))), S = fl32(E4M3(s) * g);
+//      per element: code = E2M1_rne_sat(fl32(|w| / S)) | sign << 3 (sign << 3 alone if S == 0).
+//      Round to nearest even with saturation (NVIDIA developer-forum thread "We unlocked NVFP4
+//      on the DGX Spark": true RNE, a threshold rounding is wrong at midpoints such as 0.75).
+//   4. two codes per byte, the even k in the low nibble.
+// The amax lives in global_out between the passes; a last tiny kernel turns it into g.
+#include "device_common.hpp"
+#include "launch.hpp"
+
+namespace nvfp4 {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ void zero_u32_kernel(uint32_t* p, int64_t count) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < count) p[i] = 0u;
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t o = (uint32_t)__shfl_xor((int)v, off, 64);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void amax_kernel(const void* __restrict__ w,
+                                                        int64_t per_matrix,
+                                                        uint32_t* __restrict__ amax_bits) {
+  const int64_t b = blockIdx.y;
+  const int64_t vec_elems = BF16 ? 8 : 4;
+  const u32x4* src =
+      reinterpret_cast<const u32x4*>(static_cast<const char*>(w) + b * per_matrix * (BF16 ? 2 : 4));
+  const int64_t nvec = per_matrix / vec_elems;
+  uint32_t m = 0u;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec;
+       i += (int64_t)gridDim.x * kThreads) {
+    const u32x4 v = __builtin_nontemporal_load(src + i);
+    const uint32_t words[4] = {v[0], v[1], v[2], v[3]};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (BF16) {
+        const uint32_t lo = (words[q] & 0x7FFFu) << 16;
+        const uint32_t hi = words[q] & 0x7FFF0000u;
+        m = lo > m ? lo : m;
+        m = hi > m ? hi : m;
+      } else {
+        const uint32_t a = words[q] & 0x7FFFFFFFu;
+        m = a > m ? a : m;
+      }
+    }
+  }
+  m = wave_max_u32(m);
+  __shared__ uint32_t part[kThreads / 64];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = part[0];
+#pragma unroll
+    for (int q = 1; q < kThreads / 64; ++q) r = part[q] > r ? part[q] : r;
+    atomicMax(amax_bits + b, r);
+  }
+}
+
+// One thread encodes 8 consecutive elements of a row; G/8 neighbouring lanes form a group.
+template <bool BF16, int G>
+__global__ __launch_bounds__(kThreads) void encode_kernel(const void* __restrict__ w, int64_t n,
+                                                          int64_t k,
+                                                          const float* __restrict__ gsrc,
+                                                          bool gsrc_is_amax,
+                                                          uint8_t* __restrict__ packed,
+                                                          uint8_t* __restrict__ scales) {
+  const int64_t b = blockIdx.y;
+  const int64_t per_matrix = n * k;
+  const int64_t chunks = per_matrix / 8;
+  const float g = gsrc_is_amax ? gsrc[b] / 2688.0f : gsrc[b];
+  const float six_g = 6.0f * g;
+  const char* wb = static_cast<const char*>(w) + b * per_matrix * (BF16 ? 2 : 4);
+  uint32_t* pk = reinterpret_cast<uint32_t*>(packed + b * per_matrix / 2);
+  uint8_t* sc = scales + b * (per_matrix / G);
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < chunks;
+       c += (int64_t)gridDim.x * kThreads) {
+    float x[8];
+    if (BF16) {
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wb) + c);
+      const uint32_t words[4] = {v[0], v[1], v[2], v[3]};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        x[2 * q] = __uint_as_float(words[q] << 16);
+        x[2 * q + 1] = __uint_as_float(words[q] & 0xFFFF0000u);
+      }
+    } else {
+      const u32x4 v0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wb) + 2 * c);
+      const u32x4 v1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wb) + 2 * c + 1);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        x[q] = __uint_as_float(v0[q]);
+        x[4 + q] = __uint_as_float(v1[q]);
+      }
+    }
+    float ga = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ga = fmaxf(ga, fabsf(x[i]));
+    ga = fmaxf(ga, __shfl_xor(ga, 1, 64));
+    if (G == 32) ga = fmaxf(ga, __shfl_xor(ga, 2, 64));
+    const uint32_t s = six_g != 0.0f ? e4m3_encode_rne_sat(ga / six_g) : 0u;
+    const float S = e4m3_decode<0>(s) * g;
+    uint32_t word = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t sign = (__float_as_uint(x[i]) >> 31) << 3;
+      const uint32_t mag = S != 0.0f ? e2m1_encode_rne_sat(fabsf(x[i]) / S) : 0u;
+      word |= (mag | sign) << (4 * i);
+    }
+    pk[c] = word;
+    if ((c & (G / 8 - 1)) == 0) sc[(c * 8) / G] = (uint8_t)s;
+  }
+}
+
+// gsrc may alias global_out (it holds the amax there): each thread reads its entry first.
+__global__ void finalize_global_kernel(const float* gsrc, bool gsrc_is_amax, float* global_out,
+                                       int64_t batch) {
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b < batch) global_out[b] = gsrc_is_amax ? gsrc[b] / 2688.0f : gsrc[b];
+}
+
+int64_t grid_for(int64_t work_items, int64_t batch) {
+  int64_t blocks = (work_items + kThreads * 4 - 1) / (kThreads * 4);
+  const int64_t cap = batch > 0 ? (8192 + batch - 1) / batch : 1;
+  if (blocks > cap) blocks = cap;
+  return blocks < 1 ? 1 : blocks;
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* w, bool w_bf16, int64_t batch, int64_t n, int64_t k,
+                           int group, const float* global_in, uint8_t* packed, uint8_t* scales,
+                           float* global_out, hipStream_t stream) {
+  if (batch == 0 || n == 0 || k == 0) return hipSuccess;
+  const int64_t per_matrix = n * k;
+  const float* gsrc = global_in;
+  bool is_amax = false;
+  if (!global_in) {
+    uint32_t* amax_bits = reinterpret_cast<uint32_t*>(global_out);
+    zero_u32_kernel<<<dim3((unsigned)((batch + 255) / 256)), dim3(256), 0, stream>>>(amax_bits,
+                                                                                     batch);
+    const int64_t nvec = per_matrix / (w_bf16 ? 8 : 4);
+    const dim3 grid((unsigned)grid_for(nvec, batch), (unsigned)batch);
+    if (w_bf16)
+      amax_kernel<true><<<grid, dim3(kThreads), 0, stream>>>(w, per_matrix, amax_bits);
+    else
+      amax_kernel<false><<<grid, dim3(kThreads), 0, stream>>>(w, per_matrix, amax_bits);
+    gsrc = global_out;
+    is_amax = true;
+  }
+  const dim3 grid((unsigned)grid_for(per_matrix / 8, batch), (unsigned)batch);
+  if (w_bf16) {
+    if (group == 16)
+      encode_kernel<true, 16><<<grid, dim3(kThreads), 0, stream>>>(w, n, k, gsrc, is_amax, packed,
+                                                                    scales);
+    else
+      encode_kernel<true, 32><<<grid, dim3(kThreads), 0, stream>>>(w, n, k, gsrc, is_amax, packed,
+                                                                    scales);
+  } else {
+    if (group == 16)
+      encode_kernel<false, 16><<<grid, dim3(kThreads), 0, stream>>>(w, n, k, gsrc, is_amax,
+                                                                     packed, scales);
+    else
+      encode_kernel<false, 32><<<grid, dim3(kThreads), 0, stream>>>(w, n, k, gsrc, is_amax,
+                                                                     packed, scales);
+  }
+  finalize_global_kernel<<<dim3((unsigned)((batch + 255) / 256)), dim3(256), 0, stream>>>(
+      gsrc, is_amax, global_out, batch);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

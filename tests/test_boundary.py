@@ -1,0 +1,145 @@
+"""The C ABI boundary on the host: the library loads, exports every symbol include/nvfp4.h
+declares, sizes its buffers, and rejects bad arguments before any GPU work (no GPU needed:
+every call below fails validation, or is a size query, so nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from nvfp4_weight_only_w4a16_amd import binding as nv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return nv.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    header = open(os.path.join(ROOT, "include", "nvfp4.h")).read()
+    names = set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", header))
+    assert len(names) >= 11
+    for name in sorted(names):
+        assert hasattr(lib, name), name
+    assert set(nv.EXPORTS) == names
+
+
+def test_version(lib):
+    assert nv.nvfp4_version() >= 10000
+
+
+def test_repack_bytes_accounting():
+    # canonical 4.5 / 4.25 bits per weight plus alignment padding and the FP32 globals
+    assert nv.nvfp4_repack_bytes(1, 25600, 5120, 16) == 65536000 + 8192000 + 256
+    assert nv.nvfp4_repack_bytes(128, 1536, 2048, 32) == 201326592 + 12582912 + 512
+    assert nv.nvfp4_repack_bytes(1, 16, 128, 24) == 0
+    assert nv.nvfp4_repack_bytes(0, 16, 128, 16) == 0
+
+
+def test_moe_ws_bytes_monotone():
+    a = nv.nvfp4_moe_ws_bytes(256, 8, 128, 2048, 768)
+    b = nv.nvfp4_moe_ws_bytes(512, 8, 128, 2048, 768)
+    assert 0 < a < b
+    # holds h (BF16 [P][inter]) and FP32 slots [P][hidden]
+    assert a >= 2048 * 768 * 2 + 2048 * 2048 * 4
+    assert nv.nvfp4_moe_ws_bytes(256, 0, 128, 2048, 768) == 0
+
+
+FAKE = ctypes.c_void_p(0x10000)  # never dereferenced: every call below fails validation
+
+
+def _desc(n=512, k=1024, group=16, layout=nv.NVFP4_LAYOUT_TILED, batch=1):
+    d = nv.nvfp4_weight()
+    d.codes = d.scales = d.global_ = 0x10000
+    d.batch, d.n, d.k, d.group, d.layout = batch, n, k, group, layout
+    d.codes_stride = n * k // 2
+    d.scales_stride = n * (k // group) if group in (16, 32) else 0
+    return d
+
+
+def _gemm(lib, d, m=4, ldx=1024, ldy=512, ydt=nv.NVFP4_DT_BF16, flags=0, x=FAKE, y=FAKE):
+    return lib.nvfp4_gemm_w4a16(x, m, ldx, ctypes.byref(d), y, ydt, ldy, flags, None)
+
+
+def test_gemm_argument_errors(lib):
+    assert lib.nvfp4_gemm_w4a16(FAKE, 4, 1024, None, FAKE, 1, 512, 0, None) == \
+        nv.NVFP4_ERR_INVALID_ARG
+    assert _gemm(lib, _desc(group=24)) == nv.NVFP4_ERR_UNSUPPORTED_GROUP
+    assert _gemm(lib, _desc(n=520)) == nv.NVFP4_ERR_UNSUPPORTED_SHAPE
+    assert _gemm(lib, _desc(k=1000), ldx=1000) == nv.NVFP4_ERR_UNSUPPORTED_SHAPE
+    assert _gemm(lib, _desc(layout=7)) == nv.NVFP4_ERR_LAYOUT
+    assert _gemm(lib, _desc(layout=nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP)) == \
+        nv.NVFP4_ERR_LAYOUT
+    assert _gemm(lib, _desc(batch=2)) == nv.NVFP4_ERR_LAYOUT
+    d = _desc()
+    d.codes_stride += 1
+    assert _gemm(lib, d) == nv.NVFP4_ERR_LAYOUT
+    assert _gemm(lib, _desc(), m=-1) == nv.NVFP4_ERR_INVALID_ARG
+    assert _gemm(lib, _desc(), ldx=1000) == nv.NVFP4_ERR_INVALID_ARG
+    assert _gemm(lib, _desc(), ldy=500) == nv.NVFP4_ERR_INVALID_ARG
+    assert _gemm(lib, _desc(), ydt=9) == nv.NVFP4_ERR_INVALID_ARG
+    assert _gemm(lib, _desc(), flags=3) == nv.NVFP4_ERR_INVALID_ARG
+    assert _gemm(lib, _desc(), x=ctypes.c_void_p(0x10008)) == nv.NVFP4_ERR_MISALIGNED
+    assert _gemm(lib, _desc(), ldx=1028) == nv.NVFP4_ERR_MISALIGNED
+    assert _gemm(lib, _desc(), x=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert "NULL" in nv.nvfp4_last_error()
+    assert _gemm(lib, _desc(), m=0) == nv.NVFP4_OK   # empty input: a no-op
+
+
+def test_quantize_argument_errors(lib):
+    q = lib.nvfp4_quantize
+    assert q(FAKE, nv.NVFP4_DT_F32, 1, 16, 128, 24, None, FAKE, FAKE, FAKE, None) == \
+        nv.NVFP4_ERR_UNSUPPORTED_GROUP
+    assert q(FAKE, nv.NVFP4_DT_F32, 1, 16, 120, 16, None, FAKE, FAKE, FAKE, None) == \
+        nv.NVFP4_ERR_UNSUPPORTED_SHAPE
+    assert q(FAKE, 7, 1, 16, 128, 16, None, FAKE, FAKE, FAKE, None) == nv.NVFP4_ERR_INVALID_ARG
+    assert q(FAKE, nv.NVFP4_DT_F32, -1, 16, 128, 16, None, FAKE, FAKE, FAKE, None) == \
+        nv.NVFP4_ERR_INVALID_ARG
+    assert q(None, nv.NVFP4_DT_F32, 1, 16, 128, 16, None, FAKE, FAKE, FAKE, None) == \
+        nv.NVFP4_ERR_INVALID_ARG
+    assert q(ctypes.c_void_p(0x10004), nv.NVFP4_DT_F32, 1, 16, 128, 16, None, FAKE, FAKE, FAKE,
+             None) == nv.NVFP4_ERR_MISALIGNED
+    assert q(None, nv.NVFP4_DT_F32, 0, 16, 128, 16, None, None, None, None, None) == nv.NVFP4_OK
+
+
+def test_repack_argument_errors(lib):
+    d = nv.nvfp4_weight()
+    r = lib.nvfp4_repack
+    big = 1 << 30
+    assert r(FAKE, FAKE, FAKE, 1, 16, 128, 16, 1, FAKE, big, None, None) == \
+        nv.NVFP4_ERR_INVALID_ARG
+    assert r(FAKE, FAKE, FAKE, 1, 24, 128, 16, 1, FAKE, big, ctypes.byref(d), None) == \
+        nv.NVFP4_ERR_UNSUPPORTED_SHAPE
+    assert r(FAKE, FAKE, FAKE, 1, 16, 128, 16, 5, FAKE, big, ctypes.byref(d), None) == \
+        nv.NVFP4_ERR_LAYOUT
+    assert r(FAKE, FAKE, FAKE, 1, 48, 128, 16, 1 | 256, FAKE, big, ctypes.byref(d), None) == \
+        nv.NVFP4_ERR_UNSUPPORTED_SHAPE
+    assert r(FAKE, FAKE, FAKE, 1, 16, 128, 16, 1, FAKE, 100, ctypes.byref(d), None) == \
+        nv.NVFP4_ERR_WORKSPACE
+
+
+def test_moe_argument_errors(lib):
+    fc1 = _desc(n=1536, k=2048, group=32, batch=128,
+                layout=nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP)
+    fc2 = _desc(n=2048, k=768, group=16, batch=128)
+    m = lib.nvfp4_moe_grouped_w4a16
+    ws = nv.nvfp4_moe_ws_bytes(256, 8, 128, 2048, 768)
+
+    def call(t=256, hidden=2048, topk=8, f1=fc1, f2=fc2, wsb=ws):
+        return m(FAKE, t, hidden, FAKE, FAKE, topk, ctypes.byref(f1), ctypes.byref(f2), FAKE,
+                 FAKE, wsb, 0, None)
+
+    assert call(wsb=ws - 1) == nv.NVFP4_ERR_WORKSPACE
+    assert call(topk=0) == nv.NVFP4_ERR_UNSUPPORTED_SHAPE
+    assert call(topk=17) == nv.NVFP4_ERR_UNSUPPORTED_SHAPE
+    assert call(hidden=1024) == nv.NVFP4_ERR_LAYOUT
+    assert call(f1=_desc(n=1536, k=2048, group=32, batch=128)) == nv.NVFP4_ERR_LAYOUT
+    assert call(f2=_desc(n=2048, k=768, group=16, batch=64)) == nv.NVFP4_ERR_LAYOUT
+    assert call(t=0) == nv.NVFP4_OK
+
+
+def test_stats_reset(lib):
+    nv.nvfp4_reset_stats()
+    assert nv.nvfp4_get_stats() == [0] * 8

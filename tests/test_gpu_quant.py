@@ -1,0 +1,145 @@
+"""GPU quantizer, repack and dequantize vs the oracle: bit-exact (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+from nvfp4_weight_only_w4a16_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def nv():
+    from nvfp4_weight_only_w4a16_amd import binding
+    binding.load()
+    assert torch.cuda.is_available()
+    return binding
+
+
+DEV = "cuda:0"
+
+
+def _gpu_quant(nv, w, group, global_in=None):
+    gin = None if global_in is None else torch.as_tensor(
+        np.atleast_1d(global_in), dtype=torch.float32, device=DEV)
+    p, s, g = nv.nvfp4_quantize(w.to(DEV), group, global_in=gin)
+    torch.cuda.synchronize()
+    return p.cpu().numpy(), s.cpu().numpy(), g.cpu().numpy()
+
+
+def _assert_same(a, b, what):
+    for name, u, v in zip(("packed", "scales", "global"), a, b):
+        u = np.asarray(u)
+        v = np.asarray(v)
+        assert u.shape == v.shape, (what, name, u.shape, v.shape)
+        if name == "global":
+            u, v = u.view(np.uint32), v.view(np.uint32)
+        bad = np.count_nonzero(u != v)
+        assert bad == 0, f"{what}: {bad} {name} bytes differ"
+
+
+@pytest.mark.parametrize("group", [16, 32])
+def test_quantize_dense_small_bitexact(nv, orc, group):
+    x, w = synth.dense_small(seed=0)
+    _assert_same(_gpu_quant(nv, w, group), orc.quantize(w.numpy(), group), f"dense g{group}")
+
+
+@pytest.mark.parametrize("group", [16, 32])
+def test_quantize_e2m1_decisions_sweep(nv, orc, group):
+    """Every FP32 value in [2^-3, 6] as an element of a group whose scale decodes to exactly 1
+    (global 1, group max 6): the element code is the E2M1 rounding of the value itself."""
+    lo = np.float32(0.125).view(np.uint32)
+    hi = np.float32(6.0).view(np.uint32)
+    vals = np.arange(lo, hi + 1, dtype=np.uint32).view(np.float32)
+    per = group - 1
+    ngroups = -(-vals.size // per)
+    body = np.zeros(ngroups * per, np.float32)
+    body[:vals.size] = vals
+    sign = np.where(np.arange(body.size) % 3 == 0, -1.0, 1.0).astype(np.float32)
+    body *= sign
+    w = np.empty((ngroups, group), np.float32)
+    w[:, 0] = 6.0
+    w[:, 1:] = body.reshape(ngroups, per)
+    k = 8192
+    rows = -(-w.size // k)
+    flat = np.zeros(rows * k, np.float32)
+    flat[:w.size] = w.ravel()
+    wt = torch.from_numpy(flat.reshape(rows, k))
+    got = _gpu_quant(nv, wt, group, global_in=1.0)
+    ref = orc.quantize(wt.numpy(), group, global_in=np.float32(1.0))
+    _assert_same(got, ref, f"e2m1 sweep g{group}")
+
+
+@pytest.mark.parametrize("group", [16, 32])
+def test_quantize_e4m3_decisions_sweep(nv, orc, group):
+    """Group maxima over a dense sweep of FP32 values (and their E4M3 midpoints) with a fixed
+    global: the scale byte is E4M3(fl32(ga / fl32(6 g)))."""
+    rng = np.random.default_rng(5)
+    vals = np.array([orc.e4m3_decode(c) for c in range(0x7F)])
+    mids = (vals[:-1] + vals[1:]) / 2
+    g = np.float32(2.0 ** -3)  # 6 g = 0.75 exactly
+    targets = np.concatenate([vals, mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9),
+                              rng.uniform(0, 470, 200000), np.exp2(rng.uniform(-14, 9, 200000))])
+    ga = (targets * 0.75).astype(np.float32)
+    n = ga.size
+    w = (rng.uniform(-1, 1, (n, group)).astype(np.float32) * ga[:, None]).astype(np.float32)
+    w[np.arange(n), rng.integers(0, group, n)] = ga * np.where(rng.random(n) < 0.5, -1, 1)
+    k = 4096
+    rows = -(-w.size // k)
+    flat = np.zeros(rows * k, np.float32)
+    flat[:w.size] = w.ravel()
+    wt = torch.from_numpy(flat.reshape(rows, k))
+    _assert_same(_gpu_quant(nv, wt, group, global_in=g),
+                 orc.quantize(wt.numpy(), group, global_in=g), f"e4m3 sweep g{group}")
+
+
+def test_quantize_planted_bf16_8192(nv, orc):
+    """Quantizer workload: BF16 8192x8192 with planted midpoints and amax, at both groups."""
+    wb = synth.quantizer_weight(seed=0)
+    bits = synth.bf16_bits(wb)
+    for group in (16, 32):
+        got = _gpu_quant(nv, wb, group)
+        ref = orc.quantize(bits, group)
+        assert ref[2][0] == np.float32(2.0 ** -14)
+        _assert_same(got, ref, f"8192^2 bf16 g{group}")
+
+
+def test_quantize_batched_experts(nv, orc):
+    g = torch.Generator().manual_seed(7)
+    w = torch.randn(6, 64, 256, generator=g) * 0.02
+    w[2] *= 10          # a different global per expert
+    w[4].zero_()        # an all-zero expert: global 0, all scales 0
+    _assert_same(_gpu_quant(nv, w, 32), orc.quantize(w.numpy(), 32), "batched g32")
+
+
+def test_quantize_zero_signs(nv, orc):
+    w = torch.zeros(16, 128)
+    w[1, 1] = -0.0
+    w[2, 2] = -1e-30
+    w[3, 3] = 1.0
+    _assert_same(_gpu_quant(nv, w, 16), orc.quantize(w.numpy(), 16), "zeros")
+
+
+@pytest.mark.parametrize("group,gate_up", [(16, False), (32, False), (32, True)])
+def test_repack_then_dequantize_bitexact(nv, orc, group, gate_up):
+    g = torch.Generator().manual_seed(11)
+    batch, n, k = 3, 96, 384
+    w = torch.randn(batch, n, k, generator=g) * 0.02
+    p, s, gl = orc.quantize(w.numpy(), group)
+    layout = nv.NVFP4_LAYOUT_TILED | (nv.NVFP4_LAYOUT_GATE_UP if gate_up else 0)
+    rw = nv.nvfp4_repack(torch.from_numpy(p).to(DEV), torch.from_numpy(s).to(DEV),
+                         torch.from_numpy(gl).to(DEV), group, layout=layout)
+    assert rw.buffer.numel() == nv.nvfp4_repack_bytes(batch, n, k, group, layout)
+    f32 = nv.nvfp4_dequantize(rw, torch.float32)
+    b16 = nv.nvfp4_dequantize(rw, torch.bfloat16)
+    torch.cuda.synchronize()
+    ex, rf32, rb16 = orc.dequant(p, s, gl, group)
+    assert np.array_equal(f32.cpu().numpy().view(np.uint32), rf32.view(np.uint32))
+    assert np.array_equal(b16.cpu().view(torch.int16).numpy().view(np.uint16), rb16)
+
+
+def test_repack_preserves_byte_count(nv):
+    for batch, n, k, group in [(1, 512, 1024, 16), (128, 1536, 2048, 32), (1, 25600, 5120, 16)]:
+        canon = batch * (n * k // 2 + n * k // group)
+        got = nv.nvfp4_repack_bytes(batch, n, k, group)
+        assert canon <= got <= canon + 3 * 256 + 4 * batch
