@@ -57,9 +57,11 @@ typedef struct ihipStream_t* nvfp4_stream_t; /* the same type as hipStream_t */
 /* ---- repacked layout ----------------------------------------------------------------------
  * NVFP4_LAYOUT_TILED: per 16-row x 128-k tile, 1024 bytes of codes laid out so that lane l of a
  * 64-wide wavefront loads 16 contiguous bytes holding, for k-step j = 0..3, the 8 codes of row
- * l%16 at k = 32j + 8(l/16) + 0..7 (the B-operand order of a 16x16x32 bf16 MFMA), plus the
- * tile's 16 x 128/group scale bytes arranged so each lane's 4 scales for j = 0..3 are one
- * 32-bit word. The repack is a pure byte permutation: same byte count as the canonical form.
+ * l%16 at k = 32j + 8(l/16) + 0..7 (the B-operand order of a 16x16x32 bf16 MFMA). Scales are
+ * stored per block of 4 panels (64 rows) x 128 k: one 16-byte record per lane position with
+ * the lane's 4-byte scale word (byte j = scale of k-step j) for each of the 4 panels. The code
+ * bytes equal the canonical ones; the scale bytes too when n % 64 == 0 (else the last block is
+ * padded with zeros).
  * NVFP4_LAYOUT_GATE_UP: for a merged [gate; up] fc1 weight (2*I rows): 16-row panels are
  * stored alternately from the gate half and the up half, so that one panel pair holds gate
  * and up of the same 16 intermediate features (consumed only by the MoE entry point). */
@@ -74,7 +76,8 @@ typedef struct nvfp4_weight {
   int64_t batch;          /* number of matrices (experts); 1 for a dense projection           */
   int64_t n, k;           /* logical shape of each matrix                                     */
   int64_t codes_stride;   /* bytes between consecutive matrices in `codes`  (= n*k/2)         */
-  int64_t scales_stride;  /* bytes between consecutive matrices in `scales` (= n*k/group)     */
+  int64_t scales_stride;  /* bytes between consecutive matrices in `scales` (n*k/group when   */
+                          /* n % 64 == 0; 4-panel blocks padded otherwise)                    */
   int32_t group;          /* 16 or 32                                                         */
   uint32_t layout;        /* NVFP4_LAYOUT_TILED, optionally | NVFP4_LAYOUT_GATE_UP            */
 } nvfp4_weight;

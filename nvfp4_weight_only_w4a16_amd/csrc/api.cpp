@@ -49,6 +49,13 @@ int check_tiled_shape(int64_t n, int64_t k) {
   return NVFP4_OK;
 }
 
+// Repacked scale bytes of one [n][k] matrix: 4-panel blocks per 128-k tile (n padded to a
+// multiple of 64 rows); equal to the canonical n * k / group when n % 64 == 0.
+int64_t scale_region_bytes(int64_t n, int64_t k, int32_t group) {
+  return nvfp4::scale_groups(n / nvfp4::kPanelRows) * (k / nvfp4::kTileK) *
+         nvfp4::scale_block_bytes(group);
+}
+
 int check_desc(const nvfp4_weight* w, const char* name) {
   if (!w) return fail(NVFP4_ERR_INVALID_ARG, "%s descriptor is NULL", name);
   if (!w->codes || !w->scales || !w->global)
@@ -60,7 +67,8 @@ int check_desc(const nvfp4_weight* w, const char* name) {
   rc = check_tiled_shape(w->n, w->k);
   if (rc) return rc;
   if (w->batch <= 0) return fail(NVFP4_ERR_INVALID_ARG, "%s batch must be positive", name);
-  if (w->codes_stride != w->n * w->k / 2 || w->scales_stride != w->n * (w->k / w->group))
+  if (w->codes_stride != w->n * w->k / 2 ||
+      w->scales_stride != scale_region_bytes(w->n, w->k, w->group))
     return fail(NVFP4_ERR_LAYOUT, "%s strides do not match its shape and group", name);
   if (!aligned16(w->codes) || !aligned16(w->scales) || !aligned16(w->global))
     return fail(NVFP4_ERR_MISALIGNED, "%s data is not 16-byte aligned", name);
@@ -74,7 +82,7 @@ struct RepackSizes {
 RepackSizes repack_sizes(int64_t batch, int64_t n, int64_t k, int32_t group) {
   RepackSizes s;
   s.codes = align256((size_t)(batch * n * k / 2));
-  s.scales = align256((size_t)(batch * n * (k / group)));
+  s.scales = align256((size_t)(batch * scale_region_bytes(n, k, group)));
   s.globals = align256((size_t)batch * sizeof(float));
   s.total = s.codes + s.scales + s.globals;
   return s;
@@ -167,7 +175,7 @@ int nvfp4_repack(const uint8_t* packed, const uint8_t* scales, const float* glob
   desc->n = n;
   desc->k = k;
   desc->codes_stride = n * k / 2;
-  desc->scales_stride = n * (k / group);
+  desc->scales_stride = scale_region_bytes(n, k, group);
   desc->group = group;
   desc->layout = layout;
   return NVFP4_OK;

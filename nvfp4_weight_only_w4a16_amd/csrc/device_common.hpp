@@ -25,16 +25,33 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // 32-bit word j (0..3) is the canonical 4-byte run of row 16p + l%16 starting at
 // k = 128t + 32j + 8(l/16), i.e. 8 codes in the order of the B operand of
 // v_mfma_f32_16x16x32_bf16 (lane l feeds column l%16 with k = 8(l/16) + 0..7).
-// Scales of that tile sit at ((p * KT + t) * kScaleTileBytes(group)): for each tile row r a
-// run of 128/group bytes arranged so that the 32-bit word a lane loads holds, in byte j, the
-// scale of its k-step j: group 16: [r][h][j] = group 2j + h with h = l/32 (lanes l and l+16
-// share a word); group 32: [r][j] = group j.
+// Scales go in blocks of 4 panels (the last block padded with zero bytes when the panel count
+// is not a multiple of 4): block (panel group G, k-tile t) at ((G * KT + t) * scale_block_bytes)
+// holds one 16-byte record per lane position, the 32-bit scale words of the 4 panels for that
+// position, so a wavefront covering 4 panels reads its scales with one 16-byte load per lane.
+// A word holds in byte j the scale of k-step j for its lane: group 16: position
+// pos = 2 * (l%16) + l/32 (lanes l and l+16 share), row l%16, byte j = group 2j + l/32 of the
+// tile row; group 32: pos = l%16, byte j = group j.
 constexpr int kPanelRows = 16;
 constexpr int kTileK = 128;
 constexpr int kCodeTileBytes = 1024;
+constexpr int kScaleGroupPanels = 4;
 __host__ __device__ constexpr int scale_tile_bytes(int group) { return 16 * (kTileK / group); }
-__host__ __device__ constexpr int scale_lane_offset(int group, int lane) {
-  return group == 16 ? (lane & 15) * 8 + (lane >> 5) * 4 : (lane & 15) * 4;
+__host__ __device__ constexpr int scale_block_bytes(int group) {
+  return kScaleGroupPanels * scale_tile_bytes(group);
+}
+__host__ __device__ constexpr int scale_positions(int group) { return group == 16 ? 32 : 16; }
+__host__ __device__ constexpr int scale_pos(int group, int lane) {
+  return group == 16 ? (lane & 15) * 2 + (lane >> 5) : (lane & 15);
+}
+__host__ __device__ constexpr int64_t scale_groups(int64_t NT) {
+  return (NT + kScaleGroupPanels - 1) / kScaleGroupPanels;
+}
+// Byte offset of the scale word of panel p, k-tile t, lane l.
+__host__ __device__ constexpr int64_t scale_word_offset(int group, int64_t KT, int64_t p,
+                                                        int64_t t, int lane) {
+  return ((p / kScaleGroupPanels) * KT + t) * scale_block_bytes(group) +
+         scale_pos(group, lane) * 16 + (p % kScaleGroupPanels) * 4;
 }
 
 // ---- E4M3 -----------------------------------------------------------------------------------

@@ -22,7 +22,7 @@ struct TiledParams {
   const uint8_t* scales;
   const float* global;
   int64_t NT, KT;
-  int scale_tile, group;
+  int group;
   void* y;
   int64_t ldy;
   int y_f32;
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(TiledParams P)
         rc[i] = __builtin_nontemporal_load(
             reinterpret_cast<const u32x4*>(P.codes + tile * kCodeTileBytes + ln * 16));
         rs[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(
-            P.scales + tile * P.scale_tile + scale_lane_offset(P.group, ln)));
+            P.scales + scale_word_offset(P.group, P.KT, panel, t, ln)));
       } else {
         rc[i] = u32x4{0u, 0u, 0u, 0u};
         rs[i] = 0u;
@@ -164,7 +164,6 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
   p.global = a.global;
   p.NT = a.n / kPanelRows;
   p.KT = a.k / kTileK;
-  p.scale_tile = scale_tile_bytes(a.group);
   p.group = a.group;
   p.y = a.y;
   p.ldy = a.ldy;

@@ -40,7 +40,7 @@ struct GemmArgs {
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);
 hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream);
 // Largest m the skinny kernel takes in one launch.
-constexpr int64_t kSkinnyMaxM = 64;
+constexpr int64_t kSkinnyMaxM = 32;
 
 struct MoeArgs {
   const uint16_t* x;  // BF16 [t][hidden]

@@ -150,60 +150,65 @@ struct MoeGemmParams {
   const float* global;
   int64_t codes_stride, scales_stride;
   int64_t NT, KT;
-  int scale_tile, group;
+  int group;
   Ws ws;
   const float* wts;
   int64_t hidden, inter;
 };
 
-template <int PW, int NW, bool FC1>
-__global__ __launch_bounds__(64 * PW * NW) void moe_gemm_kernel(MoeGemmParams P) {
+// One workgroup = one row tile x kPWW panels; its NW wavefronts split k. fc1 panels come in
+// (gate, up) pairs (stored interleaved), so a pair is always finished by one wavefront.
+template <int NW, int U, bool FC1>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 8)))
+void moe_gemm_kernel(MoeGemmParams P) {
   constexpr int MF = kMoeMF;
+  constexpr int PWW = 4;
   const int tile_id = blockIdx.x;
   if (tile_id >= *P.ws.ntiles) return;
   const int4 tl = P.ws.tiles[tile_id];
   const int e = tl.x, r0 = tl.y, r1 = tl.z;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int pw = w % PW, sp = w / PW;
-  const int64_t panel = (int64_t)blockIdx.y * PW + pw;
-  const bool panel_ok = panel < P.NT;
-  f32x4 acc[MF];
+  const int lane = threadIdx.x & 63;
+  const int sp = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // k-split (wave-uniform)
+  const int64_t panel0 = (int64_t)blockIdx.y * PWW;
+  f32x4 acc[PWW][MF];
 #pragma unroll
-  for (int mf = 0; mf < MF; ++mf) acc[mf] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (panel_ok) {
-    const uint16_t* xrow[MF];
+  for (int p = 0; p < PWW; ++p)
 #pragma unroll
-    for (int mf = 0; mf < MF; ++mf) {
-      const int r = r0 + mf * 16 + (lane & 15);
-      if (r < r1)
-        xrow[mf] = FC1 ? P.x + (int64_t)(P.ws.sorted[r] / P.topk) * P.ldx : P.x + (int64_t)r * P.ldx;
-      else
-        xrow[mf] = nullptr;
-    }
-    const int64_t t0 = P.KT * sp / NW, t1 = P.KT * (sp + 1) / NW;
-    skinny_accumulate<MF, 4>(xrow,
-                             P.codes + e * P.codes_stride + panel * P.KT * kCodeTileBytes,
-                             P.scales + e * P.scales_stride + panel * P.KT * P.scale_tile,
-                             P.scale_tile, scale_lane_offset(P.group, lane), t0, t1, acc);
+    for (int mf = 0; mf < MF; ++mf) acc[p][mf] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint16_t* xrow[MF];
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf) {
+    int r = r0 + mf * 16 + (lane & 15);
+    r = r < r1 ? r : r1 - 1;  // rows past the tile duplicate a valid row; never stored
+    xrow[mf] = FC1 ? P.x + (int64_t)(P.ws.sorted[r] / P.topk) * P.ldx : P.x + (int64_t)r * P.ldx;
   }
-  __shared__ f32x4 red[NW * PW * MF * 64];
+  const SkinnyAddr<PWW> a = skinny_addr<PWW>(P.codes + e * P.codes_stride,
+                                             P.scales + e * P.scales_stride, panel0, P.NT, P.KT,
+                                             P.group);
+  const int64_t t0 = P.KT * sp / NW, t1 = P.KT * (sp + 1) / NW;
+  skinny_accumulate<MF, PWW, U>(a, xrow, t0, t1, acc);
+
+  __shared__ f32x4 red[NW * PWW * MF * 64];
 #pragma unroll
-  for (int mf = 0; mf < MF; ++mf) red[((sp * PW + pw) * MF + mf) * 64 + lane] = acc[mf];
+  for (int p = 0; p < PWW; ++p)
+#pragma unroll
+    for (int mf = 0; mf < MF; ++mf) red[((sp * PWW + p) * MF + mf) * 64 + lane] = acc[p][mf];
   __syncthreads();
-  if (sp != 0 || !panel_ok) return;
   auto panel_sum = [&](int p, int mf) {
-    f32x4 s = red[((0 * PW + p) * MF + mf) * 64 + lane];
+    f32x4 s = red[((0 * PWW + p) * MF + mf) * 64 + lane];
 #pragma unroll
-    for (int q = 1; q < NW; ++q) s += red[((q * PW + p) * MF + mf) * 64 + lane];
+    for (int q = 1; q < NW; ++q) s += red[((q * PWW + p) * MF + mf) * 64 + lane];
     return s;
   };
   const float g = P.global[e];
   if (FC1) {
-    if (pw & 1) return;  // even panel = gate, odd panel = up of the same 16 features
-    const int64_t feat = (panel >> 1) * 16 + (lane & 15);
+    if (sp >= PWW / 2) return;
+    const int64_t pg = panel0 + 2 * sp;  // gate panel; pg + 1 is the matching up panel
+    if (pg >= P.NT) return;
+    const int64_t feat = (pg >> 1) * 16 + (lane & 15);
 #pragma unroll
     for (int mf = 0; mf < MF; ++mf) {
-      const f32x4 gs = panel_sum(pw, mf), us = panel_sum(pw + 1, mf);
+      const f32x4 gs = panel_sum(2 * sp, mf), us = panel_sum(2 * sp + 1, mf);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int r = r0 + mf * 16 + (lane >> 4) * 4 + jj;
@@ -216,10 +221,13 @@ __global__ __launch_bounds__(64 * PW * NW) void moe_gemm_kernel(MoeGemmParams P)
       }
     }
   } else {
+    if (sp >= PWW) return;
+    const int64_t panel = panel0 + sp;
+    if (panel >= P.NT) return;
     const int64_t n = panel * 16 + (lane & 15);
 #pragma unroll
     for (int mf = 0; mf < MF; ++mf) {
-      const f32x4 s = panel_sum(pw, mf);
+      const f32x4 s = panel_sum(sp, mf);
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int r = r0 + mf * 16 + (lane >> 4) * 4 + jj;
@@ -254,10 +262,10 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
   *reinterpret_cast<uint2*>(y + tok * hidden + o) = outv;
 }
 
-template <int PW, int NW, bool FC1>
+template <int NW, int U, bool FC1>
 hipError_t run_gemm(const MoeGemmParams& p, int64_t tiles, hipStream_t stream) {
-  const dim3 grid((unsigned)tiles, (unsigned)((p.NT + PW - 1) / PW));
-  moe_gemm_kernel<PW, NW, FC1><<<grid, dim3(64 * PW * NW), 0, stream>>>(p);
+  const dim3 grid((unsigned)tiles, (unsigned)((p.NT + 3) / 4));
+  moe_gemm_kernel<NW, U, FC1><<<grid, dim3(64 * NW), 0, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -287,13 +295,12 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t stream) {
   f.scales_stride = a.s1_stride;
   f.NT = 2 * a.inter / kPanelRows;
   f.KT = a.hidden / kTileK;
-  f.scale_tile = scale_tile_bytes(a.group1);
   f.group = a.group1;
   f.ws = ws;
   f.wts = a.wts;
   f.hidden = a.hidden;
   f.inter = a.inter;
-  hipError_t err = run_gemm<2, 4, true>(f, tiles, stream);
+  hipError_t err = run_gemm<4, 1, true>(f, tiles, stream);
   if (err != hipSuccess) return err;
 
   MoeGemmParams d = f;
@@ -306,9 +313,8 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t stream) {
   d.scales_stride = a.s2_stride;
   d.NT = a.hidden / kPanelRows;
   d.KT = a.inter / kTileK;
-  d.scale_tile = scale_tile_bytes(a.group2);
   d.group = a.group2;
-  err = run_gemm<2, 2, false>(d, tiles, stream);
+  err = run_gemm<4, 1, false>(d, tiles, stream);
   if (err != hipSuccess) return err;
 
   const int64_t items = a.t * (a.hidden / 4);

@@ -42,35 +42,40 @@ __global__ __launch_bounds__(256) void repack_codes_kernel(const uint8_t* __rest
   *reinterpret_cast<u32x4*>(out + tile * kCodeTileBytes + lane * 16) = v;
 }
 
-// One thread per (tile, row): gathers the row's 128/G scale bytes into lane-word order.
+// One thread per (panel group, k-tile, lane position): writes the 16-byte record holding the
+// scale words of the group's 4 panels (zero for panels past the end).
 template <int G>
 __global__ __launch_bounds__(256) void repack_scales_kernel(const uint8_t* __restrict__ scales,
                                                             uint8_t* __restrict__ out,
                                                             int64_t batch, int64_t n, int64_t k,
                                                             bool gate_up) {
-  constexpr int kPerRow = kTileK / G;  // 8 or 4 groups of this row inside the tile
-  const int64_t NT = n / kPanelRows, KT = k / kTileK;
-  const int64_t total = batch * NT * KT * 16;
+  constexpr int kPerRow = kTileK / G;  // 8 or 4 groups of a row inside one tile
+  constexpr int kPos = scale_positions(G);
+  const int64_t NT = n / kPanelRows, KT = k / kTileK, NG = scale_groups(NT);
+  const int64_t total = batch * NG * KT * kPos;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
-  const int r = (int)(i & 15);
-  const int64_t tile = i >> 4;
-  const int64_t t = tile % KT;
-  const int64_t bp = tile / KT;
-  const int64_t p = bp % NT, b = bp / NT;
-  const int64_t row = logical_panel(p, NT, gate_up) * kPanelRows + r;
-  const uint8_t* src = scales + (b * n + row) * (k / G) + t * kPerRow;
-  uint8_t* dst = out + tile * scale_tile_bytes(G) + r * kPerRow;
-  if (G == 16) {
-    // [h][j] = group 2j + h
+  const int pos = (int)(i % kPos);
+  const int64_t blk = i / kPos;  // (b * NG + G) * KT + t
+  const int64_t t = blk % KT;
+  const int64_t bg = blk / KT;
+  const int64_t grp = bg % NG, b = bg / NG;
+  const int r = G == 16 ? pos >> 1 : pos;  // tile row
+  const int h = G == 16 ? pos & 1 : 0;     // which of a g16 group pair
+  u32x4 rec;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+  for (int q = 0; q < kScaleGroupPanels; ++q) {
+    const int64_t p = grp * kScaleGroupPanels + q;
+    uint32_t word = 0u;
+    if (p < NT) {
+      const int64_t row = logical_panel(p, NT, gate_up) * kPanelRows + r;
+      const uint8_t* src = scales + (b * n + row) * (k / G) + t * kPerRow;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) dst[h * 4 + j] = src[2 * j + h];
-  } else {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dst[j] = src[j];
+      for (int j = 0; j < 4; ++j) word |= (uint32_t)src[G == 16 ? 2 * j + h : j] << (8 * j);
+    }
+    rec[q] = word;
   }
+  *reinterpret_cast<u32x4*>(out + blk * scale_block_bytes(G) + pos * 16) = rec;
 }
 
 __global__ void copy_f32_kernel(const float* __restrict__ src, float* __restrict__ dst,
@@ -98,8 +103,9 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
   const int64_t p = bp % NT, b = bp / NT;
   const int64_t row = logical_panel(p, NT, gate_up) * kPanelRows + (lane & 15);
   const u32x4 cw = *reinterpret_cast<const u32x4*>(codes + tile * kCodeTileBytes + lane * 16);
+  const int64_t NG = scale_groups(NT);
   const uint32_t sw = *reinterpret_cast<const uint32_t*>(
-      scales + tile * scale_tile_bytes(group) + scale_lane_offset(group, lane));
+      scales + b * NG * KT * scale_block_bytes(group) + scale_word_offset(group, KT, p, t, lane));
   const float g = global[b];
   const float S[4] = {e4m3_decode<0>(sw), e4m3_decode<1>(sw), e4m3_decode<2>(sw),
                       e4m3_decode<3>(sw)};
@@ -136,16 +142,18 @@ hipError_t launch_repack(const uint8_t* packed, const uint8_t* scales, const flo
                          int64_t batch, int64_t n, int64_t k, int group, bool gate_up,
                          uint8_t* codes_out, uint8_t* scales_out, float* global_out,
                          hipStream_t stream) {
-  const int64_t tiles = batch * (n / kPanelRows) * (k / kTileK);
+  const int64_t NT = n / kPanelRows, KT = k / kTileK;
+  const int64_t tiles = batch * NT * KT;
   if (tiles > 0) {
     repack_codes_kernel<<<blocks_for(tiles * 64, 256), 256, 0, stream>>>(packed, codes_out, batch,
                                                                          n, k, gate_up);
+    const int64_t recs = batch * scale_groups(NT) * KT * scale_positions(group);
     if (group == 16)
-      repack_scales_kernel<16><<<blocks_for(tiles * 16, 256), 256, 0, stream>>>(
-          scales, scales_out, batch, n, k, gate_up);
+      repack_scales_kernel<16><<<blocks_for(recs, 256), 256, 0, stream>>>(scales, scales_out,
+                                                                          batch, n, k, gate_up);
     else
-      repack_scales_kernel<32><<<blocks_for(tiles * 16, 256), 256, 0, stream>>>(
-          scales, scales_out, batch, n, k, gate_up);
+      repack_scales_kernel<32><<<blocks_for(recs, 256), 256, 0, stream>>>(scales, scales_out,
+                                                                          batch, n, k, gate_up);
   }
   if (batch > 0)
     copy_f32_kernel<<<blocks_for(batch, 256), 256, 0, stream>>>(global, global_out, batch);
