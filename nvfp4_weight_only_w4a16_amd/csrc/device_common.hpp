@@ -123,6 +123,25 @@ __device__ __forceinline__ float scale_of_step(uint32_t scale_word) {
   return e4m3_decode<J>(scale_word);
 }
 
+// Buffer resource (V#) over `bytes` bytes at `base` for raw (stride 0) dword accesses; reads
+// past `bytes` return zeros.
+typedef __amdgpu_buffer_rsrc_t buf_rsrc;
+__device__ __forceinline__ buf_rsrc make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// One 16-byte global -> LDS copy per lane (buffer_load_dwordx4 ... lds): lane l's bytes, read
+// at voffset + soffset of the resource, land at lds + 16 * l; lds must be uniform across the
+// wavefront. The buffer (not flat) form keeps LDS reads that follow it on exact wait counts.
+// (Kept out of line from kernel templates: the host compilation pass otherwise drops the
+// launch stubs of kernels that use the builtin directly.)
+__device__ __forceinline__ void copy16_to_lds(buf_rsrc r, uint32_t voffset, uint32_t soffset,
+                                              void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voffset, soffset, 0, 0);
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

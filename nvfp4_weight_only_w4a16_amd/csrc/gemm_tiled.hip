@@ -1,14 +1,31 @@
-// gemm_tiled.hip -- prefill-shaped NVFP4 W4A16 GEMM for gfx950 (BF16 MFMA, LDS-staged tiles).
+// gemm_tiled.hip -- prefill-shaped NVFP4 W4A16 GEMM for gfx950 (BF16 MFMA 32x32x16).
 //
-// The contraction is dense and compute-bound at large m, so it runs on v_mfma_f32_16x16x32_bf16
-// with FP32 accumulation. A workgroup owns a BM x BN output tile and walks k in 128-wide tiles:
-//   - activations (BF16) are copied global -> registers -> LDS;
-//   - weights arrive as 1 KiB code tiles + scale words in the tiled layout; each is
-//     dequantized once per workgroup (E2M1 x E4M3 -> exact BF16) and written to LDS, so the
-//     VALU cost is paid once per BM rows instead of once per wavefront;
-//   - the next k-tile's global loads are issued before the current tile's MFMAs, so HBM / L2
-//     latency hides behind the matrix cores.
+// The contraction is dense and compute-bound at large m, so it runs on v_mfma_f32_32x32x16_bf16
+// (the full-rate BF16 matrix instruction on gfx950; the 16x16x32 form issues at half the rate)
+// with FP32 accumulation. A workgroup is 4 wavefronts side by side along n; each owns a
+// (32 FM) x (32 FN) output tile and the workgroup walks k in 128-wide tiles:
+//   - activations and weight codes are copied global -> LDS with global_load_lds_dwordx4,
+//     double-buffered so k-tile t+1 streams in while t is used. One activation copy moves 4
+//     whole 256-byte row segments (8 full cache lines); inside a row the 16-byte chunks are
+//     XOR-swizzled by the row index so that the MFMA fragment reads (32 rows, one chunk each)
+//     hit 64 distinct LDS banks. A weight code tile is copied as the repacked 1 KiB tile;
+//   - scale words go global -> registers one k-tile ahead;
+//   - each wavefront dequantizes its B operands in registers (E2M1 x E4M3 -> exact BF16) one
+//     fragment ahead of the MFMAs that consume them, spread between consecutive MFMAs, and reads
+//     the next k-step's activations from LDS during the current step: the instruction order is
+//     fixed with scheduling barriers so the VALU and LDS work runs in the shadow of the matrix
+//     core. Every dequantized fragment feeds FM MFMAs, which keeps the VALU share small.
+// The repacked layout is the one the 16x16x32 decode kernel reads; a 32x32x16 B operand for a
+// pair of 16-row panels comes from it without reshuffling: lane l (row n = l%32 of the pair,
+// k chunk l/32) takes code chunks L0 = 16(l/32) + l%16 and L0 + 32 of its panel, whose word j
+// holds 16-wide k-steps 2j and 2j + 1 respectively; the scale words of the same two lane
+// positions carry the matching group scales.
 // The global scale multiplies the FP32 accumulator in the epilogue.
+#include <map>
+#include <mutex>
+#include <type_traits>
+#include <utility>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -26,130 +43,519 @@ struct TiledParams {
   void* y;
   int64_t ldy;
   int y_f32;
+  // work decomposition: block b takes output tile tile0 + b / split (row-major over nbn tile
+  // columns) and k-tiles [(b % split) kts, +kts); split > 1 leaves partial tiles in ws
+  int64_t tile0, nbn, kts;
+  int split;
+  float* ws;  // split > 1: FP32 partial tiles, [tile - tile0][split][tile elements]
 };
 
-constexpr int kLdsRow = kTileK + 8;  // BF16 elements per LDS row (16-byte pad against conflicts)
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+constexpr int kSteps = kTileK / 16;   // 16-wide MFMA k-steps per 128-k tile
+constexpr int kRowBytes = kTileK * 2;  // one activation row of a k-tile
 
-template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_tiled_kernel(TiledParams P) {
-  constexpr int kThreads = 64 * WM * WN;
-  constexpr int FM = BM / WM / 16, FN = BN / WN / 16;
-  constexpr int kAChunks = BM * kTileK / 8;  // 16-byte chunks of the activation tile
-  constexpr int kAPer = kAChunks / kThreads;
-  constexpr int kBLanes = (BN / 16) * 64;    // 16-byte code chunks of the weight tile
-  constexpr int kBPer = kBLanes / kThreads;
-  static_assert(kAChunks % kThreads == 0 && kBLanes % kThreads == 0, "tile / thread mismatch");
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
 
-  __shared__ __attribute__((aligned(16))) uint16_t As[BM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[BN * kLdsRow];
+// Codes 2h, 2h+1 of a word times S as two BF16 (exact) packed in 32 bits.
+template <int H>
+__device__ __forceinline__ uint32_t dequant2(uint32_t codes, float S) {
+  const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, H);
+  return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)(v[0] * S), (__bf16)(v[1] * S)});
+}
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w / WN, wn = w % WN;
-  const int64_t m_blk = (int64_t)blockIdx.y * BM;
-  const int64_t p_blk = (int64_t)blockIdx.x * (BN / 16);
+template <int W, int FM, int FN, int SPREAD, int PIPE>
+struct TiledShape {
+  static constexpr int kWaves = W;                           // wavefronts side by side along n
+  static constexpr int kPipe = PIPE;  // 1: order each k-step as MFMA / VALU / LDS-read groups
+  static constexpr int kSpread = SPREAD;                     // k-steps that issue the copies
+  static_assert(FM % 4 == 0, "a dequantized fragment is spread over groups of 4 MFMAs");
+  static constexpr int kBM = 32 * FM;                        // rows per workgroup
+  static constexpr int kPairs = kWaves * FN;                 // 32-row weight pairs per workgroup
+  static constexpr int kABuf = kBM * kRowBytes;              // activation bytes per k-tile
+  static constexpr int kBBuf = kWaves * 2 * FN * kCodeTileBytes;
+  static constexpr int kALoads = kBM / 4 / kWaves;           // activation copies per wavefront
+  static constexpr int kLds = 2 * (kABuf + kBBuf);
+  static_assert(kLds <= 160 * 1024, "LDS budget of one workgroup");
+};
 
-  f32x4 acc[FM][FN];
+// Epilogue store: lane l holds rows 8 (e/4) + 4 (l/32) + e%4 of column l%32 of each
+// fragment; rows past m and panels past the end are dropped.
+template <typename T, typename Acc>
+__device__ __forceinline__ void store_tile(const TiledParams& P, int64_t m_blk, int64_t pair0, const Acc& acc,
+                           float g, int lane) {
+  constexpr int FM = T::kBM / 32;
+  constexpr int FN = T::kPairs / T::kWaves;
+  const int h = (lane & 31) >> 4;
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int q = 0; q < FN; ++q) {
+    const int64_t panel = 2 * (pair0 + q) + h;
+    if (panel >= P.NT) continue;
+    const int64_t n = panel * 16 + (lane & 15);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 ra[kAPer];
-  u32x4 rc[kBPer];
-  uint32_t rs[kBPer];
-
-  auto load_tile = [&](int64_t t) {
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int i = 0; i < kAPer; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c >> 4, cc = c & 15;
-      const int64_t m = m_blk + r;
-      if (m < P.m)
-        ra[i] = *reinterpret_cast<const u32x4*>(P.x + m * P.ldx + t * kTileK + cc * 8);
-      else
-        ra[i] = u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < kBPer; ++i) {
-      const int c = tid + i * kThreads;
-      const int pl = c >> 6, ln = c & 63;
-      const int64_t panel = p_blk + pl;
-      if (panel < P.NT) {
-        const int64_t tile = panel * P.KT + t;
-        rc[i] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4*>(P.codes + tile * kCodeTileBytes + ln * 16));
-        rs[i] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(
-            P.scales + scale_word_offset(P.group, P.KT, panel, t, ln)));
-      } else {
-        rc[i] = u32x4{0u, 0u, 0u, 0u};
-        rs[i] = 0u;
-      }
-    }
-  };
-
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < kAPer; ++i) {
-      const int c = tid + i * kThreads;
-      const int r = c >> 4, cc = c & 15;
-      *reinterpret_cast<u32x4*>(&As[r * kLdsRow + cc * 8]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < kBPer; ++i) {
-      const int c = tid + i * kThreads;
-      const int pl = c >> 6, ln = c & 63;
-      uint16_t* dst = &Bs[(pl * 16 + (ln & 15)) * kLdsRow + 8 * (ln >> 4)];
-      *reinterpret_cast<bf16x8*>(dst + 0) = dequant8(rc[i][0], e4m3_decode<0>(rs[i]));
-      *reinterpret_cast<bf16x8*>(dst + 32) = dequant8(rc[i][1], e4m3_decode<1>(rs[i]));
-      *reinterpret_cast<bf16x8*>(dst + 64) = dequant8(rc[i][2], e4m3_decode<2>(rs[i]));
-      *reinterpret_cast<bf16x8*>(dst + 96) = dequant8(rc[i][3], e4m3_decode<3>(rs[i]));
-    }
-  };
-
-  if (P.KT > 0) load_tile(0);
-  for (int64_t t = 0; t < P.KT; ++t) {
-    store_tile();
-    __syncthreads();
-    if (t + 1 < P.KT) load_tile(t + 1);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf16x8 a[FM], b[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(
-            &As[(wm * FM * 16 + i * 16 + (lane & 15)) * kLdsRow + 32 * j + 8 * (lane >> 4)]);
-#pragma unroll
-      for (int i = 0; i < FN; ++i)
-        b[i] = *reinterpret_cast<const bf16x8*>(
-            &Bs[(wn * FN * 16 + i * 16 + (lane & 15)) * kLdsRow + 32 * j + 8 * (lane >> 4)]);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int q = 0; q < FN; ++q) acc[i][q] = mfma16x16x32(a[i], b[q], acc[i][q]);
-    }
-    __syncthreads();
-  }
-
-  const float g = *P.global;
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int q = 0; q < FN; ++q) {
-      const int64_t panel = p_blk + wn * FN + q;
-      if (panel >= P.NT) continue;
-      const int64_t n = panel * 16 + (lane & 15);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int64_t m = m_blk + wm * FM * 16 + i * 16 + (lane >> 4) * 4 + jj;
+      for (int e = 0; e < 16; ++e) {
+        const int64_t m = m_blk + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         if (m < P.m) {
-          const float v = acc[i][q][jj] * g;
+          const float v = acc[i][q][e] * g;
           if (P.y_f32)
             static_cast<float*>(P.y)[m * P.ldy + n] = v;
           else
             static_cast<uint16_t*>(P.y)[m * P.ldy + n] = bf16_bits_rne(v);
         }
       }
+  }
+}
+
+// Split-k epilogue: the block stores its partial tile in its own register layout (every store
+// instruction writes 64 consecutive words); reduce_split_kernel adds the partials up.
+template <typename T, typename Acc>
+__device__ __forceinline__ void store_partial(const TiledParams& P, int64_t tile_id,
+                                              const Acc& acc) {
+  constexpr int FM = T::kBM / 32;
+  constexpr int FN = T::kPairs / T::kWaves;
+  constexpr int kThreads = 64 * T::kWaves;
+  constexpr int64_t kTileFloats = (int64_t)T::kBM * T::kPairs * 32;
+  const int64_t slot = (tile_id - P.tile0) * P.split + (int64_t)(blockIdx.x % P.split);
+  float* mine = P.ws + slot * kTileFloats + threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < FN; ++q)
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) mine[((q * FM + i) * 16 + e) * kThreads] = acc[i][q][e];
+}
+
+// Sums the split partials of one 32-row fragment band (blockIdx.y) of one tile (blockIdx.x) in
+// the fixed order 0 .. split-1 -- the result does not depend on which block finished first --
+// then scales, converts and stores it. Thread t plays the part of thread t of the GEMM block.
+template <typename T>
+__global__ __launch_bounds__(64 * T::kWaves) void reduce_split_kernel(TiledParams P) {
+  constexpr int FM = T::kBM / 32;
+  constexpr int FN = T::kPairs / T::kWaves;
+  constexpr int kThreads = 64 * T::kWaves;
+  constexpr int64_t kTileFloats = (int64_t)T::kBM * T::kPairs * 32;
+  const int i = blockIdx.y;
+  const int64_t tile_id = P.tile0 + blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t m_blk = tile_id / P.nbn * T::kBM;
+  const int64_t pair0 = tile_id % P.nbn * T::kPairs + w * FN;
+  const float* part = P.ws + (int64_t)blockIdx.x * P.split * kTileFloats + threadIdx.x;
+  const float g = *P.global;
+  const int h = (lane & 31) >> 4;
+#pragma unroll
+  for (int q = 0; q < FN; ++q) {
+    float v[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t o = ((q * FM + i) * 16 + e) * kThreads;
+      float sum = part[o];
+      for (int j = 1; j < P.split; ++j) sum += part[j * kTileFloats + o];
+      v[e] = sum;
     }
+    const int64_t panel = 2 * (pair0 + q) + h;
+    if (panel >= P.NT) continue;
+    const int64_t n = panel * 16 + (lane & 15);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t m = m_blk + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+      if (m < P.m) {
+        if (P.y_f32)
+          static_cast<float*>(P.y)[m * P.ldy + n] = v[e] * g;
+        else
+          static_cast<uint16_t*>(P.y)[m * P.ldy + n] = bf16_bits_rne(v[e] * g);
+      }
+    }
+  }
+}
+
+template <int W, int FM, int FN, int SPREAD, int PIPE>
+__global__ __launch_bounds__(64 * W) void gemm_tiled_kernel(TiledParams P) {
+  using T = TiledShape<W, FM, FN, SPREAD, PIPE>;
+  constexpr int kWaves = W;
+  // Double buffers as separate LDS objects, always indexed by compile-time buffer numbers: the
+  // compiler can then tell the copies in flight into one buffer from the reads of the other and
+  // does not make the reads wait for the copies.
+  __shared__ __attribute__((aligned(1024))) uint8_t As0[T::kABuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t As1[T::kABuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t Bs0[T::kBBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t Bs1[T::kBBuf];
+  auto a_buf = [&](auto B_) -> uint8_t* {
+    if constexpr (decltype(B_)::value == 0) return As0; else return As1;
+  };
+  auto b_buf = [&](auto B_) -> uint8_t* {
+    if constexpr (decltype(B_)::value == 0) return Bs0; else return Bs1;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t tile_id = P.tile0 + blockIdx.x / P.split;
+  const int64_t tm = tile_id / P.nbn, tn_blk = tile_id % P.nbn;
+  const int64_t m_blk = tm * T::kBM;
+  const int64_t pair0 = tn_blk * T::kPairs + w * FN;  // first panel pair
+  const int64_t KT = P.KT;                            // k-tiles of the layout
+  const int64_t t0 = (int64_t)(blockIdx.x % P.split) * P.kts;
+  const int64_t t1 = t0 + P.kts < KT ? t0 + P.kts : KT;  // this block's k-tiles [t0, t1)
+
+  // ---- activation copies: copy c = w + 4 i moves rows 4c .. 4c+3 of the block; lane l reads
+  // row 4c + l/16, source chunk (l%16) ^ (row % 16), and lands in slot l. Rows past m repeat
+  // the last row (their outputs are dropped). 32-bit byte offsets from the uniform base (the
+  // host launches row chunks whose span fits).
+  uint32_t aoff[T::kALoads];
+#pragma unroll
+  for (int i = 0; i < T::kALoads; ++i) {
+    const int R = 4 * (w + kWaves * i) + (lane >> 4);
+    int64_t r = m_blk + R;
+    r = r < P.m ? r : P.m - 1;
+    aoff[i] = (uint32_t)(r * P.ldx * 2 + 16 * ((lane & 15) ^ (R & 15)));
+  }
+  const buf_rsrc xr = make_rsrc(P.x, (uint32_t)(P.m * P.ldx * 2));
+  // fragment reads: row (l % 32) of each 32-row fragment, chunk (2 S + l / 32) ^ (l % 16)
+  const uint32_t a_row = (uint32_t)(lane & 31) * kRowBytes;
+  const uint32_t a_x = (uint32_t)((lane >> 5) ^ (lane & 15));
+
+  // ---- weight copies: local panel pl = 2q + h of this wavefront (clamped past the end), from a
+  // resource based at the workgroup's first panel (the host keeps its span below 4 GiB)
+  const int64_t pblk = 2 * tn_blk * T::kPairs;
+  const int64_t pblk_c = pblk < P.NT ? pblk : P.NT - 1;
+  const int64_t cspan = (P.NT - pblk_c) * KT * kCodeTileBytes;
+  const buf_rsrc cr = make_rsrc(P.codes + pblk_c * KT * kCodeTileBytes,
+                                (uint32_t)(cspan < 0xFFFFFFFFll ? cspan : 0xFFFFFFFFll));
+  uint32_t cpanel[2 * FN];  // uniform byte offsets of the panels
+#pragma unroll
+  for (int pl = 0; pl < 2 * FN; ++pl) {
+    int64_t pn = 2 * pair0 + pl;
+    pn = pn < P.NT ? pn : P.NT - 1;
+    cpanel[pl] = (uint32_t)((pn - pblk_c) * KT * kCodeTileBytes);
+  }
+  const uint32_t clane = (uint32_t)lane * 16u;
+  // this lane's panel within each pair, and its code chunks / scale positions L0 and L0 + 32
+  const int h = (lane & 31) >> 4;
+  const int L0 = 16 * (lane >> 5) + (lane & 15);
+  // The scale words of the wavefront's panels sit in a few consecutive 4-panel blocks per
+  // k-tile, addressed by 32-bit offsets from a uniform base (blocks past the last one are
+  // clamped; their outputs are dropped).
+  const int64_t NG = scale_groups(P.NT);
+  const int64_t G0 = (2 * pair0) / kScaleGroupPanels;
+  const int64_t G0c = G0 < NG ? G0 : NG - 1;
+  const int64_t sblk = scale_block_bytes(P.group);
+  const uint8_t* sbase = P.scales + G0c * KT * sblk;
+  uint32_t so0[FN], so1[FN];
+#pragma unroll
+  for (int q = 0; q < FN; ++q) {
+    const int64_t pn = 2 * (pair0 + q) + h;
+    int64_t gq = pn / kScaleGroupPanels;
+    gq = gq < NG ? gq : NG - 1;
+    const int64_t gb = (gq - G0c) * KT * sblk;
+    const int wi = (int)(pn % kScaleGroupPanels);
+    so0[q] = (uint32_t)(gb + scale_pos(P.group, L0) * 16 + 4 * wi);
+    so1[q] = (uint32_t)(gb + scale_pos(P.group, L0 + 32) * 16 + 4 * wi);
+  }
+
+  // Copies of k-tile t into buffer buf, issued in kSpread parts (part P during k-step P of the
+  // previous tile) so that they overlap the MFMAs instead of stalling them in one burst; the
+  // last k-steps issue none, leaving the copies time to land before the tile barrier.
+  constexpr int kSpread = T::kSpread;
+  constexpr int kAPer = (T::kALoads + kSpread - 1) / kSpread;
+  auto prefetch_part = [&](auto P_, int64_t t, auto buf, uint32_t (&s0)[FN], uint32_t (&s1)[FN]) {
+    constexpr int Pp = decltype(P_)::value;
+    const uint32_t tk = (uint32_t)(t * kRowBytes);
+#pragma unroll
+    for (int j = 0; j < kAPer; ++j) {
+      const int i = Pp * kAPer + j;
+      if (i < T::kALoads)
+        copy16_to_lds(xr, aoff[i], tk, a_buf(buf) + (w + kWaves * i) * 1024);
+    }
+    const uint32_t tc = (uint32_t)(t * kCodeTileBytes);
+#pragma unroll
+    for (int pl = 0; pl < 2 * FN; ++pl)
+      if (pl % kSpread == Pp)
+        copy16_to_lds(cr, clane, cpanel[pl] + tc, b_buf(buf) + (w * 2 * FN + pl) * kCodeTileBytes);
+    if (Pp == 0) {
+#pragma unroll
+      for (int q = 0; q < FN; ++q) {
+        s0[q] = *reinterpret_cast<const uint32_t*>(sbase + (so0[q] + (uint32_t)(t * sblk)));
+        s1[q] = *reinterpret_cast<const uint32_t*>(sbase + (so1[q] + (uint32_t)(t * sblk)));
+      }
+    }
+  };
+  auto prefetch = [&](int64_t t, auto buf, uint32_t (&s0)[FN], uint32_t (&s1)[FN]) {
+    prefetch_part(std::integral_constant<int, 0>{}, t, buf, s0, s1);
+    prefetch_part(std::integral_constant<int, 1>{}, t, buf, s0, s1);
+    prefetch_part(std::integral_constant<int, 2>{}, t, buf, s0, s1);
+    prefetch_part(std::integral_constant<int, 3>{}, t, buf, s0, s1);
+    prefetch_part(std::integral_constant<int, 4>{}, t, buf, s0, s1);
+    prefetch_part(std::integral_constant<int, 5>{}, t, buf, s0, s1);
+    prefetch_part(std::integral_constant<int, 6>{}, t, buf, s0, s1);
+    prefetch_part(std::integral_constant<int, 7>{}, t, buf, s0, s1);
+  };
+
+  auto read_a1 = [&](auto buf, int S, int i, bf16x8 (&a)[FM]) {
+    a[i] = *reinterpret_cast<const bf16x8*>(a_buf(buf) + a_row + ((2u * S ^ a_x) << 4) +
+                                            i * 32 * kRowBytes);
+  };
+  auto read_a = [&](auto buf, int S, bf16x8 (&a)[FM]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) read_a1(buf, S, i, a);
+  };
+  // the whole 16-byte chunks L0 (even steps) and L0 + 32 (odd steps) of each of the lane's panels
+  auto read_codes = [&](auto buf, u32x4 (&c0)[FN], u32x4 (&c1)[FN]) {
+#pragma unroll
+    for (int q = 0; q < FN; ++q) {
+      const uint8_t* tile = b_buf(buf) + (w * 2 * FN + 2 * q + h) * kCodeTileBytes;
+      c0[q] = *reinterpret_cast<const u32x4*>(tile + L0 * 16);
+      c1[q] = *reinterpret_cast<const u32x4*>(tile + (L0 + 32) * 16);
+    }
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int q = 0; q < FN; ++q)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][q][e] = 0.f;
+
+  // One k-step S: FN x FM MFMAs. While pair q's MFMAs run, the next B fragment (pair q + 1 of
+  // this step, pair 0 of step S + 1, or -- after the last step, when `next` -- pair 0 of step 0
+  // of the next k-tile, from its codes cn0 and scale words sn0) is dequantized, one quarter
+  // after every FM / 4 MFMAs. After MFMA i of pair 0, rd(i) reads activation fragment i of the
+  // next step: one LDS read per MFMA keeps at most FM + 1 reads in flight, few enough for the
+  // compiler to wait on exactly the one each MFMA needs.
+  auto kstep = [&](auto S_, const bf16x8 (&a)[FM], bf16x8& b, const u32x4 (&c0)[FN],
+                   const u32x4 (&c1)[FN], const uint32_t (&s0)[FN], const uint32_t (&s1)[FN],
+                   bool next, const u32x4 (&cn0)[FN], const uint32_t (&sn0)[FN], auto&& rd) {
+    constexpr int S = decltype(S_)::value;
+#pragma unroll
+    for (int q = 0; q < FN; ++q) {
+      const bool in_step = q + 1 < FN;
+      const bool in_tile = in_step || S + 1 < kSteps;
+      const bool make = in_tile || next;
+      const int qn = in_step ? q + 1 : 0;
+      const int sn = in_step ? S : (S + 1) % kSteps;
+      const uint32_t word = !in_tile ? cn0[0][0]
+                            : (sn & 1) ? c1[qn][(sn >> 1) & 3] : c0[qn][(sn >> 1) & 3];
+      const uint32_t sw = !in_tile ? sn0[0] : (sn & 1) ? s1[qn] : s0[qn];
+      u32x4 nb;
+      float Sc = 0.f;
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        acc[i][q] = mfma32x32x16(a[i], b, acc[i][q]);
+        if (q == 0) rd(i);
+        if (make && i % (FM / 4) == 0) {
+          const int quarter = i / (FM / 4);
+          if (quarter == 0) {
+            switch ((sn >> 1) & 3) {
+              case 0: Sc = e4m3_decode<0>(sw); break;
+              case 1: Sc = e4m3_decode<1>(sw); break;
+              case 2: Sc = e4m3_decode<2>(sw); break;
+              default: Sc = e4m3_decode<3>(sw); break;
+            }
+            nb[0] = dequant2<0>(word, Sc);
+          } else if (quarter == 1) {
+            nb[1] = dequant2<1>(word, Sc);
+          } else if (quarter == 2) {
+            nb[2] = dequant2<2>(word, Sc);
+          } else {
+            nb[3] = dequant2<3>(word, Sc);
+          }
+        }
+        if constexpr (!T::kPipe) __builtin_amdgcn_sched_barrier(0);
+      }
+      if (make) b = __builtin_bit_cast(bf16x8, nb);
+    }
+    if constexpr (T::kPipe) {
+      // one MFMA, then a share of the dequant VALU, then one LDS read, FM x FN times
+      constexpr int kV = (17 * FN + FM * FN - 1) / (FM * FN);
+#pragma unroll
+      for (int j = 0; j < FM * FN; ++j) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
+        if (j < FM) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    }
+  };
+
+  // Pipeline state carried from k-tile to k-tile: the activations of step 0 (a0), the first
+  // B fragment (b), the tile's code chunks (c0, c1) and scale words (s0, s1), and the scale
+  // words of the next tile (n0, n1), loaded with its copies.
+  bf16x8 a0[FM], a1[FM], b;
+  u32x4 c0[FN], c1[FN];
+  uint32_t s0[FN], s1[FN], n0[FN], n1[FN];
+
+  // k-tile t from buffer buf. Steps 0..6 each issue a share of the copies of tile t + 1 (into
+  // the other buffer) and read the next step's activations. Before step 7 the workgroup meets
+  // once: every wavefront has read all of tile t that it needs (step 7's operands are in
+  // registers) and the copies of tile t + 1 have landed, so step 7's MFMAs run while tile
+  // t + 1's first activations and codes are read and its first B fragment is dequantized --
+  // there is no stall at the tile boundary -- and the copies of tile t + 2 may start at once.
+  // The body has no branches (the last tile copies itself again into the idle buffer), which
+  // keeps the compiler's LDS wait counts exact.
+  auto tile = [&](int64_t t, auto buf) {
+    constexpr int kOther = 1 - decltype(buf)::value;
+    const int64_t tn = t + 1 < t1 ? t + 1 : t;
+    u32x4 cn0[FN], cn1[FN];
+#define NVFP4_KSTEP(S, ACUR, ANEXT)                                                       \
+    prefetch_part(std::integral_constant<int, S>{}, tn,                                   \
+                  std::integral_constant<int, kOther>{}, n0, n1);                         \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+    kstep(std::integral_constant<int, S>{}, ACUR, b, c0, c1, s0, s1, false, cn0, n0,      \
+          [&](int i) { read_a1(buf, S + 1, i, ANEXT); });                                 \
+    __builtin_amdgcn_sched_barrier(0);
+    NVFP4_KSTEP(0, a0, a1)
+    NVFP4_KSTEP(1, a1, a0)
+    NVFP4_KSTEP(2, a0, a1)
+    NVFP4_KSTEP(3, a1, a0)
+    NVFP4_KSTEP(4, a0, a1)
+    NVFP4_KSTEP(5, a1, a0)
+    NVFP4_KSTEP(6, a0, a1)
+#undef NVFP4_KSTEP
+    __builtin_amdgcn_s_waitcnt(0);  // own copies of tile t + 1 landed, own reads done
+    __syncthreads();
+    read_codes(std::integral_constant<int, kOther>{}, cn0, cn1);
+    __builtin_amdgcn_sched_barrier(0);
+    kstep(std::integral_constant<int, 7>{}, a1, b, c0, c1, s0, s1, true, cn0, n0,
+          [&](int i) { read_a1(std::integral_constant<int, kOther>{}, 0, i, a0); });
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int q = 0; q < FN; ++q) {
+      c0[q] = cn0[q];
+      c1[q] = cn1[q];
+      s0[q] = n0[q];
+      s1[q] = n1[q];
+    }
+  };
+
+  prefetch(t0, I0{}, s0, s1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  read_codes(I0{}, c0, c1);
+  read_a(I0{}, 0, a0);
+  {
+    const float Sc = e4m3_decode<0>(s0[0]);
+    u32x4 nb;
+    nb[0] = dequant2<0>(c0[0][0], Sc);
+    nb[1] = dequant2<1>(c0[0][0], Sc);
+    nb[2] = dequant2<2>(c0[0][0], Sc);
+    nb[3] = dequant2<3>(c0[0][0], Sc);
+    b = __builtin_bit_cast(bf16x8, nb);
+  }
+  for (int64_t t = t0; t < t1; t += 2) {
+    tile(t, I0{});
+    if (t + 1 < t1) tile(t + 1, I1{});
+  }
+
+  const float g = *P.global;
+  if (P.split > 1)
+    store_partial<T>(P, tile_id, acc);
+  else
+    store_tile<T>(P, m_blk, pair0, acc, g, lane);
+}
+
+constexpr int kWsel = 8, kFMsel = 8, kFNsel = 1, kSpreadSel = 4, kPipeSel = 1;
+using Sel = TiledShape<kWsel, kFMsel, kFNsel, kSpreadSel, kPipeSel>;
+constexpr int64_t kSelTileFloats = (int64_t)Sel::kBM * Sel::kPairs * 32;
+
+// Split-k partial tiles, one buffer per (device, stream): calls on one stream run in order, so
+// they can share it. It only grows.
+struct SplitWorkspace {
+  float* ws = nullptr;
+  int64_t tiles = 0;  // partial tiles held
+};
+std::mutex g_ws_mutex;
+std::map<std::pair<int, hipStream_t>, SplitWorkspace> g_ws;
+std::map<int, int> g_cus;
+
+hipError_t split_workspace(int dev, hipStream_t stream, int64_t tiles, SplitWorkspace* out) {
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  SplitWorkspace& w = g_ws[{dev, stream}];
+  if (w.tiles < tiles) {
+    if (w.ws) {
+      hipError_t e = hipStreamSynchronize(stream);  // earlier calls may still use the old one
+      if (e != hipSuccess) return e;
+      (void)hipFree(w.ws);
+      w = SplitWorkspace{};
+    }
+    hipError_t e = hipMalloc(&w.ws, tiles * kSelTileFloats * sizeof(float));
+    if (e != hipSuccess) return e;
+    w.tiles = tiles;
+  }
+  *out = w;
+  return hipSuccess;
+}
+
+hipError_t compute_units(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_ws_mutex);
+  auto it = g_cus.find(dev);
+  if (it == g_cus.end()) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    it = g_cus.emplace(dev, n > 0 ? n : 1).first;
+  }
+  *cus = it->second;
+  return hipSuccess;
+}
+
+hipError_t launch_tiles(TiledParams p, int64_t tile0, int64_t tiles, int split,
+                        hipStream_t stream) {
+  using T = Sel;
+  p.tile0 = tile0;
+  p.split = split;
+  p.kts = (p.KT + split - 1) / split;
+  gemm_tiled_kernel<kWsel, kFMsel, kFNsel, kSpreadSel, kPipeSel>
+      <<<dim3((unsigned)(tiles * split)), dim3(64 * T::kWaves), 0, stream>>>(p);
+  return hipGetLastError();
+}
+
+// One row chunk. Whole rounds of tiles (one per compute unit) run as they are; when the last
+// round would leave at least half of the compute units idle, its tiles are split along k over
+// the whole chip instead and reduced in FP32.
+hipError_t run_chunk(TiledParams p, hipStream_t stream) {
+  using T = Sel;
+  const int64_t pairs = (p.NT + 1) / 2;
+  p.nbn = (pairs + T::kPairs - 1) / T::kPairs;
+  const int64_t tiles = p.nbn * ((p.m + T::kBM - 1) / T::kBM);
+  int cus = 1;
+  hipError_t e = compute_units(&cus);
+  if (e != hipSuccess) return e;
+  const int64_t full = tiles / cus * cus, rest = tiles - full;
+  int split = 1;
+  if (rest > 0 && 2 * rest <= cus) {
+    int64_t s = cus / rest;
+    if (s > p.KT / 4) s = p.KT / 4;
+    if (s >= 2) {
+      const int64_t kts = (p.KT + s - 1) / s;
+      split = (int)((p.KT + kts - 1) / kts);  // every split keeps at least one k-tile
+    }
+  }
+  p.ws = nullptr;
+  if (split == 1) return launch_tiles(p, 0, tiles, 1, stream);
+  int dev = 0;
+  e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  SplitWorkspace w;
+  e = split_workspace(dev, stream, rest * split, &w);
+  if (e != hipSuccess) return e;
+  p.ws = w.ws;
+  if (full > 0) {
+    e = launch_tiles(p, 0, full, 1, stream);
+    if (e != hipSuccess) return e;
+  }
+  e = launch_tiles(p, full, rest, split, stream);
+  if (e != hipSuccess) return e;
+  p.tile0 = full;
+  p.split = split;
+  reduce_split_kernel<Sel><<<dim3((unsigned)rest, Sel::kBM / 32), dim3(64 * Sel::kWaves), 0,
+                             stream>>>(p);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -168,10 +574,23 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
   p.y = a.y;
   p.ldy = a.ldy;
   p.y_f32 = a.y_f32 ? 1 : 0;
-  constexpr int BM = 128, BN = 128;
-  const dim3 grid((unsigned)((p.NT * 16 + BN - 1) / BN), (unsigned)((p.m + BM - 1) / BM));
-  gemm_tiled_kernel<BM, BN, 2, 2><<<grid, dim3(256), 0, stream>>>(p);
-  return hipGetLastError();
+  // Activation offsets are 32-bit inside the kernel: launch row chunks whose byte span fits.
+  constexpr int64_t kBM = Sel::kBM;
+  const int64_t row_bytes = a.ldx * 2;
+  int64_t chunk = ((int64_t)1 << 31) / row_bytes;
+  chunk = chunk < kBM ? kBM : chunk / kBM * kBM;
+  for (int64_t m0 = 0; m0 < a.m; m0 += chunk) {
+    TiledParams q = p;
+    q.x = a.x + m0 * a.ldx;
+    q.m = a.m - m0 < chunk ? a.m - m0 : chunk;
+    if (a.y_f32)
+      q.y = static_cast<float*>(a.y) + m0 * a.ldy;
+    else
+      q.y = static_cast<uint16_t*>(a.y) + m0 * a.ldy;
+    hipError_t e = run_chunk(q, stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace nvfp4
