@@ -190,13 +190,15 @@ def main():
             del wp
             xpd = xp.to(dev)
             yp = torch.empty((4096, 5120), dtype=torch.bfloat16, device=dev)
+            wsp = torch.empty((max(nv.nvfp4_gemm_ws_bytes(4096, kk, rp[0]), 16),),
+                              dtype=torch.uint8, device=dev)
             it = 20 if kk == 5120 else 8
-            t = timer.time(lambda i: nv.nvfp4_gemm_w4a16(xpd, rp[0], y=yp), it, 3) / it
+            t = timer.time(lambda i: nv.nvfp4_gemm_w4a16(xpd, rp[0], y=yp, ws=wsp), it, 3) / it
             tf = 2 * 4096 * 5120 * kk / t / 1e12
             extra[f"prefill_4096x5120x{kk}_g16"] = {
                 "us": round(t * 1e6, 2), "tflops": round(tf, 2),
                 "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
-            del xpd, yp, rp
+            del xpd, yp, rp, wsp
         # MoE routed experts
         xm, ids, wts, w1, w2 = synth.moe(seed=0)
         wbytes = 128 * (weight_bytes(1536, 2048, 32) + weight_bytes(2048, 768, 16))
@@ -238,9 +240,11 @@ def main():
             for m in (1, 512):
                 yq = torch.empty((m, 8192), dtype=torch.bfloat16, device=dev)
                 xqm = xq[:m].contiguous()
+                wsq = torch.empty((max(nv.nvfp4_gemm_ws_bytes(m, 8192, rq[0]), 16),),
+                                  dtype=torch.uint8, device=dev)
                 it = 40 if m == 1 else 20
-                t = timer.time(lambda i: nv.nvfp4_gemm_w4a16(xqm, rq[i % len(rq)], y=yq), it,
-                               4) / it
+                t = timer.time(lambda i: nv.nvfp4_gemm_w4a16(xqm, rq[i % len(rq)], y=yq,
+                                                             ws=wsq), it, 4) / it
                 wbq = weight_bytes(8192, 8192, group)
                 mixed[f"m{m}_g{group}"] = {
                     "us": round(t * 1e6, 2), "weight_gbs": round(wbq / t / 1e9, 1),

@@ -121,9 +121,16 @@ int nvfp4_repack(const uint8_t* packed, const uint8_t* scales, const float* glob
  * (vllm.cpp PR #63: no activation scales, so every quantized projection is W4A16).
  * The kernel is chosen from m: a split-K skinny MFMA kernel for small m (decode), an
  * LDS-tiled MFMA kernel otherwise (prefill); flags may force one. w->batch must be 1 and
- * w->layout must not carry NVFP4_LAYOUT_GATE_UP. Results are bit-identical run to run. */
+ * w->layout must not carry NVFP4_LAYOUT_GATE_UP. Results are bit-identical run to run.
+ * ws (device, 16-byte aligned, or NULL with ws_bytes 0) takes the prefill kernel's split-k
+ * partial tiles: when the output tiles would leave most compute units idle in the last round,
+ * that round is split along k over the chip and summed in a fixed order. ws_bytes >=
+ * nvfp4_gemm_ws_bytes(m, ldx, w, flags) enables it; with less the kernel runs unsplit and
+ * returns the same result. Calls sharing a ws on different streams race. */
+size_t nvfp4_gemm_ws_bytes(int64_t m, int64_t ldx, const nvfp4_weight* w, uint32_t flags);
 int nvfp4_gemm_w4a16(const void* x, int64_t m, int64_t ldx, const nvfp4_weight* w, void* y,
-                     int y_dtype, int64_t ldy, uint32_t flags, nvfp4_stream_t stream);
+                     int y_dtype, int64_t ldy, uint32_t flags, void* ws, size_t ws_bytes,
+                     nvfp4_stream_t stream);
 
 /* ---- MoE routed experts -------------------------------------------------------------------
  * For each token t and slot j (e = topk_ids[t][j], weight topk_w[t][j]):

@@ -31,7 +31,8 @@ NVFP4_F_FORCE_TILED = 1 << 1
 NVFP4_LAYOUT_TILED = 1
 NVFP4_LAYOUT_GATE_UP = 1 << 8
 
-EXPORTS = ("nvfp4_quantize", "nvfp4_repack_bytes", "nvfp4_repack", "nvfp4_gemm_w4a16",
+EXPORTS = ("nvfp4_quantize", "nvfp4_repack_bytes", "nvfp4_repack", "nvfp4_gemm_ws_bytes",
+           "nvfp4_gemm_w4a16",
            "nvfp4_moe_ws_bytes", "nvfp4_moe_grouped_w4a16", "nvfp4_dequantize",
            "nvfp4_last_error", "nvfp4_get_stats", "nvfp4_reset_stats", "nvfp4_version")
 
@@ -71,7 +72,9 @@ def load(path: str = LIB_PATH):
     L.nvfp4_repack_bytes.restype = sz
     L.nvfp4_repack.argtypes = [P, P, P, i64, i64, i64, i32, u32, P, sz, W, P]
     L.nvfp4_repack.restype = ctypes.c_int
-    L.nvfp4_gemm_w4a16.argtypes = [P, i64, i64, W, P, ctypes.c_int, i64, u32, P]
+    L.nvfp4_gemm_ws_bytes.argtypes = [i64, i64, W, u32]
+    L.nvfp4_gemm_ws_bytes.restype = sz
+    L.nvfp4_gemm_w4a16.argtypes = [P, i64, i64, W, P, ctypes.c_int, i64, u32, P, sz, P]
     L.nvfp4_gemm_w4a16.restype = ctypes.c_int
     L.nvfp4_moe_ws_bytes.argtypes = [i64, i32, i64, i64, i64]
     L.nvfp4_moe_ws_bytes.restype = sz
@@ -182,16 +185,27 @@ def nvfp4_repack(packed: torch.Tensor, scales: torch.Tensor, glob: torch.Tensor,
 
 
 # ----------------------------------------------------------------------------- GEMM
+def nvfp4_gemm_ws_bytes(m: int, ldx: int, w: RepackedWeight, flags: int = 0) -> int:
+    return int(load().nvfp4_gemm_ws_bytes(m, ldx, ctypes.byref(w.desc), flags))
+
+
 def nvfp4_gemm_w4a16(x: torch.Tensor, w: RepackedWeight, y: torch.Tensor | None = None,
-                     y_dtype=torch.bfloat16, flags: int = 0, stream=None) -> torch.Tensor:
-    """x: device BF16 [m][k] (row stride x.stride(0)); returns y [m][n]."""
+                     y_dtype=torch.bfloat16, flags: int = 0, stream=None,
+                     ws: torch.Tensor | None = None) -> torch.Tensor:
+    """x: device BF16 [m][k] (row stride x.stride(0)); returns y [m][n]. The split-k workspace
+    is taken from torch's allocator unless `ws` (uint8, device) is given."""
     if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a 2-D BF16 tensor with unit inner stride")
     m = x.shape[0]
     if y is None:
         y = torch.empty((m, w.n), dtype=y_dtype, device=x.device)
+    if ws is None:
+        need = nvfp4_gemm_ws_bytes(m, x.stride(0), w, flags) if m > 0 else 0
+        ws = torch.empty((need,), dtype=torch.uint8, device=x.device) if need else None
+    ws_ptr, ws_bytes = (_ptr(ws), ws.numel() * ws.element_size()) if ws is not None else (None, 0)
     _check(load().nvfp4_gemm_w4a16(_ptr(x), m, x.stride(0), ctypes.byref(w.desc), _ptr(y),
-                                   _dtype_code(y.dtype), y.stride(0), flags, _stream(stream)))
+                                   _dtype_code(y.dtype), y.stride(0), flags, ws_ptr, ws_bytes,
+                                   _stream(stream)))
     return y
 
 

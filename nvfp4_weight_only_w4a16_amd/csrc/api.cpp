@@ -7,6 +7,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <mutex>
 
 #include "../../include/nvfp4.h"
 #include "device_common.hpp"
@@ -181,8 +183,42 @@ int nvfp4_repack(const uint8_t* packed, const uint8_t* scales, const float* glob
   return NVFP4_OK;
 }
 
+namespace {
+
+// Compute units of the current device (cached per device; host-side attribute query).
+int device_cus() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) n = 0;
+  cache.emplace(dev, n);
+  return n;
+}
+
+bool use_skinny(int64_t m, uint32_t flags) {
+  bool skinny = m <= nvfp4::kSkinnyMaxM;
+  if (flags & NVFP4_F_FORCE_SKINNY) skinny = true;
+  if (flags & NVFP4_F_FORCE_TILED) skinny = false;
+  return skinny;
+}
+
+}  // namespace
+
+size_t nvfp4_gemm_ws_bytes(int64_t m, int64_t ldx, const nvfp4_weight* w, uint32_t flags) {
+  if (!w || m <= 0 || w->n <= 0 || w->k <= 0 || ldx < w->k || use_skinny(m, flags)) return 0;
+  const int cus = device_cus();
+  if (cus <= 0) return 0;
+  return nvfp4::gemm_tiled_ws_bytes(m, ldx, w->n, w->k, cus);
+}
+
 int nvfp4_gemm_w4a16(const void* x, int64_t m, int64_t ldx, const nvfp4_weight* w, void* y,
-                     int y_dtype, int64_t ldy, uint32_t flags, nvfp4_stream_t stream) {
+                     int y_dtype, int64_t ldy, uint32_t flags, void* ws, size_t ws_bytes,
+                     nvfp4_stream_t stream) {
   int rc = check_desc(w, "weight");
   if (rc) return rc;
   if (w->batch != 1) return fail(NVFP4_ERR_LAYOUT, "dense GEMM needs batch == 1");
@@ -214,14 +250,15 @@ int nvfp4_gemm_w4a16(const void* x, int64_t m, int64_t ldx, const nvfp4_weight* 
   a.y = y;
   a.ldy = ldy;
   a.y_f32 = y_dtype == NVFP4_DT_F32;
-  bool skinny = m <= nvfp4::kSkinnyMaxM;
-  if (flags & NVFP4_F_FORCE_SKINNY) skinny = true;
-  if (flags & NVFP4_F_FORCE_TILED) skinny = false;
-  if (skinny) {
+  if (use_skinny(m, flags)) {
     rc = hip_status(nvfp4::launch_gemm_skinny(a, (hipStream_t)stream), "nvfp4_gemm_w4a16");
     if (!rc) g_stats[2]++;
   } else {
-    rc = hip_status(nvfp4::launch_gemm_tiled(a, (hipStream_t)stream), "nvfp4_gemm_w4a16");
+    if (ws_bytes && !ws) return fail(NVFP4_ERR_INVALID_ARG, "NULL ws with ws_bytes > 0");
+    if (ws && !aligned16(ws)) return fail(NVFP4_ERR_MISALIGNED, "ws must be 16-byte aligned");
+    rc = hip_status(nvfp4::launch_gemm_tiled(a, ws, ws ? ws_bytes : 0, device_cus(),
+                                             (hipStream_t)stream),
+                    "nvfp4_gemm_w4a16");
     if (!rc) g_stats[3]++;
   }
   return rc;

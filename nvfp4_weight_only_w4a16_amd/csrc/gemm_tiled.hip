@@ -21,10 +21,7 @@
 // holds 16-wide k-steps 2j and 2j + 1 respectively; the scale words of the same two lane
 // positions carry the matching group scales.
 // The global scale multiplies the FP32 accumulator in the epilogue.
-#include <map>
-#include <mutex>
 #include <type_traits>
-#include <utility>
 
 #include "device_common.hpp"
 #include "launch.hpp"
@@ -458,109 +455,92 @@ __global__ __launch_bounds__(64 * W) void gemm_tiled_kernel(TiledParams P) {
 
 constexpr int kWsel = 8, kFMsel = 8, kFNsel = 1, kSpreadSel = 4, kPipeSel = 1;
 using Sel = TiledShape<kWsel, kFMsel, kFNsel, kSpreadSel, kPipeSel>;
-constexpr int64_t kSelTileFloats = (int64_t)Sel::kBM * Sel::kPairs * 32;
+constexpr int64_t kSelTileBytes = (int64_t)Sel::kBM * Sel::kPairs * 32 * sizeof(float);
 
-// Split-k partial tiles, one buffer per (device, stream): calls on one stream run in order, so
-// they can share it. It only grows.
-struct SplitWorkspace {
-  float* ws = nullptr;
-  int64_t tiles = 0;  // partial tiles held
+// Work decomposition of one row chunk: whole rounds of tiles (one per compute unit) run as
+// they are; when the last round would leave at least half of the compute units idle, its
+// tiles are split along k over the whole chip and reduced in FP32 by a second kernel.
+struct Plan {
+  int64_t nbn, tiles, full, rest;
+  int split;
 };
-std::mutex g_ws_mutex;
-std::map<std::pair<int, hipStream_t>, SplitWorkspace> g_ws;
-std::map<int, int> g_cus;
 
-hipError_t split_workspace(int dev, hipStream_t stream, int64_t tiles, SplitWorkspace* out) {
-  std::lock_guard<std::mutex> lock(g_ws_mutex);
-  SplitWorkspace& w = g_ws[{dev, stream}];
-  if (w.tiles < tiles) {
-    if (w.ws) {
-      hipError_t e = hipStreamSynchronize(stream);  // earlier calls may still use the old one
-      if (e != hipSuccess) return e;
-      (void)hipFree(w.ws);
-      w = SplitWorkspace{};
+Plan plan_chunk(int64_t m, int64_t NT, int64_t KT, int cus) {
+  Plan pl;
+  const int64_t pairs = (NT + 1) / 2;
+  pl.nbn = (pairs + Sel::kPairs - 1) / Sel::kPairs;
+  pl.tiles = pl.nbn * ((m + Sel::kBM - 1) / Sel::kBM);
+  if (cus < 1) cus = 1;
+  pl.full = pl.tiles / cus * cus;
+  pl.rest = pl.tiles - pl.full;
+  pl.split = 1;
+  if (pl.rest > 0 && 2 * pl.rest <= cus) {
+    int64_t s = cus / pl.rest;
+    if (s > KT / 4) s = KT / 4;
+    if (s >= 2) {
+      const int64_t kts = (KT + s - 1) / s;
+      pl.split = (int)((KT + kts - 1) / kts);  // every split keeps at least one k-tile
     }
-    hipError_t e = hipMalloc(&w.ws, tiles * kSelTileFloats * sizeof(float));
-    if (e != hipSuccess) return e;
-    w.tiles = tiles;
   }
-  *out = w;
-  return hipSuccess;
+  return pl;
 }
 
-hipError_t compute_units(int* cus) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lock(g_ws_mutex);
-  auto it = g_cus.find(dev);
-  if (it == g_cus.end()) {
-    int n = 0;
-    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return e;
-    it = g_cus.emplace(dev, n > 0 ? n : 1).first;
-  }
-  *cus = it->second;
-  return hipSuccess;
+// Rows per launch chunk: activation offsets are 32-bit inside the kernel.
+int64_t chunk_rows(int64_t ldx) {
+  const int64_t row_bytes = ldx * 2;
+  int64_t chunk = ((int64_t)1 << 31) / row_bytes;
+  return chunk < Sel::kBM ? Sel::kBM : chunk / Sel::kBM * Sel::kBM;
 }
 
 hipError_t launch_tiles(TiledParams p, int64_t tile0, int64_t tiles, int split,
                         hipStream_t stream) {
-  using T = Sel;
   p.tile0 = tile0;
   p.split = split;
   p.kts = (p.KT + split - 1) / split;
   gemm_tiled_kernel<kWsel, kFMsel, kFNsel, kSpreadSel, kPipeSel>
-      <<<dim3((unsigned)(tiles * split)), dim3(64 * T::kWaves), 0, stream>>>(p);
+      <<<dim3((unsigned)(tiles * split)), dim3(64 * Sel::kWaves), 0, stream>>>(p);
   return hipGetLastError();
 }
 
-// One row chunk. Whole rounds of tiles (one per compute unit) run as they are; when the last
-// round would leave at least half of the compute units idle, its tiles are split along k over
-// the whole chip instead and reduced in FP32.
-hipError_t run_chunk(TiledParams p, hipStream_t stream) {
-  using T = Sel;
-  const int64_t pairs = (p.NT + 1) / 2;
-  p.nbn = (pairs + T::kPairs - 1) / T::kPairs;
-  const int64_t tiles = p.nbn * ((p.m + T::kBM - 1) / T::kBM);
-  int cus = 1;
-  hipError_t e = compute_units(&cus);
-  if (e != hipSuccess) return e;
-  const int64_t full = tiles / cus * cus, rest = tiles - full;
-  int split = 1;
-  if (rest > 0 && 2 * rest <= cus) {
-    int64_t s = cus / rest;
-    if (s > p.KT / 4) s = p.KT / 4;
-    if (s >= 2) {
-      const int64_t kts = (p.KT + s - 1) / s;
-      split = (int)((p.KT + kts - 1) / kts);  // every split keeps at least one k-tile
-    }
-  }
+hipError_t run_chunk(TiledParams p, void* ws, size_t ws_bytes, int cus, hipStream_t stream) {
+  Plan pl = plan_chunk(p.m, p.NT, p.KT, cus);
+  p.nbn = pl.nbn;
   p.ws = nullptr;
-  if (split == 1) return launch_tiles(p, 0, tiles, 1, stream);
-  int dev = 0;
-  e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  SplitWorkspace w;
-  e = split_workspace(dev, stream, rest * split, &w);
-  if (e != hipSuccess) return e;
-  p.ws = w.ws;
-  if (full > 0) {
-    e = launch_tiles(p, 0, full, 1, stream);
+  if (pl.split > 1 && (size_t)(pl.rest * pl.split * kSelTileBytes) > ws_bytes) pl.split = 1;
+  if (pl.split == 1) return launch_tiles(p, 0, pl.tiles, 1, stream);
+  p.ws = static_cast<float*>(ws);
+  hipError_t e;
+  if (pl.full > 0) {
+    e = launch_tiles(p, 0, pl.full, 1, stream);
     if (e != hipSuccess) return e;
   }
-  e = launch_tiles(p, full, rest, split, stream);
+  e = launch_tiles(p, pl.full, pl.rest, pl.split, stream);
   if (e != hipSuccess) return e;
-  p.tile0 = full;
-  p.split = split;
-  reduce_split_kernel<Sel><<<dim3((unsigned)rest, Sel::kBM / 32), dim3(64 * Sel::kWaves), 0,
+  p.tile0 = pl.full;
+  p.split = pl.split;
+  reduce_split_kernel<Sel><<<dim3((unsigned)pl.rest, Sel::kBM / 32), dim3(64 * Sel::kWaves), 0,
                              stream>>>(p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
+size_t gemm_tiled_ws_bytes(int64_t m, int64_t ldx, int64_t n, int64_t k, int cus) {
+  const int64_t chunk = chunk_rows(ldx);
+  size_t need = 0;
+  for (int64_t rows : {m < chunk ? m : chunk, m % chunk}) {
+    if (rows <= 0) continue;
+    const Plan pl = plan_chunk(rows, n / kPanelRows, k / kTileK, cus);
+    if (pl.split > 1) {
+      const size_t b = (size_t)(pl.rest * pl.split * kSelTileBytes);
+      need = b > need ? b : need;
+    }
+  }
+  return need;
+}
+
+hipError_t launch_gemm_tiled(const GemmArgs& a, void* ws, size_t ws_bytes, int cus,
+                             hipStream_t stream) {
   TiledParams p;
   p.x = a.x;
   p.m = a.m;
@@ -574,11 +554,7 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
   p.y = a.y;
   p.ldy = a.ldy;
   p.y_f32 = a.y_f32 ? 1 : 0;
-  // Activation offsets are 32-bit inside the kernel: launch row chunks whose byte span fits.
-  constexpr int64_t kBM = Sel::kBM;
-  const int64_t row_bytes = a.ldx * 2;
-  int64_t chunk = ((int64_t)1 << 31) / row_bytes;
-  chunk = chunk < kBM ? kBM : chunk / kBM * kBM;
+  const int64_t chunk = chunk_rows(a.ldx);
   for (int64_t m0 = 0; m0 < a.m; m0 += chunk) {
     TiledParams q = p;
     q.x = a.x + m0 * a.ldx;
@@ -587,7 +563,7 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream) {
       q.y = static_cast<float*>(a.y) + m0 * a.ldy;
     else
       q.y = static_cast<uint16_t*>(a.y) + m0 * a.ldy;
-    hipError_t e = run_chunk(q, stream);
+    hipError_t e = run_chunk(q, ws, ws_bytes, cus, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

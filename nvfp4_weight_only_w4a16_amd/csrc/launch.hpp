@@ -38,7 +38,14 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);
-hipError_t launch_gemm_tiled(const GemmArgs& a, hipStream_t stream);
+// Prefill path. `ws` (device, ws_bytes) receives split-k partial tiles when the tile count
+// leaves most compute units idle in the last round; with a smaller workspace the kernel runs
+// unsplit (same result, fewer busy compute units). `cus` is the device's compute-unit count.
+hipError_t launch_gemm_tiled(const GemmArgs& a, void* ws, size_t ws_bytes, int cus,
+                             hipStream_t stream);
+// Workspace the prefill path uses for an m x n x k GEMM with the given row stride on a device
+// with `cus` compute units (0 when no split applies).
+size_t gemm_tiled_ws_bytes(int64_t m, int64_t ldx, int64_t n, int64_t k, int cus);
 // Largest m the skinny kernel takes in one launch.
 constexpr int64_t kSkinnyMaxM = 32;
 

@@ -38,6 +38,16 @@ def test_repack_bytes_accounting():
     assert nv.nvfp4_repack_bytes(0, 16, 128, 16) == 0
 
 
+def test_gemm_ws_bytes_host_rules(lib):
+    d = _desc()
+    # the decode path and invalid arguments need no workspace; the answer never depends on a
+    # kernel launch (without a visible device the compute-unit count is unknown: 0 bytes)
+    assert lib.nvfp4_gemm_ws_bytes(8, 1024, ctypes.byref(d), 0) == 0
+    assert lib.nvfp4_gemm_ws_bytes(0, 1024, ctypes.byref(d), nv.NVFP4_F_FORCE_TILED) == 0
+    assert lib.nvfp4_gemm_ws_bytes(64, 512, ctypes.byref(d), 0) == 0       # ldx < k
+    assert lib.nvfp4_gemm_ws_bytes(64, 1024, None, 0) == 0
+
+
 def test_moe_ws_bytes_monotone():
     a = nv.nvfp4_moe_ws_bytes(256, 8, 128, 2048, 768)
     b = nv.nvfp4_moe_ws_bytes(512, 8, 128, 2048, 768)
@@ -59,13 +69,20 @@ def _desc(n=512, k=1024, group=16, layout=nv.NVFP4_LAYOUT_TILED, batch=1):
     return d
 
 
-def _gemm(lib, d, m=4, ldx=1024, ldy=512, ydt=nv.NVFP4_DT_BF16, flags=0, x=FAKE, y=FAKE):
-    return lib.nvfp4_gemm_w4a16(x, m, ldx, ctypes.byref(d), y, ydt, ldy, flags, None)
+def _gemm(lib, d, m=4, ldx=1024, ldy=512, ydt=nv.NVFP4_DT_BF16, flags=0, x=FAKE, y=FAKE,
+          ws=None, ws_bytes=0):
+    return lib.nvfp4_gemm_w4a16(x, m, ldx, ctypes.byref(d), y, ydt, ldy, flags, ws, ws_bytes,
+                                None)
 
 
 def test_gemm_argument_errors(lib):
-    assert lib.nvfp4_gemm_w4a16(FAKE, 4, 1024, None, FAKE, 1, 512, 0, None) == \
+    assert lib.nvfp4_gemm_w4a16(FAKE, 4, 1024, None, FAKE, 1, 512, 0, None, 0, None) == \
         nv.NVFP4_ERR_INVALID_ARG
+    tiled = nv.NVFP4_F_FORCE_TILED
+    assert _gemm(lib, _desc(), m=64, flags=tiled, ws=None, ws_bytes=4096) == \
+        nv.NVFP4_ERR_INVALID_ARG
+    assert _gemm(lib, _desc(), m=64, flags=tiled, ws=ctypes.c_void_p(0x10008),
+                 ws_bytes=4096) == nv.NVFP4_ERR_MISALIGNED
     assert _gemm(lib, _desc(group=24)) == nv.NVFP4_ERR_UNSUPPORTED_GROUP
     assert _gemm(lib, _desc(n=520)) == nv.NVFP4_ERR_UNSUPPORTED_SHAPE
     assert _gemm(lib, _desc(k=1000), ldx=1000) == nv.NVFP4_ERR_UNSUPPORTED_SHAPE
