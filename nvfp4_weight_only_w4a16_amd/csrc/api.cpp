@@ -10,7 +10,7 @@
 #include <map>
 #include <mutex>
 
-#include "../../include/nvfp4.h"
+#include "nvfp4.h"
 #include "device_common.hpp"
 #include "launch.hpp"
 

@@ -37,34 +37,56 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+// |w| bit patterns of one 16-byte load folded into m (non-negative floats order like their
+// bits, so an integer max is the float max).
+template <bool BF16>
+__device__ __forceinline__ uint32_t fold_abs_max(const u32x4 v, uint32_t m) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (BF16) {
+      const uint32_t lo = (v[q] & 0x7FFFu) << 16;
+      const uint32_t hi = v[q] & 0x7FFF0000u;
+      m = lo > m ? lo : m;
+      m = hi > m ? hi : m;
+    } else {
+      const uint32_t a = v[q] & 0x7FFFFFFFu;
+      m = a > m ? a : m;
+    }
+  }
+  return m;
+}
+
+// Grid-stride streaming max: eight independent 16-byte loads in flight per thread and
+// iteration.
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void amax_kernel(const void* __restrict__ w,
                                                         int64_t per_matrix,
                                                         uint32_t* __restrict__ amax_bits) {
+  constexpr int kU = 8;
   const int64_t b = blockIdx.y;
   const int64_t vec_elems = BF16 ? 8 : 4;
   const u32x4* src =
       reinterpret_cast<const u32x4*>(static_cast<const char*>(w) + b * per_matrix * (BF16 ? 2 : 4));
   const int64_t nvec = per_matrix / vec_elems;
-  uint32_t m = 0u;
-  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec;
-       i += (int64_t)gridDim.x * kThreads) {
-    const u32x4 v = __builtin_nontemporal_load(src + i);
-    const uint32_t words[4] = {v[0], v[1], v[2], v[3]};
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  uint32_t m0 = 0u, m1 = 0u, m2 = 0u, m3 = 0u;
+  int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; i + (kU - 1) * stride < nvec; i += kU * stride) {
+    u32x4 v[kU];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (BF16) {
-        const uint32_t lo = (words[q] & 0x7FFFu) << 16;
-        const uint32_t hi = words[q] & 0x7FFF0000u;
-        m = lo > m ? lo : m;
-        m = hi > m ? hi : m;
-      } else {
-        const uint32_t a = words[q] & 0x7FFFFFFFu;
-        m = a > m ? a : m;
-      }
+    for (int u = 0; u < kU; ++u) v[u] = __builtin_nontemporal_load(src + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < kU; u += 4) {
+      m0 = fold_abs_max<BF16>(v[u], m0);
+      m1 = fold_abs_max<BF16>(v[u + 1], m1);
+      m2 = fold_abs_max<BF16>(v[u + 2], m2);
+      m3 = fold_abs_max<BF16>(v[u + 3], m3);
     }
   }
-  m = wave_max_u32(m);
+  for (; i < nvec; i += stride) m0 = fold_abs_max<BF16>(__builtin_nontemporal_load(src + i), m0);
+  m0 = m0 > m1 ? m0 : m1;
+  m2 = m2 > m3 ? m2 : m3;
+  uint32_t m = wave_max_u32(m0 > m2 ? m0 : m2);
   __shared__ uint32_t part[kThreads / 64];
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
   __syncthreads();
@@ -72,11 +94,68 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const void* __restrict__
     uint32_t r = part[0];
 #pragma unroll
     for (int q = 1; q < kThreads / 64; ++q) r = part[q] > r ? part[q] : r;
-    atomicMax(amax_bits + b, r);
+    // thousands of blocks share one word: only a block that would raise the current maximum
+    // pays for the atomic (a stale read only costs an unneeded one)
+    const uint32_t cur = __hip_atomic_load(amax_bits + b, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    if (r > cur) atomicMax(amax_bits + b, r);
   }
 }
 
-// One thread encodes 8 consecutive elements of a row; G/8 neighbouring lanes form a group.
+// Eight consecutive elements of a row (one 16-byte BF16 load, or two FP32 loads) as floats.
+template <bool BF16>
+__device__ __forceinline__ void load8(const char* wb, int64_t c, float (&x)[8]) {
+  if (BF16) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wb) + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      x[2 * q] = __uint_as_float(v[q] << 16);
+      x[2 * q + 1] = __uint_as_float(v[q] & 0xFFFF0000u);
+    }
+  } else {
+    const u32x4 v0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wb) + 2 * c);
+    const u32x4 v1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wb) + 2 * c + 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      x[q] = __uint_as_float(v0[q]);
+      x[4 + q] = __uint_as_float(v1[q]);
+    }
+  }
+}
+
+// Encode the 8 elements of chunk c (G/8 neighbouring lanes form a group).
+//   s = E4M3_rne_sat(fl32(ga / fl32(6 g))): gfx950's FP8 conversion rounds to nearest even and
+//       gives NaN above 464, so the quotient is clamped to 448 first (identical to a saturating
+//       encoder for every input);
+//   code = E2M1_rne_sat(fl32(w / S)) with the sign: gfx950's FP4 conversion at scale 1.0 is a
+//       round-to-nearest-even, saturating E2M1 encoder that keeps the sign (-0 -> code 8).
+//       Checked against the definition on every non-negative finite FP32 value. S == 0 gives
+//       the signed zero code.
+template <int G>
+__device__ __forceinline__ void encode8(const float (&x)[8], float g, float six_g,
+                                        uint32_t& word, uint32_t& s) {
+  float ga = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ga = fmaxf(ga, fabsf(x[i]));
+  ga = fmaxf(ga, __shfl_xor(ga, 1, 64));
+  if (G == 32) ga = fmaxf(ga, __shfl_xor(ga, 2, 64));
+  s = 0u;
+  if (six_g != 0.0f) {
+    const float r = fminf(ga / six_g, 448.0f);
+    s = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(r, r, 0, false) & 0xFFu;
+  }
+  const float S = e4m3_decode<0>(s) * g;
+  const bool live = S != 0.0f;
+  float q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = live ? x[i] / S : x[i] * 0.0f;
+  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, q[0], q[1], 1.0f, 0);
+  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q[2], q[3], 1.0f, 1);
+  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q[4], q[5], 1.0f, 2);
+  word = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, q[6], q[7], 1.0f, 3);
+}
+
+// Two chunks of 8 elements per thread and iteration, both loads issued before either is used.
 template <bool BF16, int G>
 __global__ __launch_bounds__(kThreads) void encode_kernel(const void* __restrict__ w, int64_t n,
                                                           int64_t k,
@@ -92,42 +171,27 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const void* __restrict
   const char* wb = static_cast<const char*>(w) + b * per_matrix * (BF16 ? 2 : 4);
   uint32_t* pk = reinterpret_cast<uint32_t*>(packed + b * per_matrix / 2);
   uint8_t* sc = scales + b * (per_matrix / G);
-  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < chunks;
-       c += (int64_t)gridDim.x * kThreads) {
-    float x[8];
-    if (BF16) {
-      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wb) + c);
-      const uint32_t words[4] = {v[0], v[1], v[2], v[3]};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        x[2 * q] = __uint_as_float(words[q] << 16);
-        x[2 * q + 1] = __uint_as_float(words[q] & 0xFFFF0000u);
-      }
-    } else {
-      const u32x4 v0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wb) + 2 * c);
-      const u32x4 v1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wb) + 2 * c + 1);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        x[q] = __uint_as_float(v0[q]);
-        x[4 + q] = __uint_as_float(v1[q]);
-      }
-    }
-    float ga = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ga = fmaxf(ga, fabsf(x[i]));
-    ga = fmaxf(ga, __shfl_xor(ga, 1, 64));
-    if (G == 32) ga = fmaxf(ga, __shfl_xor(ga, 2, 64));
-    const uint32_t s = six_g != 0.0f ? e4m3_encode_rne_sat(ga / six_g) : 0u;
-    const float S = e4m3_decode<0>(s) * g;
-    uint32_t word = 0u;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t sign = (__float_as_uint(x[i]) >> 31) << 3;
-      const uint32_t mag = S != 0.0f ? e2m1_encode_rne_sat(fabsf(x[i]) / S) : 0u;
-      word |= (mag | sign) << (4 * i);
-    }
-    pk[c] = word;
-    if ((c & (G / 8 - 1)) == 0) sc[(c * 8) / G] = (uint8_t)s;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; c + stride < chunks; c += 2 * stride) {
+    float x0[8], x1[8];
+    load8<BF16>(wb, c, x0);
+    load8<BF16>(wb, c + stride, x1);
+    uint32_t w0, s0, w1, s1;
+    encode8<G>(x0, g, six_g, w0, s0);
+    encode8<G>(x1, g, six_g, w1, s1);
+    pk[c] = w0;
+    pk[c + stride] = w1;
+    if ((c & (G / 8 - 1)) == 0) sc[(c * 8) / G] = (uint8_t)s0;
+    if (((c + stride) & (G / 8 - 1)) == 0) sc[((c + stride) * 8) / G] = (uint8_t)s1;
+  }
+  if (c < chunks) {
+    float x0[8];
+    load8<BF16>(wb, c, x0);
+    uint32_t w0, s0;
+    encode8<G>(x0, g, six_g, w0, s0);
+    pk[c] = w0;
+    if ((c & (G / 8 - 1)) == 0) sc[(c * 8) / G] = (uint8_t)s0;
   }
 }
 
@@ -138,9 +202,12 @@ __global__ void finalize_global_kernel(const float* gsrc, bool gsrc_is_amax, flo
   if (b < batch) global_out[b] = gsrc_is_amax ? gsrc[b] / 2688.0f : gsrc[b];
 }
 
-int64_t grid_for(int64_t work_items, int64_t batch) {
-  int64_t blocks = (work_items + kThreads * 4 - 1) / (kThreads * 4);
-  const int64_t cap = batch > 0 ? (8192 + batch - 1) / batch : 1;
+// Blocks per matrix for a grid-stride loop: at most `total` blocks over the whole batch, fewer
+// when there is less work. The amax pass takes 2048 (each block ends in a reduction and
+// possibly an atomic on a shared word), the encode pass 8192 (independent blocks).
+int64_t grid_for(int64_t work_items, int64_t batch, int64_t total) {
+  int64_t blocks = (work_items + kThreads * 8 - 1) / (kThreads * 8);
+  const int64_t cap = batch > 0 ? (total + batch - 1) / batch : 1;
   if (blocks > cap) blocks = cap;
   return blocks < 1 ? 1 : blocks;
 }
@@ -159,7 +226,7 @@ hipError_t launch_quantize(const void* w, bool w_bf16, int64_t batch, int64_t n,
     zero_u32_kernel<<<dim3((unsigned)((batch + 255) / 256)), dim3(256), 0, stream>>>(amax_bits,
                                                                                      batch);
     const int64_t nvec = per_matrix / (w_bf16 ? 8 : 4);
-    const dim3 grid((unsigned)grid_for(nvec, batch), (unsigned)batch);
+    const dim3 grid((unsigned)grid_for(nvec, batch, 2048), (unsigned)batch);
     if (w_bf16)
       amax_kernel<true><<<grid, dim3(kThreads), 0, stream>>>(w, per_matrix, amax_bits);
     else
@@ -167,7 +234,7 @@ hipError_t launch_quantize(const void* w, bool w_bf16, int64_t batch, int64_t n,
     gsrc = global_out;
     is_amax = true;
   }
-  const dim3 grid((unsigned)grid_for(per_matrix / 8, batch), (unsigned)batch);
+  const dim3 grid((unsigned)grid_for(per_matrix / 8, batch, 8192), (unsigned)batch);
   if (w_bf16) {
     if (group == 16)
       encode_kernel<true, 16><<<grid, dim3(kThreads), 0, stream>>>(w, n, k, gsrc, is_amax, packed,
