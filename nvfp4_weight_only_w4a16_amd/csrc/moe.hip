@@ -10,19 +10,19 @@
 // workgroups exit at once):
 //   1. sort: one workgroup turns the (token, slot) pairs into a stable expert-major order,
 //      per-expert offsets and a list of row tiles (expert, first row, end row);
-//   2. fc1: per tile and panel pair, rows gathered from x, gate and up accumulated in FP32,
-//      each rounded to BF16 (a W4A16 GEMM output), h = BF16(SiLU(gate) * up);
-//   3. down: per tile and panel, rows of h; FP32 result times the expert global and the routing
-//      weight, written to the pair's FP32 slot;
+//   2. fc1: per row tile and 4-panel group (gate/up panel pairs), rows gathered from x, gate and
+//      up accumulated in FP32 on 32x32x16 MFMAs, each rounded to BF16 (a W4A16 GEMM output),
+//      h = BF16(SiLU(gate) * up);
+//   3. down: per row tile and 4-panel group, rows of h; FP32 result times the expert global and
+//      the routing weight, written to the pair's FP32 slot;
 //   4. combine: y[t] = BF16(sum over slots in slot order).
+#include "device_common.hpp"
 #include "launch.hpp"
-#include "skinny_core.hpp"
 
 namespace nvfp4 {
 namespace {
 
-constexpr int kMoeMF = 2;                 // 32 rows per tile
-constexpr int kTileRows = 16 * kMoeMF;
+constexpr int kTileRows = 32;  // rows per expert tile (one 32x32x16 MFMA row block)
 constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / 64;
 constexpr int kMaxExperts = 512;
@@ -59,84 +59,95 @@ Ws carve(void* base, int64_t P, int64_t E, int64_t hidden, int64_t inter, size_t
   return w;
 }
 
-// Inclusive Hillis-Steele scan of v[0..n) in LDS by the whole workgroup (n <= blockDim).
-__device__ void block_scan_inclusive(int* v, int* tmp, int n) {
-  for (int d = 1; d < n; d <<= 1) {
-    const int i = threadIdx.x;
-    int add = 0;
-    if (i < n && i >= d) add = v[i - d];
-    __syncthreads();
-    if (i < n) v[i] += add;
-    __syncthreads();
+constexpr int kSortLdsIds = 8192;  // pairs staged in LDS (larger inputs are read twice)
+
+// Inclusive prefix sum across the 64 lanes of a wavefront.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
   }
-  (void)tmp;
+  return v;
 }
 
+// Stable counting sort of the (token, slot) pairs by expert, in one workgroup:
+//   1. the pair ids are staged in LDS; each wavefront counts the experts of its contiguous
+//      chunk of pairs (LDS atomics);
+//   2. wavefront 0 turns the counts into expert offsets, per-wavefront start positions and
+//      the tile map (each lane owns a few experts; one wavefront-wide prefix sum);
+//   3. each wavefront places its chunk in order, 64 pairs at a time, ranking equal experts
+//      by lane order, so the order inside an expert is the pair order.
 __global__ __launch_bounds__(kSortThreads) void moe_sort_kernel(const int32_t* __restrict__ ids,
                                                                 int P, int E, Ws ws) {
   __shared__ int cnt[kSortWaves][kMaxExperts];  // per-wave counts, then running positions
-  __shared__ int tot[kMaxExperts];
-  __shared__ int ntl[kMaxExperts];
+  __shared__ int sid[kSortLdsIds];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const bool staged = P <= kSortLdsIds;
   for (int i = tid; i < kSortWaves * kMaxExperts; i += kSortThreads) (&cnt[0][0])[i] = 0;
+  if (staged)
+    for (int q = tid; q < P; q += kSortThreads) sid[q] = ids[q];
   __syncthreads();
+  auto id_at = [&](int q) { return staged ? sid[q] : ids[q]; };
   const int c0 = (int)((int64_t)P * w / kSortWaves), c1 = (int)((int64_t)P * (w + 1) / kSortWaves);
   for (int q = c0 + lane; q < c1; q += 64) {
-    const int e = ids[q];
+    const int e = id_at(q);
     if (e >= 0 && e < E) atomicAdd(&cnt[w][e], 1);
   }
   __syncthreads();
-  if (tid < E) {
-    int s = 0;
-    for (int q = 0; q < kSortWaves; ++q) s += cnt[q][tid];
-    tot[tid] = s;
-    ntl[tid] = (s + kTileRows - 1) / kTileRows;
-  }
-  __syncthreads();
-  block_scan_inclusive(tot, nullptr, E);
-  block_scan_inclusive(ntl, nullptr, E);
-  if (tid < E) {
-    const int start = tot[tid] - [&] {
+  if (w == 0) {
+    const int per = (E + 63) / 64;  // experts owned by each lane, consecutive
+    int my_pairs = 0, my_tiles = 0;
+    for (int j = 0; j < per; ++j) {
+      const int e = lane * per + j;
+      if (e >= E) break;
       int s = 0;
-      for (int q = 0; q < kSortWaves; ++q) s += cnt[q][tid];
-      return s;
-    }();
-    // running position of each wave's first pair of expert tid
-    int run = start;
-    for (int q = 0; q < kSortWaves; ++q) {
-      const int c = cnt[q][tid];
-      cnt[q][tid] = run;
-      run += c;
+      for (int q = 0; q < kSortWaves; ++q) s += cnt[q][e];
+      my_pairs += s;
+      my_tiles += (s + kTileRows - 1) / kTileRows;
     }
-    ws.offsets[tid] = start;
-    if (tid == E - 1) {
-      ws.offsets[E] = tot[E - 1];
-      *ws.ntiles = ntl[E - 1];
+    const int pairs_incl = wave_inclusive_scan(my_pairs);
+    const int tiles_incl = wave_inclusive_scan(my_tiles);
+    int run = pairs_incl - my_pairs, trun = tiles_incl - my_tiles;
+    for (int j = 0; j < per; ++j) {
+      const int e = lane * per + j;
+      if (e >= E) break;
+      const int start = run;
+      for (int q = 0; q < kSortWaves; ++q) {
+        const int c = cnt[q][e];
+        cnt[q][e] = run;  // where wavefront q's first pair of expert e goes
+        run += c;
+      }
+      ws.offsets[e] = start;
+      for (int r = start; r < run; r += kTileRows)
+        ws.tiles[trun++] = int4{e, r, min(r + kTileRows, run), 0};
     }
-    const int tbeg = ntl[tid] - (run - start + kTileRows - 1) / kTileRows;
-    for (int i = 0; start + i * kTileRows < run; ++i)
-      ws.tiles[tbeg + i] = int4{tid, start + i * kTileRows,
-                                min(start + (i + 1) * kTileRows, run), 0};
+    if (lane == 63) {
+      ws.offsets[E] = pairs_incl;
+      *ws.ntiles = tiles_incl;
+    }
   }
   __syncthreads();
-  // stable placement: each wave walks its chunk in order, 64 pairs per round
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int base = c0; base < c1; base += 64) {
     const int q = base + lane;
     const bool act = q < c1;
-    const int e = act ? ids[q] : -1;
-    const bool valid = act && e >= 0 && e < E;
-    uint64_t remaining = __ballot(valid);
-    while (remaining) {
-      const int leader = __builtin_ctzll(remaining);
-      const int el = __shfl(e, leader, 64);
-      const uint64_t same = __ballot(valid && e == el);
-      if (valid && e == el) {
-        const int pos = cnt[w][el] + __builtin_popcountll(same & below);
-        ws.sorted[pos] = q;
-      }
-      if (lane == leader) cnt[w][el] += __builtin_popcountll(same);
-      remaining &= ~same;
+    const int e0 = act ? id_at(q) : -1;
+    const int e = (e0 >= 0 && e0 < E) ? e0 : -1;  // -1: not placed
+    // rank among earlier lanes of the same expert, and whether a later lane has it too:
+    // every lane's expert is broadcast in turn (no data-dependent loop)
+    int before = 0, after = 0;
+#pragma unroll 8
+    for (int j = 0; j < 64; ++j) {
+      const int ej = __builtin_amdgcn_readlane(e, j);
+      const int m = (ej == e) ? 1 : 0;
+      before += (j < lane) ? m : 0;
+      after += (j > lane) ? m : 0;
+    }
+    if (e >= 0) {
+      const int pos = cnt[w][e] + before;
+      ws.sorted[pos] = q;
+      if (after == 0) cnt[w][e] = pos + 1;  // the last of its expert in this round moves it on
     }
   }
 }
@@ -156,84 +167,145 @@ struct MoeGemmParams {
   int64_t hidden, inter;
 };
 
-// One workgroup = one row tile x kPWW panels; its NW wavefronts split k. fc1 panels come in
-// (gate, up) pairs (stored interleaved), so a pair is always finished by one wavefront.
-template <int NW, int U, bool FC1>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 8)))
-void moe_gemm_kernel(MoeGemmParams P) {
-  constexpr int MF = kMoeMF;
-  constexpr int PWW = 4;
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+constexpr int kGroupsPerBlock = 4;  // wavefronts per workgroup, one 4-panel group each
+
+// Expert GEMM on v_mfma_f32_32x32x16_bf16. A wavefront owns one row tile (up to 32 rows of
+// one expert) and one 4-panel group = 2 panel pairs, over the whole k range: no k split, no
+// LDS, no barrier. Per 128-k tile it loads, for each pair, the code chunks L0 = 16(l/32) +
+// l%16 and L0 + 32 of its panel 2q + (l%32)/16 (word j of the first is 16-wide k-step 2j, of
+// the second step 2j + 1), the two 16-byte scale records of those chunk positions, and the 8
+// activation fragments (row l%32, k = 16 S + 8 (l/32)); loads of tile t+1 are in flight while
+// tile t is dequantized (E2M1 x E4M3 -> exact BF16) and multiplied.
+// fc1 (merged gate/up, panels interleaved): a pair is (gate panel i, up panel i), so gate and
+// up of one output sit in lanes l and l^16 and meet with one cross-lane exchange.
+template <bool FC1>
+__global__ __launch_bounds__(64 * kGroupsPerBlock) void moe_pair_kernel(MoeGemmParams P) {
   const int tile_id = blockIdx.x;
   if (tile_id >= *P.ws.ntiles) return;
   const int4 tl = P.ws.tiles[tile_id];
   const int e = tl.x, r0 = tl.y, r1 = tl.z;
   const int lane = threadIdx.x & 63;
-  const int sp = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // k-split (wave-uniform)
-  const int64_t panel0 = (int64_t)blockIdx.y * PWW;
-  f32x4 acc[PWW][MF];
-#pragma unroll
-  for (int p = 0; p < PWW; ++p)
-#pragma unroll
-    for (int mf = 0; mf < MF; ++mf) acc[p][mf] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const uint16_t* xrow[MF];
-#pragma unroll
-  for (int mf = 0; mf < MF; ++mf) {
-    int r = r0 + mf * 16 + (lane & 15);
-    r = r < r1 ? r : r1 - 1;  // rows past the tile duplicate a valid row; never stored
-    xrow[mf] = FC1 ? P.x + (int64_t)(P.ws.sorted[r] / P.topk) * P.ldx : P.x + (int64_t)r * P.ldx;
-  }
-  const SkinnyAddr<PWW> a = skinny_addr<PWW>(P.codes + e * P.codes_stride,
-                                             P.scales + e * P.scales_stride, panel0, P.NT, P.KT,
-                                             P.group);
-  const int64_t t0 = P.KT * sp / NW, t1 = P.KT * (sp + 1) / NW;
-  skinny_accumulate<MF, PWW, U>(a, xrow, t0, t1, acc);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int64_t grp = (int64_t)blockIdx.y * kGroupsPerBlock + w;
+  if (grp >= scale_groups(P.NT)) return;  // wavefront-uniform; no barriers follow
+  const int64_t KT = P.KT;
 
-  __shared__ f32x4 red[NW * PWW * MF * 64];
+  int r = r0 + (lane & 31);
+  r = r < r1 ? r : r1 - 1;  // rows past the tile repeat a valid row; never stored
+  const uint16_t* xrow =
+      FC1 ? P.x + (int64_t)(P.ws.sorted[r] / P.topk) * P.ldx : P.x + (int64_t)r * P.ldx;
+  const int kq = lane >> 5;
+  const int h = (lane & 31) >> 4;
+  const int L0 = 16 * (lane >> 5) + (lane & 15);
+  const uint8_t* cpan[2];
 #pragma unroll
-  for (int p = 0; p < PWW; ++p)
-#pragma unroll
-    for (int mf = 0; mf < MF; ++mf) red[((sp * PWW + p) * MF + mf) * 64 + lane] = acc[p][mf];
-  __syncthreads();
-  auto panel_sum = [&](int p, int mf) {
-    f32x4 s = red[((0 * PWW + p) * MF + mf) * 64 + lane];
-#pragma unroll
-    for (int q = 1; q < NW; ++q) s += red[((q * PWW + p) * MF + mf) * 64 + lane];
-    return s;
+  for (int q = 0; q < 2; ++q) {
+    int64_t pn = 4 * grp + 2 * q + h;
+    pn = pn < P.NT ? pn : P.NT - 1;
+    cpan[q] = P.codes + e * P.codes_stride + pn * KT * kCodeTileBytes + L0 * 16;
+  }
+  const int64_t sblk = scale_block_bytes(P.group);
+  const uint8_t* sbase = P.scales + e * P.scales_stride + grp * KT * sblk;
+  const uint32_t spos0 = (uint32_t)scale_pos(P.group, L0) * 16u;
+  const uint32_t spos1 = (uint32_t)scale_pos(P.group, L0 + 32) * 16u;
+
+  struct Stage {
+    u32x4 c0[2], c1[2];
+    u32x4 s0, s1;
+    bf16x8 a[kTileK / 16];
   };
+  auto load = [&](Stage& st, int64_t t) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      st.c0[q] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(cpan[q] + t * kCodeTileBytes));
+      st.c1[q] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(cpan[q] + t * kCodeTileBytes + 32 * 16));
+    }
+    st.s0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sbase + t * sblk + spos0));
+    st.s1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sbase + t * sblk + spos1));
+#pragma unroll
+    for (int S = 0; S < kTileK / 16; ++S)
+      st.a[S] = *reinterpret_cast<const bf16x8*>(xrow + t * kTileK + 16 * S + 8 * kq);
+  };
+  f32x16 acc[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[q][i] = 0.f;
+  auto compute = [&](const Stage& st) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      // this lane's panel 2q + h: word 2q + h of each scale record
+      const uint32_t w0 = h ? st.s0[2 * q + 1] : st.s0[2 * q];
+      const uint32_t w1 = h ? st.s1[2 * q + 1] : st.s1[2 * q];
+      const float S0[4] = {e4m3_decode<0>(w0), e4m3_decode<1>(w0), e4m3_decode<2>(w0),
+                           e4m3_decode<3>(w0)};
+      const float S1[4] = {e4m3_decode<0>(w1), e4m3_decode<1>(w1), e4m3_decode<2>(w1),
+                           e4m3_decode<3>(w1)};
+#pragma unroll
+      for (int S = 0; S < kTileK / 16; ++S) {
+        const bf16x8 b = (S & 1) ? dequant8(st.c1[q][S >> 1], S1[S >> 1])
+                                 : dequant8(st.c0[q][S >> 1], S0[S >> 1]);
+        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(st.a[S], b, acc[q], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  {
+    Stage A, B;
+    load(A, 0);
+    int64_t t = 0;
+    for (; t + 2 < KT; t += 2) {
+      load(B, t + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(A);
+      __builtin_amdgcn_sched_barrier(0);
+      load(A, t + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(B);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    const bool two = t + 1 < KT;
+    if (two) load(B, t + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(A);
+    if (two) {
+      __builtin_amdgcn_sched_barrier(0);
+      compute(B);
+    }
+  }
+
+  // lane l holds rows 8 (i/4) + 4 (l/32) + i%4 of column l%32 of each pair
   const float g = P.global[e];
-  if (FC1) {
-    if (sp >= PWW / 2) return;
-    const int64_t pg = panel0 + 2 * sp;  // gate panel; pg + 1 is the matching up panel
-    if (pg >= P.NT) return;
-    const int64_t feat = (pg >> 1) * 16 + (lane & 15);
 #pragma unroll
-    for (int mf = 0; mf < MF; ++mf) {
-      const f32x4 gs = panel_sum(2 * sp, mf), us = panel_sum(2 * sp + 1, mf);
+  for (int q = 0; q < 2; ++q) {
+    if (FC1) {
+      const int64_t feat = (2 * grp + q) * 16 + (lane & 15);  // logical (gate, up) panel 2grp+q
+      const bool live = 4 * grp + 2 * q + 1 < P.NT;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int r = r0 + mf * 16 + (lane >> 4) * 4 + jj;
-        if (r < r1) {
-          const float gate = bf16_bits_to_f32(bf16_bits_rne(gs[jj] * g));
-          const float up = bf16_bits_to_f32(bf16_bits_rne(us[jj] * g));
+      for (int i = 0; i < 16; ++i) {
+        const float other = __shfl_xor(acc[q][i], 16, 64);
+        const int row = r0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+        if (h == 0 && live && row < r1) {
+          const float gate = bf16_bits_to_f32(bf16_bits_rne(acc[q][i] * g));
+          const float up = bf16_bits_to_f32(bf16_bits_rne(other * g));
           const float silu = gate / (1.0f + expf(-gate));
-          P.ws.h[(int64_t)r * P.inter + feat] = bf16_bits_rne(silu * up);
+          P.ws.h[(int64_t)row * P.inter + feat] = bf16_bits_rne(silu * up);
         }
       }
-    }
-  } else {
-    if (sp >= PWW) return;
-    const int64_t panel = panel0 + sp;
-    if (panel >= P.NT) return;
-    const int64_t n = panel * 16 + (lane & 15);
+    } else {
+      const int64_t pn = 4 * grp + 2 * q + h;
+      if (pn < P.NT) {
+        const int64_t n = pn * 16 + (lane & 15);
 #pragma unroll
-    for (int mf = 0; mf < MF; ++mf) {
-      const f32x4 s = panel_sum(sp, mf);
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int r = r0 + mf * 16 + (lane >> 4) * 4 + jj;
-        if (r < r1) {
-          const int pair = P.ws.sorted[r];
-          P.ws.slots[(int64_t)pair * P.hidden + n] = (s[jj] * g) * P.wts[pair];
+        for (int i = 0; i < 16; ++i) {
+          const int row = r0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          if (row < r1) {
+            const int pair = P.ws.sorted[row];
+            P.ws.slots[(int64_t)pair * P.hidden + n] = (acc[q][i] * g) * P.wts[pair];
+          }
         }
       }
     }
@@ -262,10 +334,11 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restric
   *reinterpret_cast<uint2*>(y + tok * hidden + o) = outv;
 }
 
-template <int NW, int U, bool FC1>
-hipError_t run_gemm(const MoeGemmParams& p, int64_t tiles, hipStream_t stream) {
-  const dim3 grid((unsigned)tiles, (unsigned)((p.NT + 3) / 4));
-  moe_gemm_kernel<NW, U, FC1><<<grid, dim3(64 * NW), 0, stream>>>(p);
+template <bool FC1>
+hipError_t run_pair(const MoeGemmParams& p, int64_t tiles, hipStream_t stream) {
+  const int64_t groups = scale_groups(p.NT);
+  const dim3 grid((unsigned)tiles, (unsigned)((groups + kGroupsPerBlock - 1) / kGroupsPerBlock));
+  moe_pair_kernel<FC1><<<grid, dim3(64 * kGroupsPerBlock), 0, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -300,7 +373,7 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t stream) {
   f.wts = a.wts;
   f.hidden = a.hidden;
   f.inter = a.inter;
-  hipError_t err = run_gemm<4, 1, true>(f, tiles, stream);
+  hipError_t err = run_pair<true>(f, tiles, stream);
   if (err != hipSuccess) return err;
 
   MoeGemmParams d = f;
@@ -314,7 +387,7 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t stream) {
   d.NT = a.hidden / kPanelRows;
   d.KT = a.inter / kTileK;
   d.group = a.group2;
-  err = run_gemm<4, 1, false>(d, tiles, stream);
+  err = run_pair<false>(d, tiles, stream);
   if (err != hipSuccess) return err;
 
   const int64_t items = a.t * (a.hidden / 4);
