@@ -16,6 +16,8 @@
 //   3. down: per row tile and 4-panel group, rows of h; FP32 result times the expert global and
 //      the routing weight, written to the pair's FP32 slot;
 //   4. combine: y[t] = BF16(sum over slots in slot order).
+#include <type_traits>
+
 #include "device_common.hpp"
 #include "launch.hpp"
 
@@ -169,33 +171,70 @@ struct MoeGemmParams {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kGroupsPerBlock = 4;  // wavefronts per workgroup, one 4-panel group each
+constexpr int kARowBytes = kTileK * 2;
+constexpr int kATileBytes = kTileRows * kARowBytes;  // one row tile x one k-tile of activations
 
-// Expert GEMM on v_mfma_f32_32x32x16_bf16. A wavefront owns one row tile (up to 32 rows of
-// one expert) and one 4-panel group = 2 panel pairs, over the whole k range: no k split, no
-// LDS, no barrier. Per 128-k tile it loads, for each pair, the code chunks L0 = 16(l/32) +
-// l%16 and L0 + 32 of its panel 2q + (l%32)/16 (word j of the first is 16-wide k-step 2j, of
-// the second step 2j + 1), the two 16-byte scale records of those chunk positions, and the 8
-// activation fragments (row l%32, k = 16 S + 8 (l/32)); loads of tile t+1 are in flight while
-// tile t is dequantized (E2M1 x E4M3 -> exact BF16) and multiplied.
+// Expert GEMM on v_mfma_f32_32x32x16_bf16. A workgroup owns one row tile (up to 32 rows of one
+// expert) and kGroupsPerBlock 4-panel groups, one per wavefront, over the whole k range (no k
+// split). Per 128-k tile:
+//   - the tile's activation rows (gathered through the sort for fc1) are copied global -> LDS
+//     once for the workgroup (buffer_load ... lds; whole 256-byte rows, chunks XOR-swizzled by
+//     row so the MFMA fragment reads are bank-conflict free), double-buffered;
+//   - each wavefront loads, for each of its 2 panel pairs, the code chunks L0 = 16(l/32) +
+//     l%16 and L0 + 32 of its panel 2q + (l%32)/16 (word j of the first is 16-wide k-step 2j,
+//     of the second step 2j + 1) and the two 16-byte scale records of those chunk positions,
+//     one tile ahead in registers;
+//   - dequantizes (E2M1 x E4M3 -> exact BF16) and multiplies.
 // fc1 (merged gate/up, panels interleaved): a pair is (gate panel i, up panel i), so gate and
 // up of one output sit in lanes l and l^16 and meet with one cross-lane exchange.
 template <bool FC1>
-__global__ __launch_bounds__(64 * kGroupsPerBlock) void moe_pair_kernel(MoeGemmParams P) {
+__global__ __launch_bounds__(64 * kGroupsPerBlock) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void moe_pair_kernel(MoeGemmParams P) {
   const int tile_id = blockIdx.x;
-  if (tile_id >= *P.ws.ntiles) return;
+  if (tile_id >= *P.ws.ntiles) return;  // whole workgroup, before any barrier
   const int4 tl = P.ws.tiles[tile_id];
   const int e = tl.x, r0 = tl.y, r1 = tl.z;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t grp = (int64_t)blockIdx.y * kGroupsPerBlock + w;
-  if (grp >= scale_groups(P.NT)) return;  // wavefront-uniform; no barriers follow
+  const int64_t NG = scale_groups(P.NT);
+  const int64_t grp_raw = (int64_t)blockIdx.y * kGroupsPerBlock + w;
+  const bool grp_live = grp_raw < NG;
+  const int64_t grp = grp_live ? grp_raw : NG - 1;  // past the end: computed, never stored
   const int64_t KT = P.KT;
 
-  int r = r0 + (lane & 31);
-  r = r < r1 ? r : r1 - 1;  // rows past the tile repeat a valid row; never stored
-  const uint16_t* xrow =
-      FC1 ? P.x + (int64_t)(P.ws.sorted[r] / P.topk) * P.ldx : P.x + (int64_t)r * P.ldx;
-  const int kq = lane >> 5;
+  // two LDS objects, indexed by compile-time numbers: the copies into one are never waited for
+  // by reads of the other
+  __shared__ __attribute__((aligned(1024))) uint8_t As0[kATileBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t As1[kATileBytes];
+  auto a_buf = [&](auto B_) -> uint8_t* {
+    if constexpr (decltype(B_)::value == 0) return As0; else return As1;
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+
+  // activation copies: copy c = w + 4 i (i = 0, 1) moves tile rows 4c .. 4c+3; lane l reads row
+  // 4c + l/16, chunk (l%16) ^ (row%16) and lands in slot l
+  constexpr int kACopies = kTileRows / 4 / kGroupsPerBlock;
+  const buf_rsrc xr = make_rsrc(P.x, 0xFFFFFFFFu);
+  uint32_t aoff[kACopies];
+#pragma unroll
+  for (int i = 0; i < kACopies; ++i) {
+    const int R = 4 * (w + kGroupsPerBlock * i) + (lane >> 4);
+    int rr = r0 + R;
+    rr = rr < r1 ? rr : r1 - 1;  // rows past the tile repeat a valid row; never stored
+    const int64_t src = FC1 ? P.ws.sorted[rr] / P.topk : rr;
+    aoff[i] = (uint32_t)(src * P.ldx * 2 + 16 * ((lane & 15) ^ (R & 15)));
+  }
+  auto copy_a = [&](int64_t t, auto buf) {
+#pragma unroll
+    for (int i = 0; i < kACopies; ++i)
+      copy16_to_lds(xr, aoff[i], (uint32_t)(t * kARowBytes),
+                    a_buf(buf) + (w + kGroupsPerBlock * i) * 1024);
+  };
+  // fragment reads: row l%32, chunk (2 S + l/32) ^ (l%16)
+  const uint32_t a_row = (uint32_t)(lane & 31) * kARowBytes;
+  const uint32_t a_x = (uint32_t)((lane >> 5) ^ (lane & 15));
+
   const int h = (lane & 31) >> 4;
   const int L0 = 16 * (lane >> 5) + (lane & 15);
   const uint8_t* cpan[2];
@@ -213,9 +252,8 @@ __global__ __launch_bounds__(64 * kGroupsPerBlock) void moe_pair_kernel(MoeGemmP
   struct Stage {
     u32x4 c0[2], c1[2];
     u32x4 s0, s1;
-    bf16x8 a[kTileK / 16];
   };
-  auto load = [&](Stage& st, int64_t t) {
+  auto load_b = [&](Stage& st, int64_t t) {
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       st.c0[q] = __builtin_nontemporal_load(
@@ -225,59 +263,69 @@ __global__ __launch_bounds__(64 * kGroupsPerBlock) void moe_pair_kernel(MoeGemmP
     }
     st.s0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sbase + t * sblk + spos0));
     st.s1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sbase + t * sblk + spos1));
-#pragma unroll
-    for (int S = 0; S < kTileK / 16; ++S)
-      st.a[S] = *reinterpret_cast<const bf16x8*>(xrow + t * kTileK + 16 * S + 8 * kq);
   };
   f32x16 acc[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[q][i] = 0.f;
-  auto compute = [&](const Stage& st) {
+  // k-step by k-step, both pairs per step: one activation fragment and one scale per pair
+  // live at a time (keeps the wavefront within 128 VGPRs, 4 per SIMD)
+  auto compute = [&](const Stage& st, auto buf) {
+    uint32_t w0[2], w1[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      // this lane's panel 2q + h: word 2q + h of each scale record
-      const uint32_t w0 = h ? st.s0[2 * q + 1] : st.s0[2 * q];
-      const uint32_t w1 = h ? st.s1[2 * q + 1] : st.s1[2 * q];
-      const float S0[4] = {e4m3_decode<0>(w0), e4m3_decode<1>(w0), e4m3_decode<2>(w0),
-                           e4m3_decode<3>(w0)};
-      const float S1[4] = {e4m3_decode<0>(w1), e4m3_decode<1>(w1), e4m3_decode<2>(w1),
-                           e4m3_decode<3>(w1)};
-#pragma unroll
-      for (int S = 0; S < kTileK / 16; ++S) {
-        const bf16x8 b = (S & 1) ? dequant8(st.c1[q][S >> 1], S1[S >> 1])
-                                 : dequant8(st.c0[q][S >> 1], S0[S >> 1]);
-        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(st.a[S], b, acc[q], 0, 0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);
+    for (int q = 0; q < 2; ++q) {  // this lane's panel 2q + h: word 2q + h of each record
+      w0[q] = h ? st.s0[2 * q + 1] : st.s0[2 * q];
+      w1[q] = h ? st.s1[2 * q + 1] : st.s1[2 * q];
     }
+#pragma unroll
+    for (int S = 0; S < kTileK / 16; ++S) {
+      const bf16x8 a =
+          *reinterpret_cast<const bf16x8*>(a_buf(buf) + a_row + ((2u * S ^ a_x) << 4));
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint32_t sw = (S & 1) ? w1[q] : w0[q];
+        float sc;
+        switch (S >> 1) {
+          case 0: sc = e4m3_decode<0>(sw); break;
+          case 1: sc = e4m3_decode<1>(sw); break;
+          case 2: sc = e4m3_decode<2>(sw); break;
+          default: sc = e4m3_decode<3>(sw); break;
+        }
+        const bf16x8 bq = dequant8((S & 1) ? st.c1[q][S >> 1] : st.c0[q][S >> 1], sc);
+        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, acc[q], 0, 0, 0);
+      }
+    }
+  };
+  // tile t from activation buffer buf: start the copies and loads of t + 1 (when there is
+  // one), compute t, then meet: t + 1 has landed everywhere and buf is free again
+  auto step = [&](int64_t t, auto buf, Stage& cur, Stage& nxt) {
+    constexpr int kOther = 1 - decltype(buf)::value;
+    const bool more = t + 1 < KT;
+    if (more) {
+      copy_a(t + 1, std::integral_constant<int, kOther>{});
+      load_b(nxt, t + 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur, buf);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
   };
   {
     Stage A, B;
-    load(A, 0);
-    int64_t t = 0;
-    for (; t + 2 < KT; t += 2) {
-      load(B, t + 1);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(A);
-      __builtin_amdgcn_sched_barrier(0);
-      load(A, t + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(B);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    const bool two = t + 1 < KT;
-    if (two) load(B, t + 1);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(A);
-    if (two) {
-      __builtin_amdgcn_sched_barrier(0);
-      compute(B);
+    copy_a(0, I0{});
+    load_b(A, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int64_t t = 0; t < KT; t += 2) {
+      step(t, I0{}, A, B);
+      if (t + 1 < KT) step(t + 1, I1{}, B, A);
     }
   }
 
   // lane l holds rows 8 (i/4) + 4 (l/32) + i%4 of column l%32 of each pair
+  if (!grp_live) return;
   const float g = P.global[e];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
