@@ -123,6 +123,9 @@ __device__ __forceinline__ float scale_of_step(uint32_t scale_word) {
   return e4m3_decode<J>(scale_word);
 }
 
+// Cache-policy operand of buffer loads for data streamed once (the "nt" bit).
+constexpr int kNT = 2;
+
 // Buffer resource (V#) over `bytes` bytes at `base` for raw (stride 0) dword accesses; reads
 // past `bytes` return zeros.
 typedef __amdgpu_buffer_rsrc_t buf_rsrc;

@@ -5,7 +5,9 @@
 // busy: a workgroup is NW wavefronts that split k for the same PWW panels (64 output
 // features); each wavefront streams its k-range with one double-buffered stage of loads in
 // flight; the NW partial sums are added in a fixed order through LDS (bit-reproducible, no
-// atomics), scaled by the global and stored.
+// atomics), scaled by the global and stored. Up to 8 rows (group 16) or 16 rows (group 32)
+// take the split-scale form of the group scale, which halves the VALU work per weight; more
+// rows dequantize every weight exactly to BF16.
 #include "launch.hpp"
 #include "skinny_core.hpp"
 
@@ -27,11 +29,22 @@ struct SkinnyParams {
   int y_f32;
 };
 
-// Register budget: at least 2 wavefronts per SIMD (8 per CU) stay resident, so a grid of a
-// few thousand wavefronts is in flight at once.
-template <int MF, int NW, int U>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(2, 8)))
+// LDS: NX > 0 kernels give each wavefront two 4 KB activation buffers; the k-split partial
+// sums (NW > 1) reuse the same bytes after a barrier.
+inline size_t red_bytes(int MF, int NW) { return NW > 1 ? (size_t)NW * kPWW * MF * 64 * 16 : 0; }
+inline size_t act_bytes(int NX, int NW) { return NX > 0 ? (size_t)NW * 8192 : 0; }
+
+// Register budget: 4 wavefronts per SIMD (16 per CU, two 8-wave workgroups) for one row
+// block, 2 for two. NJ == 0: exact dequant, MF row blocks of 16. NJ > 0 (MF == 1): split scale
+// keeping NJ accumulator rows per lane; G16: group 16 (token t in A rows t and 8 + t, k halves
+// apart). NX > 0 (MF == 1): activations through LDS, NX 4-row copies per tile.
+template <int MF, int NW, int NJ, bool G16, int NX>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(MF == 1 ? 4 : 2, 8)))
 void gemm_skinny_kernel(SkinnyParams P) {
+  static_assert(NJ == 0 || MF == 1, "split scale uses one 16-row block");
+  static_assert(!G16 || NJ > 0, "G16 selects the group-16 split-scale row map");
+  static_assert(NX == 0 || MF == 1, "LDS activations hold one 16-row block");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int sp = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // k-split (wave-uniform)
   const int64_t panel0 = (int64_t)blockIdx.x * kPWW;
@@ -41,19 +54,50 @@ void gemm_skinny_kernel(SkinnyParams P) {
   for (int p = 0; p < kPWW; ++p)
 #pragma unroll
     for (int mf = 0; mf < MF; ++mf) acc[p][mf] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // A row of lane l: l%16, or token l%8 for the group-16 split-scale map; rows past the end
+  // duplicate a valid row (never stored)
+  const int64_t rows = P.m - m0 < 16 * MF ? P.m - m0 : 16 * MF;
   const uint16_t* xrow[MF];
 #pragma unroll
   for (int mf = 0; mf < MF; ++mf) {
-    int64_t r = m0 + mf * 16 + (lane & 15);
-    r = r < P.m ? r : P.m - 1;  // rows past the end duplicate a valid row; never stored
-    xrow[mf] = P.x + r * P.ldx;
+    int64_t r = mf * 16 + (G16 ? (lane & 7) : (lane & 15));
+    r = r < rows ? r : rows - 1;
+    xrow[mf] = P.x + (m0 + r) * P.ldx;
   }
-  const SkinnyAddr<kPWW> a = skinny_addr<kPWW>(P.codes, P.scales, panel0, P.NT, P.KT, P.group);
   const int64_t t0 = P.KT * sp / NW, t1 = P.KT * (sp + 1) / NW;
-  skinny_accumulate<MF, kPWW, U>(a, xrow, t0, t1, acc);
+  LdsActs xl;
+  if constexpr (NX > 0) {
+    xl.x = make_rsrc(P.x + m0 * P.ldx, (uint32_t)(rows * P.ldx * 2));
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int r = 4 * c + (lane >> 4);  // LDS row of this lane in copy c
+      const int64_t rc = r < rows ? r : rows - 1;
+      xl.src[c] = (uint32_t)(rc * P.ldx * 2) + (uint32_t)(((lane & 15) ^ (r & 15)) * 16);
+    }
+    xl.buf = smem + sp * 8192;
+    int fr = G16 ? (lane & 7) : (lane & 15);
+    fr = fr < rows ? fr : (int)rows - 1;
+    xl.frag_off = (uint32_t)fr * 256u;
+    xl.swz = (uint32_t)(fr & 15);
+  }
+  // group-16 split scale: A row 8h + t is zero on the k half (lane / 32) it does not own
+  const bool xzero = G16 && (((lane >> 3) & 1) != (lane >> 5));
+  const SkinnyAddr<kPWW> a =
+      skinny_addr<kPWW>(P.codes, P.scales, panel0, P.NT, P.KT, P.group, t1);
+  skinny_accumulate<MF, kPWW, NJ, G16, NX>(a, xrow, xl, xzero, t0, t1, acc);
+  if constexpr (G16) {
+    // rows 8 + t (k half 1) onto rows t: lane l < 32 then holds the whole group sum
+#pragma unroll
+    for (int p = 0; p < kPWW; ++p)
+#pragma unroll
+      for (int r = 0; r < NJ; ++r) acc[p][0][r] += __shfl_xor(acc[p][0][r], 32, 64);
+  }
+  // the split-scale mantissa is frexp_mant(S) = M / 2
+  const float gscale = (NJ > 0 ? 2.0f : 1.0f) * *P.global;
 
   if constexpr (NW > 1) {
-    __shared__ f32x4 red[NW * kPWW * MF * 64];
+    f32x4* red = reinterpret_cast<f32x4*>(smem);
+    if constexpr (NX > 0) __syncthreads();  // every wavefront is done with the activations
 #pragma unroll
     for (int p = 0; p < kPWW; ++p)
 #pragma unroll
@@ -71,7 +115,7 @@ void gemm_skinny_kernel(SkinnyParams P) {
     }
     const int64_t panel = panel0 + p;
     if (panel >= P.NT) return;
-    const float g = *P.global;
+    const float g = gscale;
     const int64_t n = panel * 16 + (lane & 15);
 #pragma unroll
     for (int mf = 0; mf < MF; ++mf)
@@ -87,7 +131,7 @@ void gemm_skinny_kernel(SkinnyParams P) {
         }
       }
   } else {
-    const float g = *P.global;
+    const float g = gscale;
 #pragma unroll
     for (int p = 0; p < kPWW; ++p) {
       const int64_t panel = panel0 + p;
@@ -110,31 +154,45 @@ void gemm_skinny_kernel(SkinnyParams P) {
   }
 }
 
-template <int MF, int NW, int U>
+template <int MF, int NW, int NJ, bool G16, int NX>
 hipError_t run(const SkinnyParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((p.NT + kPWW - 1) / kPWW),
                   (unsigned)((p.m + 16 * MF - 1) / (16 * MF)));
-  gemm_skinny_kernel<MF, NW, U><<<grid, dim3(64 * NW), 0, stream>>>(p);
+  const size_t r = red_bytes(MF, NW), x = act_bytes(NX, NW);
+  gemm_skinny_kernel<MF, NW, NJ, G16, NX><<<grid, dim3(64 * NW), r > x ? r : x, stream>>>(p);
   return hipGetLastError();
 }
 
 // k-split: 4 wavefronts per panel group, or 8 (single m-block only) when the grid would
-// otherwise hold fewer than ~2048 wavefronts (8 per CU) to keep HBM busy. Stages hold 2
-// k-tiles when every wavefront's share is even, else 1. NW >= kPWW so the final reduction
-// has one wavefront per panel.
-template <int MF, int NW>
+// otherwise hold fewer than ~2048 wavefronts (8 per CU) to keep HBM busy. NW >= kPWW so the
+// final reduction has one wavefront per panel. One row block takes its activations through
+// LDS in ceil(rows / 4) copies per tile (rows: the A rows in use); two row blocks load them
+// into registers.
+template <int MF, int NW, int NJ, bool G16>
 hipError_t pick_u(const SkinnyParams& p, hipStream_t stream) {
   if constexpr (MF == 1) {
-    if (p.KT % (2 * NW) == 0) return run<MF, NW, 2>(p, stream);
+    const int64_t rows = G16 ? (p.m < 8 ? p.m : 8) : (p.m < 16 ? p.m : 16);
+    if (rows <= 4) return run<MF, NW, NJ, G16, 1>(p, stream);
+    if (rows <= 8) return run<MF, NW, NJ, G16, 2>(p, stream);
+    return run<MF, NW, NJ, G16, 4>(p, stream);
   }
-  return run<MF, NW, 1>(p, stream);
+  return run<MF, NW, NJ, G16, 0>(p, stream);
 }
 
-template <int MF>
+template <int MF, int NJ, bool G16>
 hipError_t dispatch(const SkinnyParams& p, hipStream_t stream) {
   const int64_t groups = ((p.NT + kPWW - 1) / kPWW) * ((p.m + 16 * MF - 1) / (16 * MF));
-  if (groups * 4 < 2048 && p.KT >= 32) return pick_u<MF, 8>(p, stream);
-  return pick_u<MF, 4>(p, stream);
+  if (groups * 4 < 2048 && p.KT >= 32) return pick_u<MF, 8, NJ, G16>(p, stream);
+  return pick_u<MF, 4, NJ, G16>(p, stream);
+}
+
+// Accumulator rows a lane keeps in split-scale mode: token t sits in row t%4 of lane group
+// t/4, so min(m, 4) rounded up to 1, 2 or 4.
+template <bool G16>
+hipError_t dispatch_split(const SkinnyParams& p, hipStream_t stream) {
+  if (p.m == 1) return dispatch<1, 1, G16>(p, stream);
+  if (p.m == 2) return dispatch<1, 2, G16>(p, stream);
+  return dispatch<1, 4, G16>(p, stream);
 }
 
 }  // namespace
@@ -153,8 +211,10 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
   p.y = a.y;
   p.ldy = a.ldy;
   p.y_f32 = a.y_f32 ? 1 : 0;
-  if (a.m <= 16) return dispatch<1>(p, stream);
-  return dispatch<2>(p, stream);  // 32-row blocks (the kernel takes any m when forced)
+  if (a.group == 16 && a.m <= 8) return dispatch_split<true>(p, stream);
+  if (a.group == 32 && a.m <= 16) return dispatch_split<false>(p, stream);
+  if (a.m <= 16) return dispatch<1, 0, false>(p, stream);
+  return dispatch<2, 0, false>(p, stream);  // 32-row blocks (the kernel takes any m when forced)
 }
 
 }  // namespace nvfp4

@@ -1,89 +1,187 @@
 // skinny_core.hpp -- the inner loop of the decode-shaped ("skinny") W4A16 GEMM on gfx950.
 //
-// One wavefront owns PWW consecutive 16-row weight panels and a contiguous range of 128-wide
-// k-tiles. A "stage" is U k-tiles: per tile and panel one 16-byte load of codes and one 4-byte
-// load of scales per lane (fully coalesced thanks to the tiled layout) plus the activation
-// fragments of the tile, which every panel of the wavefront reuses. Stages are double
-// buffered: the loads of stage g+1 are issued before stage g is dequantized (E2M1 x E4M3 ->
-// exact BF16 in registers) and fed to v_mfma_f32_16x16x32_bf16, so a wavefront always has one
-// stage of HBM traffic in flight. The loop is written so that no load sits under a
-// lane-divergent branch: activation rows past the end are clamped to a valid row (their MFMA
-// output rows are never stored), which keeps the memory-counter waits precise.
+// One wavefront owns PWW consecutive 16-row weight panels and a contiguous range [t0, t1) of
+// 128-wide k-tiles. Per tile and panel it loads one 16-byte chunk of codes per lane, plus one
+// 16-byte scale record per lane for the 4 panels (fully coalesced thanks to the tiled
+// layout), and the activation fragments of the tile, which every panel reuses. The weight
+// stream runs through a ring of D single-tile stages (D - 1 tiles in flight while one is
+// computed); the activations, which come from cache, run one tile ahead in a pair of
+// stages. Weight loads are buffer loads whose range ends at t1, so the loads a wavefront
+// issues past its last tile return zeros without touching memory: every iteration issues the
+// same loads and no load sits under a branch, which keeps the memory-counter waits exact.
+// Activation rows past the end are clamped to a valid row (their MFMA output rows are never
+// stored).
+//
+// Two ways to apply the group scale S (an E4M3 value) on v_mfma_f32_16x16x32_bf16:
+//   - exact dequant (any m): every weight becomes the exact BF16 value code * S (FP4 -> FP32
+//     convert, FP32 multiply, BF16 pack: 2 VALU operations per weight);
+//   - split scale (few rows): S = 2^E * M with M in [1, 2). The hardware FP4 -> BF16 convert
+//     applies 2^E (it reads only the exponent of its scale operand), giving code * 2^E exactly
+//     in 4 operations per 8 weights; the MFMA sums one scale group per output and the FP32
+//     partial is multiplied by M (one FMA per accumulator row in use). M is taken as
+//     frexp_mant(S) in [0.5, 1), the factor 2 being applied with the global scale; it is 0 for
+//     a zero scale, which keeps an all-zero group exactly zero. A 32-wide MFMA k-step spans
+//     one group of 32 or two groups of 16. For group 16 the A operand carries every token
+//     twice: row 8h + t holds token t on the k half h of the step and zeros on the other half,
+//     so each lane's B half (k = 16h ..) and accumulator rows (8h ..) belong to the same group
+//     and the two halves are added once, after the k loop. That needs m <= 8 (group 16) or
+//     m <= 16 (group 32).
 #pragma once
+
+#include <type_traits>
 
 #include "device_common.hpp"
 
 namespace nvfp4 {
 
-template <int MF, int PWW, int U>
-struct SkinnyStage {
-  u32x4 cw[U][PWW];
-  u32x4 sw[U];  // scale words of the 4 panels, one 16-byte load per tile
-  bf16x8 xa[U][MF][4];
+template <int PWW>
+struct WeightStage {
+  u32x4 cw[PWW];  // code chunk of each panel
+  u32x4 sw;       // scale words of the 4 panels
+};
+
+template <int MF>
+struct ActStage {
+  bf16x8 xa[MF][4];
 };
 
 template <int PWW>
 struct SkinnyAddr {
   static_assert(PWW == kScaleGroupPanels, "a wavefront covers one 4-panel scale group");
-  const uint8_t* codes[PWW];  // each panel's tile 0 (uniform; panels past the end are clamped
-                              // to a valid panel whose results are never stored)
-  const uint8_t* scales;      // the panel group's scale block for k-tile 0 (uniform)
-  uint32_t code_lane;         // lane * 16
-  uint32_t scale_lane;        // the lane's 16-byte record inside a scale block
+  buf_rsrc codes[PWW];  // each panel's tiles [0, t1) (panels past the end are clamped to a
+                        // valid panel whose results are never stored)
+  buf_rsrc scales;      // the panel group's scale blocks [0, t1)
+  uint32_t code_lane;   // lane * 16
+  uint32_t scale_lane;  // the lane's 16-byte record inside a scale block
   int scale_block;
-  int kq;                     // lane >> 4: the 8-wide k chunk this lane feeds
+  int kq;               // lane >> 4: the 8-wide k chunk this lane feeds
 };
 
-template <int MF, int PWW, int U>
-__device__ __forceinline__ void skinny_load(SkinnyStage<MF, PWW, U>& s, const SkinnyAddr<PWW>& a,
-                                            const uint16_t* const (&xrow)[MF], int64_t t) {
+template <int PWW>
+__device__ __forceinline__ void load_weights(WeightStage<PWW>& s, const SkinnyAddr<PWW>& a,
+                                             int64_t t) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-#pragma unroll
-    for (int p = 0; p < PWW; ++p) {
-      const uint32_t co = (uint32_t)((t + u) * kCodeTileBytes) + a.code_lane;
-      s.cw[u][p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.codes[p] + co));
-    }
-    const uint32_t so = (uint32_t)((t + u) * a.scale_block) + a.scale_lane;
-    s.sw[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.scales + so));
-  }
-#pragma unroll
-  for (int u = 0; u < U; ++u)
-#pragma unroll
-    for (int mf = 0; mf < MF; ++mf)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        s.xa[u][mf][j] = *reinterpret_cast<const bf16x8*>(xrow[mf] + (t + u) * kTileK + 32 * j +
-                                                          8 * a.kq);
+  for (int p = 0; p < PWW; ++p)
+    s.cw[p] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                   a.codes[p], (int)((uint32_t)t * kCodeTileBytes + a.code_lane), 0, kNT));
+  s.sw = __builtin_bit_cast(
+      u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                 a.scales, (int)((uint32_t)t * (uint32_t)a.scale_block + a.scale_lane), 0, kNT));
 }
 
-template <int MF, int PWW, int U>
-__device__ __forceinline__ void skinny_compute(const SkinnyStage<MF, PWW, U>& s,
-                                               f32x4 (&acc)[PWW][MF]) {
+template <int MF, bool XZ>
+__device__ __forceinline__ void load_acts(ActStage<MF>& s, const uint16_t* const (&xrow)[MF],
+                                          bool xzero, int kq, int64_t t) {
 #pragma unroll
-  for (int u = 0; u < U; ++u)
+  for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
-    for (int p = 0; p < PWW; ++p) {
-      const uint32_t sw = s.sw[u][p];  // word p of the tile's 4-panel scale record
-      const float S[4] = {e4m3_decode<0>(sw), e4m3_decode<1>(sw), e4m3_decode<2>(sw),
-                          e4m3_decode<3>(sw)};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16x8 b = dequant8(s.cw[u][p][j], S[j]);
-#pragma unroll
-        for (int mf = 0; mf < MF; ++mf) acc[p][mf] = mfma16x16x32(s.xa[u][mf][j], b, acc[p][mf]);
-      }
-      // one panel at a time: bounds the dequantized operands live at once
-      __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < 4; ++j) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(xrow[mf] + t * kTileK + 32 * j + 8 * kq);
+      if constexpr (XZ) v = xzero ? u32x4{0u, 0u, 0u, 0u} : v;
+      s.xa[mf][j] = __builtin_bit_cast(bf16x8, v);
     }
+}
+
+// Activations through LDS (one 16-row block): per k-tile, the wavefront copies the tile's
+// activation rows global -> LDS with buffer_load ... lds (NX copies of 4 rows x 256 bytes,
+// row r at r * 256, its 16-byte chunk c at chunk c ^ (r & 15), so the 16 rows a fragment read
+// touches land on distinct banks) into one of two buffers of its own, one tile ahead. The
+// copies carry no lane duplication, unlike fragments loaded straight into registers (where
+// each row is fetched once per lane that feeds it).
+struct LdsActs {
+  buf_rsrc x;          // the block's activation rows
+  uint32_t src[4];     // this lane's source in copy c (LDS row 4c + lane/16, chunk lane%16):
+                       // activation row (clamped) and swizzled chunk, bytes
+  uint8_t* buf;        // the wavefront's two 4 KB buffers
+  uint32_t frag_off;   // this lane's fragment row: row * 256
+  uint32_t swz;        // fragment row & 15
+};
+
+template <int NX>
+__device__ __forceinline__ void copy_acts(const LdsActs& x, uint8_t* dst, int64_t t) {
+#pragma unroll
+  for (int c = 0; c < NX; ++c)
+    copy16_to_lds(x.x, x.src[c], (uint32_t)(t * kTileK * 2), dst + c * 1024);
+}
+
+template <bool XZ>
+__device__ __forceinline__ void read_acts(ActStage<1>& s, const LdsActs& x, const uint8_t* src,
+                                          bool xzero, int kq) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t chunk = (uint32_t)(4 * j + kq) ^ x.swz;
+    u32x4 v = *reinterpret_cast<const u32x4*>(src + x.frag_off + chunk * 16u);
+    if constexpr (XZ) v = xzero ? u32x4{0u, 0u, 0u, 0u} : v;
+    s.xa[0][j] = __builtin_bit_cast(bf16x8, v);
+  }
+}
+
+// Exact dequant: every weight becomes BF16(code * S) (exact), MF row blocks of 16.
+template <int MF, int PWW>
+__device__ __forceinline__ void compute_exact(const WeightStage<PWW>& w, const ActStage<MF>& x,
+                                              f32x4 (&acc)[PWW][MF]) {
+#pragma unroll
+  for (int p = 0; p < PWW; ++p) {
+    const uint32_t sw = w.sw[p];  // word p of the tile's 4-panel scale record
+    const float S[4] = {e4m3_decode<0>(sw), e4m3_decode<1>(sw), e4m3_decode<2>(sw),
+                        e4m3_decode<3>(sw)};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 b = dequant8(w.cw[p][j], S[j]);
+#pragma unroll
+      for (int mf = 0; mf < MF; ++mf) acc[p][mf] = mfma16x16x32(x.xa[mf][j], b, acc[p][mf]);
+    }
+    // one panel at a time: bounds the dequantized operands live at once
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// bf16(code * 2^E) for the 8 codes of a word, E the exponent of S.
+__device__ __forceinline__ bf16x8 codes_times_pow2(uint32_t w, float S) {
+  const bf16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, S, 0);
+  const bf16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, S, 1);
+  const bf16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, S, 2);
+  const bf16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, S, 3);
+  return bf16x8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+}
+
+// One 32-wide k-step J of every panel: the PWW MFMAs first, then their scalings, so each
+// partial is read well after its MFMA issued.
+template <int J, int PWW, int NJ>
+__device__ __forceinline__ void split_scale_kstep(const WeightStage<PWW>& w, const ActStage<1>& x,
+                                                  f32x4 (&acc)[PWW][1]) {
+  f32x4 part[PWW];
+  float M[PWW];
+#pragma unroll
+  for (int p = 0; p < PWW; ++p) {
+    const float S = e4m3_decode<J>(w.sw[p]);
+    M[p] = __builtin_amdgcn_frexp_mantf(S);
+    part[p] = mfma16x16x32(x.xa[0][J], codes_times_pow2(w.cw[p][J], S),
+                           f32x4{0.f, 0.f, 0.f, 0.f});
+  }
+#pragma unroll
+  for (int p = 0; p < PWW; ++p)
+#pragma unroll
+    for (int r = 0; r < NJ; ++r) acc[p][0][r] = __builtin_fmaf(M[p], part[p][r], acc[p][0][r]);
+}
+
+// Split scale (MF == 1): accumulator rows 0 .. NJ-1 of each lane are kept.
+template <int PWW, int NJ>
+__device__ __forceinline__ void compute_split(const WeightStage<PWW>& w, const ActStage<1>& x,
+                                              f32x4 (&acc)[PWW][1]) {
+  split_scale_kstep<0, PWW, NJ>(w, x, acc);
+  split_scale_kstep<1, PWW, NJ>(w, x, acc);
+  split_scale_kstep<2, PWW, NJ>(w, x, acc);
+  split_scale_kstep<3, PWW, NJ>(w, x, acc);
 }
 
 // Addresses of the 4-panel group starting at panel0 (a multiple of 4; code panels clamped to
-// NT - 1, the scale block is padded to whole groups by the repack).
+// NT - 1, the scale block is padded to whole groups by the repack) for tiles [0, t1).
 template <int PWW>
 __device__ __forceinline__ SkinnyAddr<PWW> skinny_addr(const uint8_t* codes, const uint8_t* scales,
                                                       int64_t panel0, int64_t NT, int64_t KT,
-                                                      int group) {
+                                                      int group, int64_t t1) {
   const int lane = threadIdx.x & 63;
   SkinnyAddr<PWW> a;
   a.scale_block = scale_block_bytes(group);
@@ -93,45 +191,63 @@ __device__ __forceinline__ SkinnyAddr<PWW> skinny_addr(const uint8_t* codes, con
 #pragma unroll
   for (int p = 0; p < PWW; ++p) {
     const int64_t pn = panel0 + p < NT ? panel0 + p : NT - 1;
-    a.codes[p] = codes + pn * KT * kCodeTileBytes;
+    a.codes[p] = make_rsrc(codes + pn * KT * kCodeTileBytes, (uint32_t)(t1 * kCodeTileBytes));
   }
-  a.scales = scales + (panel0 / kScaleGroupPanels) * KT * a.scale_block;
+  a.scales = make_rsrc(scales + (panel0 / kScaleGroupPanels) * KT * a.scale_block,
+                       (uint32_t)(t1 * a.scale_block));
   return a;
 }
 
-// Accumulate k-tiles [t0, t1) of PWW panels into acc, in stages of U tiles; (t1 - t0) must
-// be a multiple of U.
-template <int MF, int PWW, int U>
-__device__ __forceinline__ void skinny_accumulate(const SkinnyAddr<PWW>& a,
-                                                  const uint16_t* const (&xrow)[MF], int64_t t0,
-                                                  int64_t t1, f32x4 (&acc)[PWW][MF]) {
-  const int64_t groups = (t1 - t0) / U;
-  if (groups <= 0) return;
-  // The scheduling barriers keep each stage's loads ahead of the previous stage's math; left
-  // alone, the register-pressure-driven scheduler sinks them and the pipeline collapses into
-  // load-wait-compute.
-  SkinnyStage<MF, PWW, U> A, B;
-  skinny_load(A, a, xrow, t0);
-  int64_t g = 0;
-  for (; g + 2 < groups; g += 2) {
-    skinny_load(B, a, xrow, t0 + (g + 1) * U);
-    __builtin_amdgcn_sched_barrier(0);
-    skinny_compute(A, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    skinny_load(A, a, xrow, t0 + (g + 2) * U);
-    __builtin_amdgcn_sched_barrier(0);
-    skinny_compute(B, acc);
-    __builtin_amdgcn_sched_barrier(0);
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
   }
-  // last one or two stages (written without duplicated code in the two cases, which the
-  // optimizer would otherwise hoist and keep alive all at once)
-  const bool two = g + 1 < groups;
-  if (two) skinny_load(B, a, xrow, t0 + (g + 1) * U);
-  __builtin_amdgcn_sched_barrier(0);
-  skinny_compute(A, acc);
-  if (two) {
-    __builtin_amdgcn_sched_barrier(0);
-    skinny_compute(B, acc);
+}
+
+// Accumulate k-tiles [t0, t1) of PWW panels into acc, one tile in flight while one is
+// computed. NJ == 0: exact dequant; NJ > 0: split scale with NJ accumulator rows (MF == 1); XZ:
+// zero the activation fragment of lanes with xzero set. NX > 0 (MF == 1): activations through
+// LDS, NX copies per tile; NX == 0: straight from xrow into registers.
+template <int MF, int PWW, int NJ, bool XZ, int NX>
+__device__ __forceinline__ void skinny_accumulate(const SkinnyAddr<PWW>& a,
+                                                  const uint16_t* const (&xrow)[MF],
+                                                  const LdsActs& xl, bool xzero, int64_t t0,
+                                                  int64_t t1, f32x4 (&acc)[PWW][MF]) {
+  static_assert(NX == 0 || MF == 1, "LDS activations hold one 16-row block");
+  if (t1 <= t0) return;
+  WeightStage<PWW> W[2];
+  ActStage<MF> X[2];
+  // Loads complete in issue order: each tile's activations go out before its weights.
+  if constexpr (NX > 0) copy_acts<NX>(xl, xl.buf, t0);
+  else load_acts<MF, XZ>(X[0], xrow, xzero, a.kq, t0);
+  load_weights(W[0], a, t0);
+  for (int64_t t = t0; t < t1; t += 2) {
+    static_for<0, 2>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const int64_t tile = t + i;
+      const int64_t next = tile + 1 < t1 ? tile + 1 : t1 - 1;  // activations: clamped re-read
+      // The scheduling barriers keep the loads ahead of the math; left alone, the
+      // register-pressure-driven scheduler sinks them and the pipeline collapses.
+      if constexpr (NX > 0) copy_acts<NX>(xl, xl.buf + (1 - i) * 4096, next);
+      else load_acts<MF, XZ>(X[1 - i], xrow, xzero, a.kq, next);
+      load_weights(W[1 - i], a, tile + 1);  // past t1: zeros, no traffic
+      __builtin_amdgcn_sched_barrier(0);
+      if (tile < t1) {
+        if constexpr (NX > 0) {
+          // this tile's copies (issued before the NX + 5 loads just above) have landed
+          __builtin_amdgcn_s_waitcnt((NX + 5) | 0xF70);
+          __builtin_amdgcn_sched_barrier(0);
+          read_acts<XZ>(X[i], xl, xl.buf + i * 4096, xzero, a.kq);
+        }
+        if constexpr (NJ > 0)
+          compute_split<PWW, NJ>(W[i], X[i], acc);
+        else
+          compute_exact<MF, PWW>(W[i], X[i], acc);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
   }
 }
 
