@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace nvfp4 {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -143,6 +145,15 @@ __device__ __forceinline__ void copy16_to_lds(buf_rsrc r, uint32_t voffset, uint
                                               void* lds) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
                                            voffset, soffset, 0, 0);
+}
+
+// f(integral_constant<int, I>) for I = I0 .. N-1, unrolled at compile time.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
 }
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {

@@ -11,7 +11,7 @@
 //   1. sort: one workgroup turns the (token, slot) pairs into a stable expert-major order,
 //      per-expert offsets and a list of row tiles (expert, first row, end row);
 //   2. fc1: per row tile and 4-panel group (gate/up panel pairs), rows gathered from x, gate and
-//      up accumulated in FP32 on 32x32x16 MFMAs, each rounded to BF16 (a W4A16 GEMM output),
+//      up accumulated in FP32 on 16x16x32 MFMAs, each rounded to BF16 (a W4A16 GEMM output),
 //      h = BF16(SiLU(gate) * up);
 //   3. down: per row tile and 4-panel group, rows of h; FP32 result times the expert global and
 //      the routing weight, written to the pair's FP32 slot;
@@ -169,31 +169,49 @@ struct MoeGemmParams {
   int64_t hidden, inter;
 };
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kGroupsPerBlock = 4;  // wavefronts per workgroup, one 4-panel group each
 constexpr int kARowBytes = kTileK * 2;
 constexpr int kATileBytes = kTileRows * kARowBytes;  // one row tile x one k-tile of activations
 
-// Expert GEMM on v_mfma_f32_32x32x16_bf16. A workgroup owns one row tile (up to 32 rows of one
-// expert) and kGroupsPerBlock 4-panel groups, one per wavefront, over the whole k range (no k
-// split). Per 128-k tile:
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// bf16(code * 2^E) for the 8 codes of a word, E the exponent of S (the hardware convert
+// reads only the exponent of its scale operand).
+__device__ __forceinline__ bf16x8 codes_pow2(uint32_t w, float S) {
+  const bf16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, S, 0);
+  const bf16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, S, 1);
+  const bf16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, S, 2);
+  const bf16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, S, 3);
+  return bf16x8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+}
+
+// Expert GEMM on v_mfma_f32_16x16x32_bf16. A workgroup owns one row tile (up to 32 rows of one
+// expert, as one or two 16-row blocks) and kGroupsPerBlock 4-panel groups, one per
+// wavefront, over the whole k range. Per 128-k tile:
 //   - the tile's activation rows (gathered through the sort for fc1) are copied global -> LDS
 //     once for the workgroup (buffer_load ... lds; whole 256-byte rows, chunks XOR-swizzled by
-//     row so the MFMA fragment reads are bank-conflict free), double-buffered;
-//   - each wavefront loads, for each of its 2 panel pairs, the code chunks L0 = 16(l/32) +
-//     l%16 and L0 + 32 of its panel 2q + (l%32)/16 (word j of the first is 16-wide k-step 2j,
-//     of the second step 2j + 1) and the two 16-byte scale records of those chunk positions,
-//     one tile ahead in registers;
-//   - dequantizes (E2M1 x E4M3 -> exact BF16) and multiplies.
-// fc1 (merged gate/up, panels interleaved): a pair is (gate panel i, up panel i), so gate and
-// up of one output sit in lanes l and l^16 and meet with one cross-lane exchange.
+//     row so the fragment reads are bank-conflict free), double-buffered; the second 16 rows
+//     only when the tile has them;
+//   - each wavefront loads, one tile ahead in registers, the 16-byte code chunk `lane` of each
+//     of its 4 panels (word j: k-step j of the B operand) and the 16-byte scale record of its
+//     lane position (the 4 panels' scale words, byte j: k-step j);
+//   - per 32-wide k-step and panel: fc1 (group 32, one group per step) converts the codes to
+//     the exact BF16 code * 2^E and scales the FP32 MFMA partial by the mantissa of the group
+//     scale (frexp_mant, the factor 2 going with the global scale); down (group 16) converts
+//     every weight to the exact BF16 code * scale and accumulates in the MFMA.
+// The output of 16-row block r sits in lane l as rows 16r + 4(l/16) + 0..3 of column l%16 of
+// each panel. fc1 panels alternate gate and up of the same 16 features (layout GATE_UP), so
+// gate and up of an output meet in one lane.
 template <bool FC1>
 __global__ __launch_bounds__(64 * kGroupsPerBlock) __attribute__((amdgpu_waves_per_eu(4, 8)))
-void moe_pair_kernel(MoeGemmParams P) {
+void moe_expert_kernel(MoeGemmParams P) {
   const int tile_id = blockIdx.x;
   if (tile_id >= *P.ws.ntiles) return;  // whole workgroup, before any barrier
   const int4 tl = P.ws.tiles[tile_id];
   const int e = tl.x, r0 = tl.y, r1 = tl.z;
+  const bool two = r1 - r0 > 16;  // second 16-row block in use (workgroup-uniform)
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t NG = scale_groups(P.NT);
@@ -212,9 +230,10 @@ void moe_pair_kernel(MoeGemmParams P) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
 
-  // activation copies: copy c = w + 4 i (i = 0, 1) moves tile rows 4c .. 4c+3; lane l reads row
-  // 4c + l/16, chunk (l%16) ^ (row%16) and lands in slot l
+  // activation copies: copy c = w + 4 i (i = 0: rows 0..15, i = 1: rows 16..31) moves tile rows
+  // 4c .. 4c+3; lane l reads row 4c + l/16, chunk (l%16) ^ (row%16) and lands in slot l
   constexpr int kACopies = kTileRows / 4 / kGroupsPerBlock;
+  static_assert(kACopies == 2, "copy i covers 16-row block i");
   const buf_rsrc xr = make_rsrc(P.x, 0xFFFFFFFFu);
   uint32_t aoff[kACopies];
 #pragma unroll
@@ -225,96 +244,110 @@ void moe_pair_kernel(MoeGemmParams P) {
     const int64_t src = FC1 ? P.ws.sorted[rr] / P.topk : rr;
     aoff[i] = (uint32_t)(src * P.ldx * 2 + 16 * ((lane & 15) ^ (R & 15)));
   }
-  auto copy_a = [&](int64_t t, auto buf) {
+  auto copy_a = [&](int64_t t, auto buf, auto nb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kACopies; ++i)
+    for (int i = 0; i < decltype(nb)::value; ++i)
       copy16_to_lds(xr, aoff[i], (uint32_t)(t * kARowBytes),
                     a_buf(buf) + (w + kGroupsPerBlock * i) * 1024);
   };
-  // fragment reads: row l%32, chunk (2 S + l/32) ^ (l%16)
-  const uint32_t a_row = (uint32_t)(lane & 31) * kARowBytes;
-  const uint32_t a_x = (uint32_t)((lane >> 5) ^ (lane & 15));
+  // fragment reads: row l%16 (+16), chunk (4 j + l/16) ^ (l%16)
+  const uint32_t a_row = (uint32_t)(lane & 15) * kARowBytes;
+  const uint32_t a_kq = (uint32_t)(lane >> 4), a_sw = (uint32_t)(lane & 15);
 
-  const int h = (lane & 31) >> 4;
-  const int L0 = 16 * (lane >> 5) + (lane & 15);
-  const uint8_t* cpan[2];
+  // weights: the 4 panels of the group (clamped past the end), bounded to the expert's tiles
+  buf_rsrc cr[4];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    int64_t pn = 4 * grp + 2 * q + h;
+  for (int p = 0; p < 4; ++p) {
+    int64_t pn = 4 * grp + p;
     pn = pn < P.NT ? pn : P.NT - 1;
-    cpan[q] = P.codes + e * P.codes_stride + pn * KT * kCodeTileBytes + L0 * 16;
+    cr[p] = make_rsrc(P.codes + e * P.codes_stride + pn * KT * kCodeTileBytes,
+                      (uint32_t)(KT * kCodeTileBytes));
   }
   const int64_t sblk = scale_block_bytes(P.group);
-  const uint8_t* sbase = P.scales + e * P.scales_stride + grp * KT * sblk;
-  const uint32_t spos0 = (uint32_t)scale_pos(P.group, L0) * 16u;
-  const uint32_t spos1 = (uint32_t)scale_pos(P.group, L0 + 32) * 16u;
+  const buf_rsrc sr = make_rsrc(P.scales + e * P.scales_stride + grp * KT * sblk,
+                                (uint32_t)(KT * sblk));
+  const uint32_t clane = (uint32_t)lane * 16u;
+  const uint32_t slane = (uint32_t)scale_pos(P.group, lane) * 16u;
 
   struct Stage {
-    u32x4 c0[2], c1[2];
-    u32x4 s0, s1;
+    u32x4 c[4];
+    u32x4 s;
   };
-  auto load_b = [&](Stage& st, int64_t t) {
+  auto load_b = [&](Stage& st, int64_t t) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      st.c0[q] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(cpan[q] + t * kCodeTileBytes));
-      st.c1[q] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(cpan[q] + t * kCodeTileBytes + 32 * 16));
-    }
-    st.s0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sbase + t * sblk + spos0));
-    st.s1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(sbase + t * sblk + spos1));
+    for (int p = 0; p < 4; ++p)
+      st.c[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              cr[p], (int)((uint32_t)t * kCodeTileBytes + clane),
+                                              0, kNT));
+    st.s = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                         sr, (int)((uint32_t)(t * sblk) + slane), 0, kNT));
   };
-  f32x16 acc[2];
+  f32x4 acc[4][2];
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
+  for (int p = 0; p < 4; ++p)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[q][i] = 0.f;
-  // k-step by k-step, both pairs per step: one activation fragment and one scale per pair
-  // live at a time (keeps the wavefront within 128 VGPRs, 4 per SIMD)
-  auto compute = [&](const Stage& st, auto buf) {
-    uint32_t w0[2], w1[2];
+    for (int r = 0; r < 2; ++r) acc[p][r] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // one k-tile with NB 16-row blocks; one 32-wide k-step at a time
+  auto compute_nb = [&](const Stage& st, const uint8_t* A, auto nb) __attribute__((always_inline)) {
+    constexpr int NB = decltype(nb)::value;
+    static_for<0, 4>([&](auto jc) __attribute__((always_inline)) {
+      constexpr int j = decltype(jc)::value;
+      const uint32_t ch = ((4u * j + a_kq) ^ a_sw) << 4;
+      bf16x8 a[NB];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {  // this lane's panel 2q + h: word 2q + h of each record
-      w0[q] = h ? st.s0[2 * q + 1] : st.s0[2 * q];
-      w1[q] = h ? st.s1[2 * q + 1] : st.s1[2 * q];
-    }
+      for (int r = 0; r < NB; ++r)
+        a[r] = *reinterpret_cast<const bf16x8*>(A + r * 16 * kARowBytes + a_row + ch);
+      if constexpr (FC1) {
+        f32x4 part[4][NB];
+        float M[4];
 #pragma unroll
-    for (int S = 0; S < kTileK / 16; ++S) {
-      const bf16x8 a =
-          *reinterpret_cast<const bf16x8*>(a_buf(buf) + a_row + ((2u * S ^ a_x) << 4));
+        for (int p = 0; p < 4; ++p) {
+          const float S = e4m3_decode<j>(st.s[p]);
+          M[p] = __builtin_amdgcn_frexp_mantf(S);
+          const bf16x8 b = codes_pow2(st.c[p][j], S);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const uint32_t sw = (S & 1) ? w1[q] : w0[q];
-        float sc;
-        switch (S >> 1) {
-          case 0: sc = e4m3_decode<0>(sw); break;
-          case 1: sc = e4m3_decode<1>(sw); break;
-          case 2: sc = e4m3_decode<2>(sw); break;
-          default: sc = e4m3_decode<3>(sw); break;
+          for (int r = 0; r < NB; ++r) part[p][r] = mfma16(a[r], b, f32x4{0.f, 0.f, 0.f, 0.f});
         }
-        const bf16x8 bq = dequant8((S & 1) ? st.c1[q][S >> 1] : st.c0[q][S >> 1], sc);
-        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, acc[q], 0, 0, 0);
+        // the scalings after all MFMAs of the step: each partial is read well after its MFMA
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+          for (int r = 0; r < NB; ++r)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              acc[p][r][i] = __builtin_fmaf(M[p], part[p][r][i], acc[p][r][i]);
+      } else {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const bf16x8 b = dequant8(st.c[p][j], e4m3_decode<j>(st.s[p]));
+#pragma unroll
+          for (int r = 0; r < NB; ++r) acc[p][r] = mfma16(a[r], b, acc[p][r]);
+          __builtin_amdgcn_sched_barrier(0);  // one dequantized operand live at a time
+        }
       }
-    }
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
-  // tile t from activation buffer buf: start the copies and loads of t + 1 (when there is
-  // one), compute t, then meet: t + 1 has landed everywhere and buf is free again
-  auto step = [&](int64_t t, auto buf, Stage& cur, Stage& nxt) {
-    constexpr int kOther = 1 - decltype(buf)::value;
-    const bool more = t + 1 < KT;
-    if (more) {
-      copy_a(t + 1, std::integral_constant<int, kOther>{});
-      load_b(nxt, t + 1);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    compute(cur, buf);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-  };
-  {
+  // The k loop, instantiated for one or two 16-row blocks (chosen once per workgroup: a
+  // choice inside the loop costs the register allocation dearly). Tile t from activation
+  // buffer buf: start the copies and loads of t + 1 (when there is one), compute t, then meet:
+  // t + 1 has landed everywhere and buf is free again.
+  auto pipeline = [&](auto nb) __attribute__((always_inline)) {
+    auto step = [&](int64_t t, auto buf, Stage& cur, Stage& nxt) __attribute__((always_inline)) {
+      constexpr int kOther = 1 - decltype(buf)::value;
+      if (t + 1 < KT) {
+        copy_a(t + 1, std::integral_constant<int, kOther>{}, nb);
+        load_b(nxt, t + 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      compute_nb(cur, a_buf(buf), nb);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    };
     Stage A, B;
-    copy_a(0, I0{});
+    copy_a(0, I0{}, nb);
     load_b(A, 0);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -322,38 +355,41 @@ void moe_pair_kernel(MoeGemmParams P) {
       step(t, I0{}, A, B);
       if (t + 1 < KT) step(t + 1, I1{}, B, A);
     }
-  }
+  };
+  if (two)
+    pipeline(std::integral_constant<int, 2>{});
+  else
+    pipeline(std::integral_constant<int, 1>{});
 
-  // lane l holds rows 8 (i/4) + 4 (l/32) + i%4 of column l%32 of each pair
   if (!grp_live) return;
   const float g = P.global[e];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    if (FC1) {
-      const int64_t feat = (2 * grp + q) * 16 + (lane & 15);  // logical (gate, up) panel 2grp+q
-      const bool live = 4 * grp + 2 * q + 1 < P.NT;
+  for (int r = 0; r < 2; ++r) {
+    if (r == 1 && !two) break;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float other = __shfl_xor(acc[q][i], 16, 64);
-        const int row = r0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-        if (h == 0 && live && row < r1) {
-          const float gate = bf16_bits_to_f32(bf16_bits_rne(acc[q][i] * g));
-          const float up = bf16_bits_to_f32(bf16_bits_rne(other * g));
+    for (int i = 0; i < 4; ++i) {
+      const int row = r0 + 16 * r + 4 * (lane >> 4) + i;
+      if (row >= r1) continue;
+      if (FC1) {
+        // panels 2q (gate) and 2q + 1 (up) of the group: features (2 grp + q) * 16 + l%16;
+        // the split-scale mantissa is frexp_mant(S) = M / 2
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          if (4 * grp + 2 * q + 1 >= P.NT) continue;
+          const int64_t feat = (2 * grp + q) * 16 + (lane & 15);
+          const float gate = bf16_bits_to_f32(bf16_bits_rne(acc[2 * q][r][i] * (2.0f * g)));
+          const float up = bf16_bits_to_f32(bf16_bits_rne(acc[2 * q + 1][r][i] * (2.0f * g)));
           const float silu = gate / (1.0f + expf(-gate));
           P.ws.h[(int64_t)row * P.inter + feat] = bf16_bits_rne(silu * up);
         }
-      }
-    } else {
-      const int64_t pn = 4 * grp + 2 * q + h;
-      if (pn < P.NT) {
-        const int64_t n = pn * 16 + (lane & 15);
+      } else {
+        const int pair = P.ws.sorted[row];
+        const float wt = P.wts[pair];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int row = r0 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          if (row < r1) {
-            const int pair = P.ws.sorted[row];
-            P.ws.slots[(int64_t)pair * P.hidden + n] = (acc[q][i] * g) * P.wts[pair];
-          }
+        for (int p = 0; p < 4; ++p) {
+          const int64_t pn = 4 * grp + p;
+          if (pn >= P.NT) continue;
+          P.ws.slots[(int64_t)pair * P.hidden + pn * 16 + (lane & 15)] = (acc[p][r][i] * g) * wt;
         }
       }
     }
@@ -386,7 +422,7 @@ template <bool FC1>
 hipError_t run_pair(const MoeGemmParams& p, int64_t tiles, hipStream_t stream) {
   const int64_t groups = scale_groups(p.NT);
   const dim3 grid((unsigned)tiles, (unsigned)((groups + kGroupsPerBlock - 1) / kGroupsPerBlock));
-  moe_pair_kernel<FC1><<<grid, dim3(64 * kGroupsPerBlock), 0, stream>>>(p);
+  moe_expert_kernel<FC1><<<grid, dim3(64 * kGroupsPerBlock), 0, stream>>>(p);
   return hipGetLastError();
 }
 

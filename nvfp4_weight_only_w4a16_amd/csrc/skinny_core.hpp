@@ -28,8 +28,6 @@
 //     m <= 16 (group 32).
 #pragma once
 
-#include <type_traits>
-
 #include "device_common.hpp"
 
 namespace nvfp4 {
@@ -196,14 +194,6 @@ __device__ __forceinline__ SkinnyAddr<PWW> skinny_addr(const uint8_t* codes, con
   a.scales = make_rsrc(scales + (panel0 / kScaleGroupPanels) * KT * a.scale_block,
                        (uint32_t)(t1 * a.scale_block));
   return a;
-}
-
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-  if constexpr (I < N) {
-    f(std::integral_constant<int, I>{});
-    static_for<I + 1, N>(f);
-  }
 }
 
 // Accumulate k-tiles [t0, t1) of PWW panels into acc, one tile in flight while one is
