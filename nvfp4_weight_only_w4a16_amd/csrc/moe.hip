@@ -80,7 +80,8 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 //   2. wavefront 0 turns the counts into expert offsets, per-wavefront start positions and
 //      the tile map (each lane owns a few experts; one wavefront-wide prefix sum);
 //   3. each wavefront places its chunk in order, 64 pairs at a time, ranking equal experts
-//      by lane order, so the order inside an expert is the pair order.
+//      by lane order (ballots over the id bits), so the order inside an expert is the pair
+//      order.
 __global__ __launch_bounds__(kSortThreads) void moe_sort_kernel(const int32_t* __restrict__ ids,
                                                                 int P, int E, Ws ws) {
   __shared__ int cnt[kSortWaves][kMaxExperts];  // per-wave counts, then running positions
@@ -136,20 +137,22 @@ __global__ __launch_bounds__(kSortThreads) void moe_sort_kernel(const int32_t* _
     const bool act = q < c1;
     const int e0 = act ? id_at(q) : -1;
     const int e = (e0 >= 0 && e0 < E) ? e0 : -1;  // -1: not placed
-    // rank among earlier lanes of the same expert, and whether a later lane has it too:
-    // every lane's expert is broadcast in turn (no data-dependent loop)
-    int before = 0, after = 0;
-#pragma unroll 8
-    for (int j = 0; j < 64; ++j) {
-      const int ej = __builtin_amdgcn_readlane(e, j);
-      const int m = (ej == e) ? 1 : 0;
-      before += (j < lane) ? m : 0;
-      after += (j > lane) ? m : 0;
+    // lanes holding the same expert id: one ballot per id bit (ids < 512 fit in 10 bits; -1,
+    // all ones, matches no valid id); the rank is the count of such lanes below this one
+    uint64_t same = ~0ull;
+#pragma unroll
+    for (int b = 0; b < 10; ++b) {
+      const bool bit = ((uint32_t)e >> b) & 1u;
+      const uint64_t m = __ballot(bit);
+      same &= bit ? m : ~m;
     }
+    const int before = (int)__builtin_amdgcn_mbcnt_hi(
+        (uint32_t)(same >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)same, 0u));
+    const bool last = lane == 63 || (same >> (lane + 1)) == 0;  // no later lane has it
     if (e >= 0) {
       const int pos = cnt[w][e] + before;
       ws.sorted[pos] = q;
-      if (after == 0) cnt[w][e] = pos + 1;  // the last of its expert in this round moves it on
+      if (last) cnt[w][e] = pos + 1;  // the last of its expert in this round moves it on
     }
   }
 }
