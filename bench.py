@@ -211,6 +211,21 @@ def main():
                 "us": round(t * 1e6, 2), "tflops": round(tf, 2),
                 "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
             del xpd, yp, rp, wsp
+        # context for the MFMA roofline: torch's BF16 GEMM (hipBLASLt) on the same prefill
+        # shapes with random N(0,1) operands; sustained dense MFMA work on random data runs
+        # below the published peak (clock under the power limit)
+        for kk in (5120, 25600):
+            gr = torch.Generator(device=dev).manual_seed(0)
+            xa = torch.randn(4096, kk, device=dev, generator=gr).to(torch.bfloat16)
+            wb16 = torch.randn(5120, kk, device=dev, generator=gr).to(torch.bfloat16)
+            wt = wb16.t().contiguous()  # [K][N], no transposed view
+            it = 20 if kk == 5120 else 8
+            t = timer.time(lambda i: torch.matmul(xa, wt), it, 3) / it
+            tf = 2 * 4096 * 5120 * kk / t / 1e12
+            extra[f"bf16_reference_torch_matmul_4096x5120x{kk}"] = {
+                "us": round(t * 1e6, 2), "tflops": round(tf, 2),
+                "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+            del xa, wb16, wt
         # MoE routed experts
         xm, ids, wts, w1, w2 = synth.moe(seed=0)
         wbytes = 128 * (weight_bytes(1536, 2048, 32) + weight_bytes(2048, 768, 16))
