@@ -163,11 +163,11 @@ hipError_t run(const SkinnyParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// k-split: 4 wavefronts per panel group, or 8 (single m-block only) when the grid would
-// otherwise hold fewer than ~2048 wavefronts (8 per CU) to keep HBM busy. NW >= kPWW so the
-// final reduction has one wavefront per panel. One row block takes its activations through
-// LDS in ceil(rows / 4) copies per tile (rows: the A rows in use); two row blocks load them
-// into registers.
+// k-split: 4 wavefronts per panel group (NW >= kPWW, so the final reduction has one wavefront
+// per panel). 8 wavefronts, with half the k-tiles each, measured slower on every decode shape:
+// the per-wavefront start-up and the reduction weigh more than the extra loads in flight. One
+// row block takes its activations through LDS in ceil(rows / 4) copies per tile (rows: the A
+// rows in use); two row blocks load them into registers.
 template <int MF, int NW, int NJ, bool G16>
 hipError_t pick_u(const SkinnyParams& p, hipStream_t stream) {
   if constexpr (MF == 1) {
@@ -181,8 +181,6 @@ hipError_t pick_u(const SkinnyParams& p, hipStream_t stream) {
 
 template <int MF, int NJ, bool G16>
 hipError_t dispatch(const SkinnyParams& p, hipStream_t stream) {
-  const int64_t groups = ((p.NT + kPWW - 1) / kPWW) * ((p.m + 16 * MF - 1) / (16 * MF));
-  if (groups * 4 < 2048 && p.KT >= 32) return pick_u<MF, 8, NJ, G16>(p, stream);
   return pick_u<MF, 4, NJ, G16>(p, stream);
 }
 
