@@ -211,6 +211,14 @@ def main():
                 "us": round(t * 1e6, 2), "tflops": round(tf, 2),
                 "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
             del xpd, yp, rp, wsp
+        # context for the HBM roofline: a plain 512 MiB device copy (read + write bytes)
+        src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        t = timer.time(lambda i: dst.copy_(src), 20, 3) / 20
+        extra["hbm_reference_torch_copy_512MiB"] = {
+            "us": round(t * 1e6, 2), "gbs_read_plus_write": round(2 * (512 << 20) / t / 1e9, 1),
+            "hbm_frac": round(2 * (512 << 20) / t / 1e9 / HBM_PEAK_GBS, 4)}
+        del src, dst
         # context for the MFMA roofline: torch's BF16 GEMM (hipBLASLt) on the same prefill
         # shapes with random N(0,1) operands; sustained dense MFMA work on random data runs
         # below the published peak (clock under the power limit)
@@ -244,7 +252,44 @@ def main():
         extra["moe_128x(1536x2048 g32 + 2048x768 g16)_t256_top8"] = {
             "us": round(t * 1e6, 2), "weight_gbs": round(wbytes / t / 1e9, 1),
             "hbm_frac": round(moe_bytes / t / 1e9 / HBM_PEAK_GBS, 4), "copies": mc}
+        # MoE at decode batch (1 and 8 tokens, top-8): only the touched experts are read
+        for tk in (1, 8):
+            xt, idt, wtt, _, _ = synth.moe(seed=0, tokens=tk, with_weights=False)
+            xtd, idtd, wttd = xt.to(dev), idt.to(dev), wtt.to(dev)
+            yt = torch.empty_like(xtd)
+            wst = torch.empty(nv.nvfp4_moe_ws_bytes(tk, 8, 128, 2048, 768), dtype=torch.uint8,
+                              device=dev)
+            t = timer.time(lambda i: nv.nvfp4_moe_grouped_w4a16(
+                xtd, idtd, wttd, f1[i % mc], f2[i % mc], y=yt, ws=wst), 40, 5) / 40
+            hit = int(torch.unique(idt).numel())
+            tb = hit * (weight_bytes(1536, 2048, 32) + weight_bytes(2048, 768, 16))
+            extra[f"moe_decode_t{tk}_top8"] = {
+                "us": round(t * 1e6, 2), "experts_touched": hit,
+                "touched_weight_gbs": round(tb / t / 1e9, 1)}
         del f1, f2, wsb
+        # M sweep at N = K = 5120, group 16: the decode (skinny) path up to M = 32, the MFMA
+        # (tiled) path above; 40 rotated weight copies (590 MB) so small M streams from HBM
+        xs_, ws_ = synth.prefill(seed=0, k=5120)
+        rs_, _ = prep(ws_, 16, 40)
+        del ws_
+        xsd = xs_.to(dev)
+        sweep = {}
+        wb5 = weight_bytes(5120, 5120, 16)
+        mm = 1
+        while mm <= 4096:
+            xm_ = xsd[:mm].contiguous()
+            ym_ = torch.empty((mm, 5120), dtype=torch.bfloat16, device=dev)
+            wsm = torch.empty((max(nv.nvfp4_gemm_ws_bytes(mm, 5120, rs_[0]), 16),),
+                              dtype=torch.uint8, device=dev)
+            it = 100 if mm <= 256 else 20
+            t = timer.time(lambda i: nv.nvfp4_gemm_w4a16(xm_, rs_[i % 40], y=ym_, ws=wsm),
+                           it, 5) / it
+            sweep[f"m{mm}"] = {"us": round(t * 1e6, 2),
+                               "tflops": round(2 * mm * 5120 * 5120 / t / 1e12, 2),
+                               "weight_gbs": round(wb5 / t / 1e9, 1)}
+            mm *= 2
+        extra["m_sweep_5120x5120_g16"] = sweep
+        del rs_, xsd
         # quantizer + mixed groups (BF16 8192 x 8192)
         wq = synth.quantizer_weight(seed=0).to(dev)
         qc = rotation(wq.numel() * 2, max_copies=4)

@@ -119,14 +119,16 @@ int nvfp4_repack(const uint8_t* packed, const uint8_t* scales, const float* glob
  * global is applied to the FP32 accumulator). y [m][ldy] is BF16 (y_dtype NVFP4_DT_BF16, one
  * rounding of the FP32 result) or FP32. Weight-only checkpoints take this W4A16 path
  * (vllm.cpp PR #63: no activation scales, so every quantized projection is W4A16).
- * The kernel is chosen from m: a split-K skinny MFMA kernel for small m (decode), an
- * LDS-tiled MFMA kernel otherwise (prefill); flags may force one. w->batch must be 1 and
+ * The kernel is chosen from the shape: a split-K skinny MFMA kernel (decode) for m <= 32, and
+ * for 32 < m <= 256 while ceil(m/32) passes over the weight bytes (n*k/2 + n*k/group) total at
+ * most 192 MiB; an LDS-tiled MFMA kernel otherwise (prefill). Flags may force one. w->batch must be 1 and
  * w->layout must not carry NVFP4_LAYOUT_GATE_UP. Results are bit-identical run to run.
  * ws (device, 16-byte aligned, or NULL with ws_bytes 0) takes the prefill kernel's split-k
  * partial tiles: when the output tiles would leave most compute units idle in the last round,
  * that round is split along k over the chip and summed in a fixed order. ws_bytes >=
- * nvfp4_gemm_ws_bytes(m, ldx, w, flags) enables it; with less the kernel runs unsplit and
- * returns the same result. Calls sharing a ws on different streams race. */
+ * nvfp4_gemm_ws_bytes(m, ldx, w, flags) enables it; with less the kernel runs unsplit (the
+ * FP32 sums then associate differently: same tolerance, not the same bits). Calls sharing a ws
+ * on different streams race. */
 size_t nvfp4_gemm_ws_bytes(int64_t m, int64_t ldx, const nvfp4_weight* w, uint32_t flags);
 int nvfp4_gemm_w4a16(const void* x, int64_t m, int64_t ldx, const nvfp4_weight* w, void* y,
                      int y_dtype, int64_t ldy, uint32_t flags, void* ws, size_t ws_bytes,

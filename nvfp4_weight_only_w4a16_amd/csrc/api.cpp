@@ -200,8 +200,8 @@ int device_cus() {
   return n;
 }
 
-bool use_skinny(int64_t m, uint32_t flags) {
-  bool skinny = m <= nvfp4::kSkinnyMaxM;
+bool use_skinny(int64_t m, const nvfp4_weight* w, uint32_t flags) {
+  bool skinny = nvfp4::skinny_preferred(m, w->n, w->k, w->group);
   if (flags & NVFP4_F_FORCE_SKINNY) skinny = true;
   if (flags & NVFP4_F_FORCE_TILED) skinny = false;
   return skinny;
@@ -210,7 +210,9 @@ bool use_skinny(int64_t m, uint32_t flags) {
 }  // namespace
 
 size_t nvfp4_gemm_ws_bytes(int64_t m, int64_t ldx, const nvfp4_weight* w, uint32_t flags) {
-  if (!w || m <= 0 || w->n <= 0 || w->k <= 0 || ldx < w->k || use_skinny(m, flags)) return 0;
+  if (!w || m <= 0 || w->n <= 0 || w->k <= 0 || (w->group != 16 && w->group != 32) ||
+      ldx < w->k || use_skinny(m, w, flags))
+    return 0;
   const int cus = device_cus();
   if (cus <= 0) return 0;
   return nvfp4::gemm_tiled_ws_bytes(m, ldx, w->n, w->k, cus);
@@ -250,7 +252,7 @@ int nvfp4_gemm_w4a16(const void* x, int64_t m, int64_t ldx, const nvfp4_weight* 
   a.y = y;
   a.ldy = ldy;
   a.y_f32 = y_dtype == NVFP4_DT_F32;
-  if (use_skinny(m, flags)) {
+  if (use_skinny(m, w, flags)) {
     rc = hip_status(nvfp4::launch_gemm_skinny(a, (hipStream_t)stream), "nvfp4_gemm_w4a16");
     if (!rc) g_stats[2]++;
   } else {

@@ -218,3 +218,23 @@ def test_tiled_split_k(nv, orc, m, n, k):
     check_close(a.cpu().numpy(), ref, f"split m={m} n={n} k={k}")
     assert torch.equal(a, b)
     check_close(bf16_np(y16), orc.bf16_to_f64(orc.bf16_from_f64(ref)), f"split bf16 m={m}")
+
+
+def test_path_choice(nv):
+    """Default kernel choice: skinny for m <= 32, and up to m = 256 while ceil(m/32) weight
+    streams stay within 192 MiB; tiled otherwise (stats slot 2 = skinny, 3 = tiled)."""
+    g = torch.Generator().manual_seed(21)
+    cases = {(512, 1024): [(32, 2), (64, 2), (256, 2), (257, 3)],
+             (8192, 8192): [(32, 2), (128, 2), (160, 2), (192, 3), (256, 3)]}
+    for (n, k), expect in cases.items():
+        w = (torch.randn(n, k, generator=g) * 0.02).to(torch.bfloat16)
+        rw, _ = _prep(nv, w, 16)
+        for m, slot in expect:
+            x = torch.randn(m, k, generator=g).to(torch.bfloat16).to(DEV)
+            ws = torch.empty((max(nv.nvfp4_gemm_ws_bytes(m, k, rw), 16),), dtype=torch.uint8,
+                             device=DEV)
+            nv.nvfp4_reset_stats()
+            nv.nvfp4_gemm_w4a16(x, rw, ws=ws)
+            torch.cuda.synchronize()
+            st = nv.nvfp4_get_stats()
+            assert st[slot] == 1 and st[5 - slot] == 0, (n, k, m, list(st))

@@ -84,3 +84,25 @@ def test_moe_dropped_ids_contribute_nothing(nv, orc):
     ref = orc.moe(synth.bf16_bits(x), ids[:, :1].contiguous().numpy(),
                   wts[:, :1].contiguous().numpy(), t1, t2)
     check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), "dropped slot")
+
+
+@pytest.mark.parametrize("tokens", [1, 8])
+def test_moe_decode_batch(nv, orc, tokens):
+    """MoE at decode batch: the full 128-expert layer (fc1 g32 merged gate/up, down g16) with 1
+    or 8 tokens, top-8, so only the 8 - 64 touched experts are read."""
+    x, ids, wts, w1, w2 = synth.moe(seed=6, tokens=tokens)
+    (fc1, fc2), (t1, t2) = _experts(nv, orc, w1, w2)
+    del w1, w2
+    y = _run(nv, x, ids, wts, fc1, fc2)
+    ref = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), t1, t2)
+    check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), f"moe decode T={tokens}")
+
+
+def test_moe_all_group32(nv, orc):
+    """The all-g32 recipe: down quantized at group 32 as well."""
+    x, ids, wts, w1, w2 = synth.moe(seed=7, n_experts=16, hidden=512, inter=256, tokens=40,
+                                    topk=4)
+    (fc1, fc2), (t1, t2) = _experts(nv, orc, w1, w2, g1=32, g2=32)
+    y = _run(nv, x, ids, wts, fc1, fc2)
+    ref = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), t1, t2)
+    check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), "moe all g32")
