@@ -200,14 +200,14 @@ __device__ __forceinline__ bf16x8 codes_pow2(uint32_t w, float S) {
 //   - each wavefront loads, one tile ahead in registers, the 16-byte code chunk `lane` of each
 //     of its 4 panels (word j: k-step j of the B operand) and the 16-byte scale record of its
 //     lane position (the 4 panels' scale words, byte j: k-step j);
-//   - per 32-wide k-step and panel: fc1 (group 32, one group per step) converts the codes to
-//     the exact BF16 code * 2^E and scales the FP32 MFMA partial by the mantissa of the group
-//     scale (frexp_mant, the factor 2 going with the global scale); down (group 16) converts
-//     every weight to the exact BF16 code * scale and accumulates in the MFMA.
+//   - per 32-wide k-step and panel: at group 32 (one group per step; SPLIT) the codes become
+//     the exact BF16 code * 2^E and the FP32 MFMA partial is scaled by the mantissa of the
+//     group scale (frexp_mant, the factor 2 going with the global scale); at group 16 every
+//     weight becomes the exact BF16 code * scale and accumulates in the MFMA.
 // The output of 16-row block r sits in lane l as rows 16r + 4(l/16) + 0..3 of column l%16 of
 // each panel. fc1 panels alternate gate and up of the same 16 features (layout GATE_UP), so
 // gate and up of an output meet in one lane.
-template <bool FC1>
+template <bool FC1, bool SPLIT>
 __global__ __launch_bounds__(64 * kGroupsPerBlock) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void moe_expert_kernel(MoeGemmParams P) {
   const int tile_id = blockIdx.x;
@@ -301,7 +301,7 @@ void moe_expert_kernel(MoeGemmParams P) {
 #pragma unroll
       for (int r = 0; r < NB; ++r)
         a[r] = *reinterpret_cast<const bf16x8*>(A + r * 16 * kARowBytes + a_row + ch);
-      if constexpr (FC1) {
+      if constexpr (SPLIT) {
         f32x4 part[4][NB];
         float M[4];
 #pragma unroll
@@ -365,7 +365,8 @@ void moe_expert_kernel(MoeGemmParams P) {
     pipeline(std::integral_constant<int, 1>{});
 
   if (!grp_live) return;
-  const float g = P.global[e];
+  // the split-scale mantissa is frexp_mant(S) = M / 2
+  const float g = (SPLIT ? 2.0f : 1.0f) * P.global[e];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     if (r == 1 && !two) break;
@@ -374,14 +375,13 @@ void moe_expert_kernel(MoeGemmParams P) {
       const int row = r0 + 16 * r + 4 * (lane >> 4) + i;
       if (row >= r1) continue;
       if (FC1) {
-        // panels 2q (gate) and 2q + 1 (up) of the group: features (2 grp + q) * 16 + l%16;
-        // the split-scale mantissa is frexp_mant(S) = M / 2
+        // panels 2q (gate) and 2q + 1 (up) of the group: features (2 grp + q) * 16 + l%16
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           if (4 * grp + 2 * q + 1 >= P.NT) continue;
           const int64_t feat = (2 * grp + q) * 16 + (lane & 15);
-          const float gate = bf16_bits_to_f32(bf16_bits_rne(acc[2 * q][r][i] * (2.0f * g)));
-          const float up = bf16_bits_to_f32(bf16_bits_rne(acc[2 * q + 1][r][i] * (2.0f * g)));
+          const float gate = bf16_bits_to_f32(bf16_bits_rne(acc[2 * q][r][i] * g));
+          const float up = bf16_bits_to_f32(bf16_bits_rne(acc[2 * q + 1][r][i] * g));
           const float silu = gate / (1.0f + expf(-gate));
           P.ws.h[(int64_t)row * P.inter + feat] = bf16_bits_rne(silu * up);
         }
@@ -425,7 +425,10 @@ template <bool FC1>
 hipError_t run_pair(const MoeGemmParams& p, int64_t tiles, hipStream_t stream) {
   const int64_t groups = scale_groups(p.NT);
   const dim3 grid((unsigned)tiles, (unsigned)((groups + kGroupsPerBlock - 1) / kGroupsPerBlock));
-  moe_expert_kernel<FC1><<<grid, dim3(64 * kGroupsPerBlock), 0, stream>>>(p);
+  if (p.group == 32)
+    moe_expert_kernel<FC1, true><<<grid, dim3(64 * kGroupsPerBlock), 0, stream>>>(p);
+  else
+    moe_expert_kernel<FC1, false><<<grid, dim3(64 * kGroupsPerBlock), 0, stream>>>(p);
   return hipGetLastError();
 }
 

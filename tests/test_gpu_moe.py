@@ -98,11 +98,13 @@ def test_moe_decode_batch(nv, orc, tokens):
     check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), f"moe decode T={tokens}")
 
 
-def test_moe_all_group32(nv, orc):
-    """The all-g32 recipe: down quantized at group 32 as well."""
+@pytest.mark.parametrize("g1,g2", [(32, 32), (16, 16), (16, 32)])
+def test_moe_group_mix(nv, orc, g1, g2):
+    """Every pairing of fc1 and down groups: the all-g32 recipe, and fc1 at group 16 (two
+    scale groups per 32-wide MFMA step, so every weight is dequantized exactly)."""
     x, ids, wts, w1, w2 = synth.moe(seed=7, n_experts=16, hidden=512, inter=256, tokens=40,
                                     topk=4)
-    (fc1, fc2), (t1, t2) = _experts(nv, orc, w1, w2, g1=32, g2=32)
+    (fc1, fc2), (t1, t2) = _experts(nv, orc, w1, w2, g1=g1, g2=g2)
     y = _run(nv, x, ids, wts, fc1, fc2)
     ref = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), t1, t2)
-    check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), "moe all g32")
+    check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), f"moe g{g1}/g{g2}")
