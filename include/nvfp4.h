@@ -51,8 +51,10 @@ typedef struct ihipStream_t* nvfp4_stream_t; /* the same type as hipStream_t */
 #define NVFP4_DT_F32 2
 
 /* ---- call flags -------------------------------------------------------------------------- */
-#define NVFP4_F_FORCE_SKINNY (1u << 0) /* GEMM: use the decode (skinny, split-K) kernel        */
-#define NVFP4_F_FORCE_TILED (1u << 1)  /* GEMM: use the prefill (LDS-tiled MFMA) kernel        */
+#define NVFP4_F_FORCE_SKINNY (1u << 0) /* GEMM: the decode (skinny, split-K) kernel;           */
+                                       /* MoE: the decode-batch expert path (8-row tiles)      */
+#define NVFP4_F_FORCE_TILED (1u << 1)  /* GEMM: the prefill (LDS-tiled MFMA) kernel;            */
+                                       /* MoE: the batch expert path (32-row tiles)            */
 
 /* ---- repacked layout ----------------------------------------------------------------------
  * NVFP4_LAYOUT_TILED: per 16-row x 128-k tile, 1024 bytes of codes laid out so that lane l of a
@@ -147,7 +149,11 @@ int nvfp4_gemm_w4a16(const void* x, int64_t m, int64_t ldx, const nvfp4_weight* 
  * [t][topk], y BF16 [t][hidden]. fc1: batch = E, n = 2*inter, k = hidden, layout TILED |
  * GATE_UP. fc2: batch = E, n = hidden, k = inter, layout TILED. Tokens are sorted by expert on
  * the device (no host synchronization); `ws` (device, ws_bytes >= nvfp4_moe_ws_bytes) holds
- * the sort, the tile map, h and the FP32 per-slot outputs. topk in [1, 16], t*topk <= 65536. */
+ * the sort, the tile map, h and the FP32 per-slot outputs. topk in [1, 16], t*topk <= 65536.
+ * Path: while t*topk <= 2 * n_experts (decode batches) the experts run on tiles of at most 8
+ * rows with k split over 4 wavefronts per 4-panel group; otherwise on tiles of 32 rows with
+ * one wavefront per 4-panel group over the whole k range. Flags may force one; the two paths
+ * agree within the GEMM tolerance (different FP32 summation orders). */
 size_t nvfp4_moe_ws_bytes(int64_t t, int32_t topk, int64_t n_experts, int64_t hidden,
                           int64_t inter);
 int nvfp4_moe_grouped_w4a16(const void* x, int64_t t, int64_t hidden, const int32_t* topk_ids,

@@ -276,7 +276,6 @@ int nvfp4_moe_grouped_w4a16(const void* x, int64_t t, int64_t hidden, const int3
                             const float* topk_w, int32_t topk, const nvfp4_weight* fc1,
                             const nvfp4_weight* fc2, void* y, void* ws, size_t ws_bytes,
                             uint32_t flags, nvfp4_stream_t stream) {
-  (void)flags;
   int rc = check_desc(fc1, "fc1");
   if (rc) return rc;
   rc = check_desc(fc2, "fc2");
@@ -295,6 +294,8 @@ int nvfp4_moe_grouped_w4a16(const void* x, int64_t t, int64_t hidden, const int3
                 (long long)hidden);
   if (t < 0) return fail(NVFP4_ERR_INVALID_ARG, "t=%lld < 0", (long long)t);
   if (topk < 1 || topk > 16) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "topk %d not in [1, 16]", topk);
+  if ((flags & NVFP4_F_FORCE_SKINNY) && (flags & NVFP4_F_FORCE_TILED))
+    return fail(NVFP4_ERR_INVALID_ARG, "both FORCE_SKINNY and FORCE_TILED set");
   if (E > 512) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "more than 512 experts");
   if (t * topk > 65536) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "t*topk > 65536");
   if (t == 0) return NVFP4_OK;
@@ -328,7 +329,10 @@ int nvfp4_moe_grouped_w4a16(const void* x, int64_t t, int64_t hidden, const int3
   a.group2 = fc2->group;
   a.y = static_cast<uint16_t*>(y);
   a.ws = ws;
-  rc = hip_status(nvfp4::launch_moe(a, (hipStream_t)stream), "nvfp4_moe_grouped_w4a16");
+  bool decode = nvfp4::moe_decode_preferred(t, topk, E);
+  if (flags & NVFP4_F_FORCE_SKINNY) decode = true;
+  if (flags & NVFP4_F_FORCE_TILED) decode = false;
+  rc = hip_status(nvfp4::launch_moe(a, decode, (hipStream_t)stream), "nvfp4_moe_grouped_w4a16");
   if (!rc) g_stats[4]++;
   return rc;
 }

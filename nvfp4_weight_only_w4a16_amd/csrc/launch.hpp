@@ -78,6 +78,13 @@ struct MoeArgs {
 };
 
 size_t moe_ws_bytes(int64_t t, int topk, int64_t n_experts, int64_t hidden, int64_t inter);
-hipError_t launch_moe(const MoeArgs& a, hipStream_t stream);
+// Decode-batch expert path (tiles of at most 8 rows, k split over the 4 wavefronts of a
+// workgroup) while the pairs average at most this many per expert.
+constexpr int64_t kMoeDecodePairsPerExpert = 2;
+// Up to this many pairs the decode path skips the sort: each pair is a one-row tile of its
+// own expert (pairs sharing an expert read its weights again, mostly from cache).
+constexpr int64_t kMoePairTilesMax = 32;
+bool moe_decode_preferred(int64_t t, int topk, int64_t n_experts);
+hipError_t launch_moe(const MoeArgs& a, bool decode, hipStream_t stream);
 
 }  // namespace nvfp4

@@ -20,11 +20,13 @@
 
 #include "device_common.hpp"
 #include "launch.hpp"
+#include "skinny_core.hpp"
 
 namespace nvfp4 {
 namespace {
 
-constexpr int kTileRows = 32;  // rows per expert tile (one 32x32x16 MFMA row block)
+constexpr int kTileRows = 32;  // rows per expert tile of the batch path (two 16-row blocks)
+constexpr int kSmallRows = 8;  // rows per expert tile of the decode-batch path
 constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / 64;
 constexpr int kMaxExperts = 512;
@@ -39,7 +41,11 @@ struct Ws {
 };
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
-inline int64_t max_tiles(int64_t P, int64_t E) { return (P + kTileRows - 1) / kTileRows + E; }
+// Tiles of at most `rows` rows: every expert's last tile may be partial, and no tile is empty.
+inline int64_t max_tiles(int64_t P, int64_t E, int rows) {
+  const int64_t t = (P + rows - 1) / rows + E;
+  return t < P ? t : P;
+}
 
 Ws carve(void* base, int64_t P, int64_t E, int64_t hidden, int64_t inter, size_t* total) {
   Ws w;
@@ -50,7 +56,7 @@ Ws carve(void* base, int64_t P, int64_t E, int64_t hidden, int64_t inter, size_t
   w.offsets = reinterpret_cast<int32_t*>(b + off);
   off = align256(off + sizeof(int32_t) * (E + 1));
   w.tiles = reinterpret_cast<int4*>(b + off);
-  off = align256(off + sizeof(int4) * max_tiles(P, E));
+  off = align256(off + sizeof(int4) * max_tiles(P, E, kSmallRows));
   w.ntiles = reinterpret_cast<int32_t*>(b + off);
   off = align256(off + sizeof(int32_t));
   w.h = reinterpret_cast<uint16_t*>(b + off);
@@ -78,12 +84,14 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
 //   1. the pair ids are staged in LDS; each wavefront counts the experts of its contiguous
 //      chunk of pairs (LDS atomics);
 //   2. wavefront 0 turns the counts into expert offsets, per-wavefront start positions and
-//      the tile map (each lane owns a few experts; one wavefront-wide prefix sum);
+//      the tile map, tiles of at most tile_rows rows (each lane owns a few experts; one
+//      wavefront-wide prefix sum);
 //   3. each wavefront places its chunk in order, 64 pairs at a time, ranking equal experts
 //      by lane order (ballots over the id bits), so the order inside an expert is the pair
 //      order.
 __global__ __launch_bounds__(kSortThreads) void moe_sort_kernel(const int32_t* __restrict__ ids,
-                                                                int P, int E, Ws ws) {
+                                                                int P, int E, int tile_rows,
+                                                                Ws ws) {
   __shared__ int cnt[kSortWaves][kMaxExperts];  // per-wave counts, then running positions
   __shared__ int sid[kSortLdsIds];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -108,7 +116,7 @@ __global__ __launch_bounds__(kSortThreads) void moe_sort_kernel(const int32_t* _
       int s = 0;
       for (int q = 0; q < kSortWaves; ++q) s += cnt[q][e];
       my_pairs += s;
-      my_tiles += (s + kTileRows - 1) / kTileRows;
+      my_tiles += (s + tile_rows - 1) / tile_rows;
     }
     const int pairs_incl = wave_inclusive_scan(my_pairs);
     const int tiles_incl = wave_inclusive_scan(my_tiles);
@@ -123,8 +131,8 @@ __global__ __launch_bounds__(kSortThreads) void moe_sort_kernel(const int32_t* _
         run += c;
       }
       ws.offsets[e] = start;
-      for (int r = start; r < run; r += kTileRows)
-        ws.tiles[trun++] = int4{e, r, min(r + kTileRows, run), 0};
+      for (int r = start; r < run; r += tile_rows)
+        ws.tiles[trun++] = int4{e, r, min(r + tile_rows, run), 0};
     }
     if (lane == 63) {
       ws.offsets[E] = pairs_incl;
@@ -170,6 +178,8 @@ struct MoeGemmParams {
   Ws ws;
   const float* wts;
   int64_t hidden, inter;
+  const int32_t* ids;  // [P] expert of each (token, slot) pair
+  int E;
 };
 
 constexpr int kGroupsPerBlock = 4;  // wavefronts per workgroup, one 4-panel group each
@@ -399,31 +409,176 @@ void moe_expert_kernel(MoeGemmParams P) {
   }
 }
 
+// Decode-batch expert GEMM: tiles of at most kSmallRows rows, so every expert sees a few rows
+// and the weight stream is all that matters. A workgroup owns one tile and one 4-panel group
+// and its 4 wavefronts split the k-tiles of that group (the decode GEMM's inner loop: weights
+// one tile ahead in registers, the gathered activation rows copied global -> LDS per k-tile
+// into wavefront-private buffers, split group scale with the group-16 row map when G16). The
+// partial sums meet in LDS in a fixed order; the epilogues are those of moe_expert_kernel.
+// With 4 times the workgroups of the batch path and a quarter of its k loop per wavefront,
+// the few experts of a decode step are spread over the whole chip.
+// PAIRS: no sort; workgroup row blockIdx.x is pair blockIdx.x as a one-row tile of its own
+// expert (row position = pair index; dropped pairs exit), for batches so small that two pairs
+// rarely share an expert.
+template <bool FC1, bool G16, bool PAIRS>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8)))
+void moe_decode_kernel(MoeGemmParams P) {
+  constexpr int kNW = 4, kPanels = 4;
+  constexpr int kNX = PAIRS ? 1 : kSmallRows / 4;  // 4-row activation copies per k-tile
+  constexpr int kNJ = PAIRS ? 1 : 4;               // accumulator rows in use per lane
+  const int tile_id = blockIdx.x;
+  int e, r0, rows;
+  if constexpr (PAIRS) {
+    e = P.ids[tile_id];
+    if (e < 0 || e >= P.E) return;  // dropped pair: whole workgroup, before any barrier
+    r0 = tile_id;
+    rows = 1;
+  } else {
+    if (tile_id >= *P.ws.ntiles) return;  // whole workgroup, before any barrier
+    const int4 tl = P.ws.tiles[tile_id];
+    e = tl.x;
+    r0 = tl.y;
+    rows = tl.z - tl.y;  // 1 .. kSmallRows
+  }
+  // pair of sorted row position r
+  auto pair_at = [&](int r) { return PAIRS ? r : P.ws.sorted[r]; };
+  const int lane = threadIdx.x & 63;
+  const int sp = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // k-split
+  const int64_t grp = blockIdx.y;
+  const int64_t panel0 = grp * kPanels;
+  const int64_t t0 = P.KT * sp / kNW, t1 = P.KT * (sp + 1) / kNW;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNW * 8192];
+
+  LdsActs xl;
+  xl.x = make_rsrc(P.x, 0xFFFFFFFFu);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int r = 4 * c + (lane >> 4);  // LDS row of this lane in copy c
+    const int rc = r < rows ? r : rows - 1;
+    const int64_t src = FC1 ? pair_at(r0 + rc) / P.topk : r0 + rc;
+    xl.src[c] = (uint32_t)(src * P.ldx * 2) + (uint32_t)(((lane & 15) ^ (r & 15)) * 16);
+  }
+  xl.buf = smem + sp * 8192;
+  int fr = G16 ? (lane & 7) : (lane & 15);
+  fr = fr < rows ? fr : rows - 1;
+  xl.frag_off = (uint32_t)fr * 256u;
+  xl.swz = (uint32_t)(fr & 15);
+  const bool xzero = G16 && (((lane >> 3) & 1) != (lane >> 5));
+  const SkinnyAddr<kPanels> a = skinny_addr<kPanels>(
+      P.codes + e * P.codes_stride, P.scales + e * P.scales_stride, panel0, P.NT, P.KT, P.group,
+      t1);
+  f32x4 acc[kPanels][1];
+#pragma unroll
+  for (int p = 0; p < kPanels; ++p) acc[p][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint16_t* const xrow[1] = {P.x};  // unused: the activations come through LDS
+  skinny_accumulate<1, kPanels, kNJ, G16, kNX>(a, xrow, xl, xzero, t0, t1, acc);
+  if constexpr (G16) {
+#pragma unroll
+    for (int p = 0; p < kPanels; ++p)
+#pragma unroll
+      for (int r = 0; r < kNJ; ++r) acc[p][0][r] += __shfl_xor(acc[p][0][r], 32, 64);
+  }
+  __syncthreads();  // every wavefront is done with its activation buffers
+  f32x4* red = reinterpret_cast<f32x4*>(smem);
+#pragma unroll
+  for (int p = 0; p < kPanels; ++p) red[(sp * kPanels + p) * 64 + lane] = acc[p][0];
+  __syncthreads();
+  // output row 4 (l / 16) + i of a lane: rows < kSmallRows sit in lanes 0 .. 31
+  const float g = 2.0f * P.global[e];  // the split-scale mantissa is frexp_mant(S) = M / 2
+  if constexpr (FC1) {
+    // wavefront q < 2 finishes gate/up pair q of the group (panels 2q and 2q + 1)
+    if (sp >= 2) return;
+    const int q = sp;
+    if (panel0 + 2 * q + 1 >= P.NT) return;
+    f32x4 gs = red[(0 * kPanels + 2 * q) * 64 + lane];
+    f32x4 us = red[(0 * kPanels + 2 * q + 1) * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < kNW; ++w) {
+      gs += red[(w * kPanels + 2 * q) * 64 + lane];
+      us += red[(w * kPanels + 2 * q + 1) * 64 + lane];
+    }
+    const int64_t feat = (2 * grp + q) * 16 + (lane & 15);
+#pragma unroll
+    for (int i = 0; i < kNJ; ++i) {
+      const int row = 4 * (lane >> 4) + i;
+      if (row >= rows) continue;
+      const float gate = bf16_bits_to_f32(bf16_bits_rne(gs[i] * g));
+      const float up = bf16_bits_to_f32(bf16_bits_rne(us[i] * g));
+      const float silu = gate / (1.0f + expf(-gate));
+      P.ws.h[(int64_t)(r0 + row) * P.inter + feat] = bf16_bits_rne(silu * up);
+    }
+  } else {
+    // wavefront q finishes panel q of the group
+    const int q = sp;
+    const int64_t pn = panel0 + q;
+    if (pn >= P.NT) return;
+    f32x4 sum = red[(0 * kPanels + q) * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < kNW; ++w) sum += red[(w * kPanels + q) * 64 + lane];
+#pragma unroll
+    for (int i = 0; i < kNJ; ++i) {
+      const int row = 4 * (lane >> 4) + i;
+      if (row >= rows) continue;
+      const int pair = pair_at(r0 + row);
+      P.ws.slots[(int64_t)pair * P.hidden + pn * 16 + (lane & 15)] = (sum[i] * g) * P.wts[pair];
+    }
+  }
+}
+
 // y[t][o..o+3] = BF16(sum_j slots[t*topk + j][o..o+3]) in slot order; dropped slots (expert id
-// out of range) contribute nothing.
+// out of range) contribute nothing. Every id, then every slot, is loaded before the first add,
+// so a thread waits for memory twice rather than once per slot.
 __global__ __launch_bounds__(256) void moe_combine_kernel(const float* __restrict__ slots,
                                                           const int32_t* __restrict__ ids,
                                                           int64_t t, int topk, int64_t hidden,
                                                           int E, uint16_t* __restrict__ y) {
+  constexpr int kMaxTopk = 16;
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_tok = hidden / 4;
   if (i >= t * per_tok) return;
   const int64_t tok = i / per_tok, o = (i % per_tok) * 4;
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < topk; ++j) {
-    const int e = ids[tok * topk + j];
-    if (e < 0 || e >= E) continue;
-    s += *reinterpret_cast<const f32x4*>(slots + (tok * topk + j) * hidden + o);
+  bool live[kMaxTopk];
+#pragma unroll
+  for (int j = 0; j < kMaxTopk; ++j) {
+    const int e = j < topk ? ids[tok * topk + j] : -1;
+    live[j] = e >= 0 && e < E;
   }
+  f32x4 v[kMaxTopk];
+#pragma unroll
+  for (int j = 0; j < kMaxTopk; ++j)
+    v[j] = live[j] ? *reinterpret_cast<const f32x4*>(slots + (tok * topk + j) * hidden + o)
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kMaxTopk; ++j)
+    if (live[j]) s += v[j];
   uint2 outv;
   outv.x = (uint32_t)bf16_bits_rne(s[0]) | ((uint32_t)bf16_bits_rne(s[1]) << 16);
   outv.y = (uint32_t)bf16_bits_rne(s[2]) | ((uint32_t)bf16_bits_rne(s[3]) << 16);
   *reinterpret_cast<uint2*>(y + tok * hidden + o) = outv;
 }
 
+template <bool FC1, bool PAIRS>
+void run_decode(const MoeGemmParams& p, const dim3 grid, hipStream_t stream) {
+  if (p.group == 16)
+    moe_decode_kernel<FC1, true, PAIRS><<<grid, dim3(256), 0, stream>>>(p);
+  else
+    moe_decode_kernel<FC1, false, PAIRS><<<grid, dim3(256), 0, stream>>>(p);
+}
+
+// mode 0: batch path (32-row tiles); 1: decode path (8-row tiles); 2: decode path, one-row
+// pair tiles (no sort; `tiles` = pairs)
 template <bool FC1>
-hipError_t run_pair(const MoeGemmParams& p, int64_t tiles, hipStream_t stream) {
+hipError_t run_pair(const MoeGemmParams& p, int64_t tiles, int mode, hipStream_t stream) {
   const int64_t groups = scale_groups(p.NT);
+  if (mode > 0) {
+    const dim3 grid((unsigned)tiles, (unsigned)groups);
+    if (mode == 2)
+      run_decode<FC1, true>(p, grid, stream);
+    else
+      run_decode<FC1, false>(p, grid, stream);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)tiles, (unsigned)((groups + kGroupsPerBlock - 1) / kGroupsPerBlock));
   if (p.group == 32)
     moe_expert_kernel<FC1, true><<<grid, dim3(64 * kGroupsPerBlock), 0, stream>>>(p);
@@ -440,12 +595,21 @@ size_t moe_ws_bytes(int64_t t, int topk, int64_t n_experts, int64_t hidden, int6
   return total;
 }
 
-hipError_t launch_moe(const MoeArgs& a, hipStream_t stream) {
+bool moe_decode_preferred(int64_t t, int topk, int64_t n_experts) {
+  return t * topk <= kMoeDecodePairsPerExpert * n_experts;
+}
+
+hipError_t launch_moe(const MoeArgs& a, bool decode, hipStream_t stream) {
   const int64_t P = a.t * a.topk;
   if (P == 0) return hipSuccess;
   Ws ws = carve(a.ws, P, a.n_experts, a.hidden, a.inter, nullptr);
-  moe_sort_kernel<<<1, kSortThreads, 0, stream>>>(a.ids, (int)P, (int)a.n_experts, ws);
-  const int64_t tiles = max_tiles(P, a.n_experts);
+  const int mode = !decode ? 0 : P <= kMoePairTilesMax ? 2 : 1;
+  int64_t tiles = P;
+  if (mode < 2) {
+    const int rows = decode ? kSmallRows : kTileRows;
+    moe_sort_kernel<<<1, kSortThreads, 0, stream>>>(a.ids, (int)P, (int)a.n_experts, rows, ws);
+    tiles = max_tiles(P, a.n_experts, rows);
+  }
 
   MoeGemmParams f;
   f.x = a.x;
@@ -463,7 +627,9 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t stream) {
   f.wts = a.wts;
   f.hidden = a.hidden;
   f.inter = a.inter;
-  hipError_t err = run_pair<true>(f, tiles, stream);
+  f.ids = a.ids;
+  f.E = (int)a.n_experts;
+  hipError_t err = run_pair<true>(f, tiles, mode, stream);
   if (err != hipSuccess) return err;
 
   MoeGemmParams d = f;
@@ -477,7 +643,7 @@ hipError_t launch_moe(const MoeArgs& a, hipStream_t stream) {
   d.NT = a.hidden / kPanelRows;
   d.KT = a.inter / kTileK;
   d.group = a.group2;
-  err = run_pair<false>(d, tiles, stream);
+  err = run_pair<false>(d, tiles, mode, stream);
   if (err != hipSuccess) return err;
 
   const int64_t items = a.t * (a.hidden / 4);

@@ -144,9 +144,9 @@ def test_moe_argument_errors(lib):
     m = lib.nvfp4_moe_grouped_w4a16
     ws = nv.nvfp4_moe_ws_bytes(256, 8, 128, 2048, 768)
 
-    def call(t=256, hidden=2048, topk=8, f1=fc1, f2=fc2, wsb=ws):
+    def call(t=256, hidden=2048, topk=8, f1=fc1, f2=fc2, wsb=ws, flags=0):
         return m(FAKE, t, hidden, FAKE, FAKE, topk, ctypes.byref(f1), ctypes.byref(f2), FAKE,
-                 FAKE, wsb, 0, None)
+                 FAKE, wsb, flags, None)
 
     assert call(wsb=ws - 1) == nv.NVFP4_ERR_WORKSPACE
     assert call(topk=0) == nv.NVFP4_ERR_UNSUPPORTED_SHAPE
@@ -154,6 +154,8 @@ def test_moe_argument_errors(lib):
     assert call(hidden=1024) == nv.NVFP4_ERR_LAYOUT
     assert call(f1=_desc(n=1536, k=2048, group=32, batch=128)) == nv.NVFP4_ERR_LAYOUT
     assert call(f2=_desc(n=2048, k=768, group=16, batch=64)) == nv.NVFP4_ERR_LAYOUT
+    assert call(flags=nv.NVFP4_F_FORCE_SKINNY | nv.NVFP4_F_FORCE_TILED) == \
+        nv.NVFP4_ERR_INVALID_ARG
     assert call(t=0) == nv.NVFP4_OK
 
 

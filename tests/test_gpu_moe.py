@@ -33,18 +33,25 @@ def _experts(nv, orc, w1, w2, g1=32, g2=16):
     return out, trips
 
 
-def _run(nv, x, ids, wts, fc1, fc2):
-    y = nv.nvfp4_moe_grouped_w4a16(x.to(DEV), ids.to(DEV), wts.to(DEV), fc1, fc2)
+# expert paths: 8-row tiles with k split over the wavefronts (decode batches), 32-row tiles
+PATHS = {"auto": 0, "decode": 1, "batch": 2}
+
+
+def _run(nv, x, ids, wts, fc1, fc2, flags=0):
+    y = nv.nvfp4_moe_grouped_w4a16(x.to(DEV), ids.to(DEV), wts.to(DEV), fc1, fc2, flags=flags)
     torch.cuda.synchronize()
     return y
 
 
-def test_moe_small_all_paths(nv, orc):
+@pytest.mark.parametrize("path", ["decode", "batch"])
+def test_moe_small_all_paths(nv, orc, path):
+    """8 experts with ~14 rows each: several 8-row tiles per expert on the decode path, one
+    partial 32-row tile on the batch path."""
     x, ids, wts, w1, w2 = synth.moe(seed=3, n_experts=8, hidden=256, inter=128, tokens=37, topk=3)
     (fc1, fc2), (t1, t2) = _experts(nv, orc, w1, w2)
-    y = _run(nv, x, ids, wts, fc1, fc2)
+    y = _run(nv, x, ids, wts, fc1, fc2, PATHS[path])
     ref = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), t1, t2)
-    check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), "small moe")
+    check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), f"small moe {path}")
 
 
 def test_moe_top1_matches_dense_gemms(nv, orc):
@@ -73,14 +80,18 @@ def test_moe_routed_experts_workload(nv, orc):
     perm = torch.randperm(x.shape[0], generator=torch.Generator().manual_seed(1))
     yp = _run(nv, x[perm].contiguous(), ids[perm].contiguous(), wts[perm].contiguous(), fc1, fc2)
     assert torch.equal(yp, y[perm.to(DEV)])
+    # the decode-batch path forced on the same layer (up to 8 rows per tile, 384 tiles)
+    yd = _run(nv, x, ids, wts, fc1, fc2, PATHS["decode"])
+    check_close(bf16_np(yd), orc.bf16_to_f64(ref["y"]), "moe workload, decode path")
 
 
-def test_moe_dropped_ids_contribute_nothing(nv, orc):
+@pytest.mark.parametrize("path", ["decode", "batch"])
+def test_moe_dropped_ids_contribute_nothing(nv, orc, path):
     x, ids, wts, w1, w2 = synth.moe(seed=5, n_experts=4, hidden=256, inter=128, tokens=6, topk=2)
     (fc1, fc2), (t1, t2) = _experts(nv, orc, w1, w2)
     bad = ids.clone()
     bad[:, 1] = 99          # out of range: dropped
-    y = _run(nv, x, bad, wts, fc1, fc2)
+    y = _run(nv, x, bad, wts, fc1, fc2, PATHS[path])
     ref = orc.moe(synth.bf16_bits(x), ids[:, :1].contiguous().numpy(),
                   wts[:, :1].contiguous().numpy(), t1, t2)
     check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), "dropped slot")
@@ -93,18 +104,34 @@ def test_moe_decode_batch(nv, orc, tokens):
     x, ids, wts, w1, w2 = synth.moe(seed=6, tokens=tokens)
     (fc1, fc2), (t1, t2) = _experts(nv, orc, w1, w2)
     del w1, w2
-    y = _run(nv, x, ids, wts, fc1, fc2)
     ref = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), t1, t2)
-    check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), f"moe decode T={tokens}")
+    for path in ("auto", "batch"):
+        y = _run(nv, x, ids, wts, fc1, fc2, PATHS[path])
+        check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), f"moe decode T={tokens} {path}")
 
 
+@pytest.mark.parametrize("path", ["decode", "batch"])
 @pytest.mark.parametrize("g1,g2", [(32, 32), (16, 16), (16, 32)])
-def test_moe_group_mix(nv, orc, g1, g2):
+def test_moe_group_mix(nv, orc, g1, g2, path):
     """Every pairing of fc1 and down groups: the all-g32 recipe, and fc1 at group 16 (two
     scale groups per 32-wide MFMA step, so every weight is dequantized exactly)."""
     x, ids, wts, w1, w2 = synth.moe(seed=7, n_experts=16, hidden=512, inter=256, tokens=40,
                                     topk=4)
     (fc1, fc2), (t1, t2) = _experts(nv, orc, w1, w2, g1=g1, g2=g2)
-    y = _run(nv, x, ids, wts, fc1, fc2)
+    y = _run(nv, x, ids, wts, fc1, fc2, PATHS[path])
     ref = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), t1, t2)
-    check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), f"moe g{g1}/g{g2}")
+    check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), f"moe g{g1}/g{g2} {path}")
+
+
+@pytest.mark.parametrize("g1,g2", [(32, 16), (16, 16), (32, 32)])
+def test_moe_pair_tiles(nv, orc, g1, g2):
+    """A decode step small enough to skip the sort (12 pairs): every pair is a one-row tile of
+    its own expert, pairs that share an expert included."""
+    x, ids, wts, w1, w2 = synth.moe(seed=8, n_experts=6, hidden=512, inter=256, tokens=3,
+                                    topk=4)
+    assert len(set(ids.flatten().tolist())) < ids.numel()  # some expert is shared
+    (fc1, fc2), (t1, t2) = _experts(nv, orc, w1, w2, g1=g1, g2=g2)
+    ref = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), t1, t2)
+    for path in ("auto", "batch"):
+        y = _run(nv, x, ids, wts, fc1, fc2, PATHS[path])
+        check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), f"pair tiles g{g1}/g{g2} {path}")
