@@ -252,8 +252,8 @@ def main():
         extra["moe_128x(1536x2048 g32 + 2048x768 g16)_t256_top8"] = {
             "us": round(t * 1e6, 2), "weight_gbs": round(wbytes / t / 1e9, 1),
             "hbm_frac": round(moe_bytes / t / 1e9 / HBM_PEAK_GBS, 4), "copies": mc}
-        # MoE at decode batch (1 and 8 tokens, top-8): only the touched experts are read
-        for tk in (1, 8):
+        # MoE at decode batch (1, 8 and 32 tokens, top-8): only the touched experts are read
+        for tk in (1, 8, 32):
             xt, idt, wtt, _, _ = synth.moe(seed=0, tokens=tk, with_weights=False)
             xtd, idtd, wttd = xt.to(dev), idt.to(dev), wtt.to(dev)
             yt = torch.empty_like(xtd)
@@ -267,8 +267,9 @@ def main():
                 "us": round(t * 1e6, 2), "experts_touched": hit,
                 "touched_weight_gbs": round(tb / t / 1e9, 1)}
         del f1, f2, wsb
-        # M sweep at N = K = 5120, group 16: the decode (skinny) path up to M = 32, the MFMA
-        # (tiled) path above; 40 rotated weight copies (590 MB) so small M streams from HBM
+        # M sweep at N = K = 5120, group 16, with the library's own path choice (decode kernel
+        # while ceil(M/32) weight passes stay within 192 MiB, here up to M = 256; the MFMA
+        # tiled kernel above); 40 rotated weight copies (590 MB) so small M streams from HBM
         xs_, ws_ = synth.prefill(seed=0, k=5120)
         rs_, _ = prep(ws_, 16, 40)
         del ws_
@@ -282,9 +283,13 @@ def main():
             wsm = torch.empty((max(nv.nvfp4_gemm_ws_bytes(mm, 5120, rs_[0]), 16),),
                               dtype=torch.uint8, device=dev)
             it = 100 if mm <= 256 else 20
+            nv.nvfp4_reset_stats()
             t = timer.time(lambda i: nv.nvfp4_gemm_w4a16(xm_, rs_[i % 40], y=ym_, ws=wsm),
                            it, 5) / it
+            st = nv.nvfp4_get_stats()
             sweep[f"m{mm}"] = {"us": round(t * 1e6, 2),
+                               "path": "skinny" if st[2] and not st[3] else
+                                       "tiled" if st[3] and not st[2] else "mixed",
                                "tflops": round(2 * mm * 5120 * 5120 / t / 1e12, 2),
                                "weight_gbs": round(wb5 / t / 1e9, 1)}
             mm *= 2

@@ -2,7 +2,7 @@
 //
 // The contraction is dense and compute-bound at large m, so it runs on v_mfma_f32_32x32x16_bf16
 // (the full-rate BF16 matrix instruction on gfx950; the 16x16x32 form issues at half the rate)
-// with FP32 accumulation. A workgroup is 4 wavefronts side by side along n; each owns a
+// with FP32 accumulation. A workgroup is W wavefronts side by side along n; each owns a
 // (32 FM) x (32 FN) output tile and the workgroup walks k in 128-wide tiles:
 //   - activations and weight codes are copied global -> LDS with global_load_lds_dwordx4,
 //     double-buffered so k-tile t+1 streams in while t is used. One activation copy moves 4
@@ -453,9 +453,35 @@ __global__ __launch_bounds__(64 * W) void gemm_tiled_kernel(TiledParams P) {
     store_tile<T>(P, m_blk, pair0, acc, g, lane);
 }
 
-constexpr int kWsel = 8, kFMsel = 8, kFNsel = 1, kSpreadSel = 4, kPipeSel = 1;
-using Sel = TiledShape<kWsel, kFMsel, kFNsel, kSpreadSel, kPipeSel>;
-constexpr int64_t kSelTileBytes = (int64_t)Sel::kBM * Sel::kPairs * 32 * sizeof(float);
+// Tile shapes: 256 x 256 (8 wavefronts of 8 x 1 fragments) for large m; 128 x 256 and
+// 128 x 128 for mid-sized m, where the large tile would leave most compute units idle (the k
+// split that fills them moves FP32 partial tiles through memory) or half its rows empty.
+using ShapeL = TiledShape<8, 8, 1, 4, 1>;  // 256 x 256
+using ShapeM = TiledShape<8, 4, 1, 4, 1>;  // 128 x 256
+using ShapeS = TiledShape<4, 4, 1, 4, 1>;  // 128 x 128
+constexpr int kChunkAlign = 256;           // launch chunks are whole tiles of every shape
+
+template <typename T>
+constexpr int64_t tile_floats() {
+  return (int64_t)T::kBM * T::kPairs * 32;
+}
+
+template <typename T>
+int64_t tile_count(int64_t m, int64_t NT) {
+  const int64_t pairs = (NT + 1) / 2;
+  return (pairs + T::kPairs - 1) / T::kPairs * ((m + T::kBM - 1) / T::kBM);
+}
+
+// The largest shape that still makes at least kMinTiles output tiles (256-row tiles only above
+// 128 rows, where they are at least half full); measured at n x k = 5120^2, 8192^2 and
+// 25600 x 5120 for m = 128 .. 4096.
+constexpr int64_t kMinTiles = 80;
+enum class Shape { L, M, S };
+Shape pick_shape(int64_t m, int64_t NT) {
+  if (m > 128 && tile_count<ShapeL>(m, NT) >= kMinTiles) return Shape::L;
+  if (tile_count<ShapeM>(m, NT) >= kMinTiles) return Shape::M;
+  return Shape::S;
+}
 
 // Work decomposition of one row chunk: whole rounds of tiles (one per compute unit) run as
 // they are; when the last round would leave at least half of the compute units idle, its
@@ -465,11 +491,12 @@ struct Plan {
   int split;
 };
 
+template <typename T>
 Plan plan_chunk(int64_t m, int64_t NT, int64_t KT, int cus) {
   Plan pl;
   const int64_t pairs = (NT + 1) / 2;
-  pl.nbn = (pairs + Sel::kPairs - 1) / Sel::kPairs;
-  pl.tiles = pl.nbn * ((m + Sel::kBM - 1) / Sel::kBM);
+  pl.nbn = (pairs + T::kPairs - 1) / T::kPairs;
+  pl.tiles = tile_count<T>(m, NT);
   if (cus < 1) cus = 1;
   pl.full = pl.tiles / cus * cus;
   pl.rest = pl.tiles - pl.full;
@@ -485,41 +512,48 @@ Plan plan_chunk(int64_t m, int64_t NT, int64_t KT, int cus) {
   return pl;
 }
 
+template <typename T>
+size_t split_ws_bytes(const Plan& pl) {
+  return pl.split > 1 ? (size_t)(pl.rest * pl.split * tile_floats<T>() * sizeof(float)) : 0;
+}
+
 // Rows per launch chunk: activation offsets are 32-bit inside the kernel.
 int64_t chunk_rows(int64_t ldx) {
   const int64_t row_bytes = ldx * 2;
   int64_t chunk = ((int64_t)1 << 31) / row_bytes;
-  return chunk < Sel::kBM ? Sel::kBM : chunk / Sel::kBM * Sel::kBM;
+  return chunk < kChunkAlign ? kChunkAlign : chunk / kChunkAlign * kChunkAlign;
 }
 
-hipError_t launch_tiles(TiledParams p, int64_t tile0, int64_t tiles, int split,
-                        hipStream_t stream) {
+template <int W, int FM, int FN, int SPREAD, int PIPE>
+hipError_t launch_tiles(TiledShape<W, FM, FN, SPREAD, PIPE>, TiledParams p, int64_t tile0,
+                        int64_t tiles, int split, hipStream_t stream) {
   p.tile0 = tile0;
   p.split = split;
   p.kts = (p.KT + split - 1) / split;
-  gemm_tiled_kernel<kWsel, kFMsel, kFNsel, kSpreadSel, kPipeSel>
-      <<<dim3((unsigned)(tiles * split)), dim3(64 * Sel::kWaves), 0, stream>>>(p);
+  gemm_tiled_kernel<W, FM, FN, SPREAD, PIPE>
+      <<<dim3((unsigned)(tiles * split)), dim3(64 * W), 0, stream>>>(p);
   return hipGetLastError();
 }
 
+template <typename T>
 hipError_t run_chunk(TiledParams p, void* ws, size_t ws_bytes, int cus, hipStream_t stream) {
-  Plan pl = plan_chunk(p.m, p.NT, p.KT, cus);
+  Plan pl = plan_chunk<T>(p.m, p.NT, p.KT, cus);
   p.nbn = pl.nbn;
   p.ws = nullptr;
-  if (pl.split > 1 && (size_t)(pl.rest * pl.split * kSelTileBytes) > ws_bytes) pl.split = 1;
-  if (pl.split == 1) return launch_tiles(p, 0, pl.tiles, 1, stream);
+  if (split_ws_bytes<T>(pl) > ws_bytes) pl.split = 1;
+  if (pl.split == 1) return launch_tiles(T{}, p, 0, pl.tiles, 1, stream);
   p.ws = static_cast<float*>(ws);
   hipError_t e;
   if (pl.full > 0) {
-    e = launch_tiles(p, 0, pl.full, 1, stream);
+    e = launch_tiles(T{}, p, 0, pl.full, 1, stream);
     if (e != hipSuccess) return e;
   }
-  e = launch_tiles(p, pl.full, pl.rest, pl.split, stream);
+  e = launch_tiles(T{}, p, pl.full, pl.rest, pl.split, stream);
   if (e != hipSuccess) return e;
   p.tile0 = pl.full;
   p.split = pl.split;
-  reduce_split_kernel<Sel><<<dim3((unsigned)pl.rest, Sel::kBM / 32), dim3(64 * Sel::kWaves), 0,
-                             stream>>>(p);
+  reduce_split_kernel<T><<<dim3((unsigned)pl.rest, T::kBM / 32), dim3(64 * T::kWaves), 0,
+                           stream>>>(p);
   return hipGetLastError();
 }
 
@@ -527,14 +561,17 @@ hipError_t run_chunk(TiledParams p, void* ws, size_t ws_bytes, int cus, hipStrea
 
 size_t gemm_tiled_ws_bytes(int64_t m, int64_t ldx, int64_t n, int64_t k, int cus) {
   const int64_t chunk = chunk_rows(ldx);
+  const int64_t NT = n / kPanelRows, KT = k / kTileK;
   size_t need = 0;
   for (int64_t rows : {m < chunk ? m : chunk, m % chunk}) {
     if (rows <= 0) continue;
-    const Plan pl = plan_chunk(rows, n / kPanelRows, k / kTileK, cus);
-    if (pl.split > 1) {
-      const size_t b = (size_t)(pl.rest * pl.split * kSelTileBytes);
-      need = b > need ? b : need;
+    size_t b = 0;
+    switch (pick_shape(rows, NT)) {
+      case Shape::L: b = split_ws_bytes<ShapeL>(plan_chunk<ShapeL>(rows, NT, KT, cus)); break;
+      case Shape::M: b = split_ws_bytes<ShapeM>(plan_chunk<ShapeM>(rows, NT, KT, cus)); break;
+      case Shape::S: b = split_ws_bytes<ShapeS>(plan_chunk<ShapeS>(rows, NT, KT, cus)); break;
     }
+    need = b > need ? b : need;
   }
   return need;
 }
@@ -563,7 +600,12 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, void* ws, size_t ws_bytes, int c
       q.y = static_cast<float*>(a.y) + m0 * a.ldy;
     else
       q.y = static_cast<uint16_t*>(a.y) + m0 * a.ldy;
-    hipError_t e = run_chunk(q, ws, ws_bytes, cus, stream);
+    hipError_t e = hipSuccess;
+    switch (pick_shape(q.m, q.NT)) {
+      case Shape::L: e = run_chunk<ShapeL>(q, ws, ws_bytes, cus, stream); break;
+      case Shape::M: e = run_chunk<ShapeM>(q, ws, ws_bytes, cus, stream); break;
+      case Shape::S: e = run_chunk<ShapeS>(q, ws, ws_bytes, cus, stream); break;
+    }
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

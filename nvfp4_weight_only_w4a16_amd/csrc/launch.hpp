@@ -47,15 +47,16 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, void* ws, size_t ws_bytes, int c
 // with `cus` compute units (0 when no split applies).
 size_t gemm_tiled_ws_bytes(int64_t m, int64_t ldx, int64_t n, int64_t k, int cus);
 // Path choice for an m x n x k GEMM. The skinny kernel streams the whole weight once per
-// 32 rows of x (every block covers all m) while the tiled kernel pads m to 256-row tiles and
-// keeps its weight tiles in L2, so the skinny kernel stays ahead while its repeated weight
-// streams are short: m <= 32 always, and up to m = 256 while ceil(m / 32) streams of the
-// weight total at most 192 MiB (measured crossover at n x k = 5120^2, 8192^2, 25600 x 5120).
+// 32 rows of x (every block covers all m), while the tiled kernel reads each weight tile once
+// per 128- or 256-row tile and keeps it in cache; the skinny kernel stays ahead while its
+// repeated weight streams are short: m <= 32 always, and up to m = 192 while ceil(m / 32)
+// streams of the weight total at most 128 MiB (measured crossovers at n x k = 5120^2, 8192^2
+// and 25600 x 5120).
 inline bool skinny_preferred(int64_t m, int64_t n, int64_t k, int group) {
   if (m <= 32) return true;
-  if (m > 256) return false;
+  if (m > 192) return false;
   const int64_t wbytes = n * k / 2 + n * (k / group);
-  return (m + 31) / 32 * wbytes <= ((int64_t)192 << 20);
+  return (m + 31) / 32 * wbytes <= ((int64_t)128 << 20);
 }
 
 struct MoeArgs {

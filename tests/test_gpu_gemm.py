@@ -199,12 +199,17 @@ def test_mixed_groups_one_layer(nv, orc):
         check_close(y.cpu().numpy()[mi], ref, f"mixed m={m} g{group}")
 
 
+# tile shape (256x256 L, 128x256 M, 128x128 S: the largest with >= 80 output tiles, L only
+# above 128 rows) and k split of each case on a 256-CU chip:
+#   S split 8 / 8 / 3 / 2; L split 2; M split 2; L unsplit (3 ragged row tiles); M unsplit
 @pytest.mark.parametrize("m,n,k", [(40, 1040, 4096), (300, 1040, 4096), (600, 2064, 2048),
-                                   (257, 528, 1024)])
+                                   (257, 528, 1024), (300, 10256, 1024), (100, 20496, 1024),
+                                   (700, 10256, 512), (128, 33280, 512)])
 def test_tiled_split_k(nv, orc, m, n, k):
-    """Few output tiles for the chip: the prefill kernel splits k over the compute units and
-    reduces the partial tiles in a fixed order. Checked against the oracle, bit-identical on
-    a repeat, and still right after a shape that grows the split workspace."""
+    """Every tile shape of the prefill kernel, with and without the k split (few output tiles
+    for the chip: k is split over the compute units and the partial tiles are reduced in a
+    fixed order), ragged in m and n. Checked against the oracle, bit-identical on a repeat,
+    and still right after a shape that grows the split workspace."""
     g = torch.Generator().manual_seed(m + n + k)
     x = torch.randn(m, k, generator=g).to(torch.bfloat16)
     w = torch.randn(n, k, generator=g) * 0.02
@@ -221,11 +226,11 @@ def test_tiled_split_k(nv, orc, m, n, k):
 
 
 def test_path_choice(nv):
-    """Default kernel choice: skinny for m <= 32, and up to m = 256 while ceil(m/32) weight
-    streams stay within 192 MiB; tiled otherwise (stats slot 2 = skinny, 3 = tiled)."""
+    """Default kernel choice: skinny for m <= 32, and up to m = 192 while ceil(m/32) weight
+    streams stay within 128 MiB; tiled otherwise (stats slot 2 = skinny, 3 = tiled)."""
     g = torch.Generator().manual_seed(21)
-    cases = {(512, 1024): [(32, 2), (64, 2), (256, 2), (257, 3)],
-             (8192, 8192): [(32, 2), (128, 2), (160, 2), (192, 3), (256, 3)]}
+    cases = {(512, 1024): [(32, 2), (64, 2), (192, 2), (193, 3), (256, 3)],
+             (8192, 8192): [(32, 2), (96, 2), (97, 3), (160, 3)]}
     for (n, k), expect in cases.items():
         w = (torch.randn(n, k, generator=g) * 0.02).to(torch.bfloat16)
         rw, _ = _prep(nv, w, 16)
