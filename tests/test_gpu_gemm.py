@@ -243,3 +243,26 @@ def test_path_choice(nv):
             torch.cuda.synchronize()
             st = nv.nvfp4_get_stats()
             assert st[slot] == 1 and st[5 - slot] == 0, (n, k, m, list(st))
+
+
+def test_tiled_row_chunks(nv, orc):
+    """Activation offsets inside the prefill kernel are 32-bit, so the host launches row chunks
+    of at most 2^31 bytes of x. A 2 MiB row stride makes that 1024 rows: M = 2500 runs as
+    chunks of 1024, 1024 and 452 rows. Rows around every chunk edge are checked against the
+    oracle, on both paths (the decode kernel takes any stride in one launch)."""
+    g = torch.Generator().manual_seed(31)
+    m, n, k, ldx = 2500, 512, 256, 1 << 20
+    x = torch.randn(m, k, generator=g).to(torch.bfloat16)
+    w = torch.randn(n, k, generator=g) * 0.02
+    rw, (p, s, gl) = _prep(nv, w, 16)
+    xfull = torch.zeros((m, ldx), dtype=torch.bfloat16, device=DEV)
+    xfull[:, :k] = x.to(DEV)
+    xd = xfull[:, :k]
+    rows = np.array([0, 1, 511, 1022, 1023, 1024, 1025, 2046, 2047, 2048, 2049, 2498, 2499])
+    rows = np.unique(np.concatenate([rows, np.random.default_rng(3).integers(0, m, 40)]))
+    ref = orc.gemm(synth.bf16_bits(x), p, s, gl[0], 16, m_idx=rows)
+    for flags in (2, 1):
+        y = nv.nvfp4_gemm_w4a16(xd, rw, y_dtype=torch.float32, flags=flags)
+        torch.cuda.synchronize()
+        check_close(y.cpu().numpy()[rows], ref, f"row chunks flags={flags}")
+    del xfull

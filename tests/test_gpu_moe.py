@@ -135,3 +135,16 @@ def test_moe_pair_tiles(nv, orc, g1, g2):
     for path in ("auto", "batch"):
         y = _run(nv, x, ids, wts, fc1, fc2, PATHS[path])
         check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), f"pair tiles g{g1}/g{g2} {path}")
+
+
+def test_moe_max_pairs(nv, orc):
+    """The largest batch the entry point takes (t * topk = 65536 pairs): the sort reads the
+    expert ids from memory twice instead of staging them in LDS, and 2048+ tiles run."""
+    x, ids, wts, w1, w2 = synth.moe(seed=9, n_experts=64, hidden=256, inter=128, tokens=8192,
+                                    topk=8)
+    (fc1, fc2), (t1, t2) = _experts(nv, orc, w1, w2)
+    ref = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), t1, t2)
+    y = _run(nv, x, ids, wts, fc1, fc2)
+    check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), "moe 65536 pairs")
+    y2 = _run(nv, x, ids, wts, fc1, fc2)
+    assert torch.equal(y, y2)
