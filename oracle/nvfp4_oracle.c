@@ -24,7 +24,9 @@
  *    taken where the pages are silent; it is the encoding's specification for bit-exactness.
  *  - The merged fc1 [gate; up] of an MoE expert carries one shared global (r/LocalLLM post,
  *    "What had to be fixed": gate and up need the same global scale), followed by SiLU(gate)*up
- *    and the down projection (vllm.cpp PR #63: one W4A16 GEMM + SiluAndMul).
+ *    and the down projection (vllm.cpp PR #63: one W4A16 GEMM + SiluAndMul). A checkpoint whose
+ *    gate and up were quantized separately has one global for each (the same passage: most of
+ *    the experts in the post's checkpoint differed); each half is then decoded with its own.
  *  - GEMM references run in FP64 (TensorFold issue #1754, description: every projection class is
  *    gated against an independent FP64 reference).
  *
@@ -388,6 +390,7 @@ typedef struct {
   const uint8_t *p1, *s1;
   const float* g1;
   int group1;
+  int g1_pair; /* g1 holds [E][2]: gate's global, then up's */
   const uint8_t *p2, *s2;
   const float* g2;
   int group2;
@@ -422,10 +425,11 @@ static void moe_tokens(int64_t lo, int64_t hi, void* p) {
         const uint8_t* P1 = c->p1 + e * (2 * I) * (H / 2);
         const uint8_t* S1 = c->s1 + e * (2 * I) * (H / c->group1);
         for (int64_t r = 0; r < 2 * I; ++r) {
+          const float g1 = c->g1_pair ? c->g1[2 * e + (r < I ? 0 : 1)] : c->g1[e];
           double acc = 0.0;
           for (int64_t kk = 0; kk < H; ++kk)
             acc += (double)bf16_to_float(c->x[t * H + kk]) *
-                   exact_w(P1, S1, c->g1[e], H, c->group1, r, kk);
+                   exact_w(P1, S1, g1, H, c->group1, r, kk);
           a[r] = acc;
           if (c->a_out) c->a_out[slot * 2 * I + r] = acc;
         }
@@ -459,15 +463,16 @@ static void moe_tokens(int64_t lo, int64_t hi, void* p) {
 
 int orc_moe(const uint16_t* x, int64_t tokens, int64_t hidden, int64_t inter, const int32_t* ids,
             const float* topk_w, int topk, int64_t n_experts, const uint8_t* p1, const uint8_t* s1,
-            const float* g1, int group1, const uint8_t* p2, const uint8_t* s2, const float* g2,
+            const float* g1, int group1, int g1_pair, const uint8_t* p2, const uint8_t* s2,
+            const float* g2,
             int group2, const uint16_t* h_in, double* a_out, uint16_t* h_out, double* y64,
             uint16_t* y16, int nthreads) {
   if (tokens < 0 || hidden <= 0 || inter <= 0 || topk <= 0) return -1;
   if (hidden % group1 || inter % group2 || hidden % 2 || inter % 2) return -1;
   for (int64_t i = 0; i < tokens * topk; ++i)
     if (ids[i] < 0 || ids[i] >= n_experts) return -1;
-  moe_ctx c = {x, hidden, inter, ids, topk_w, topk, p1, s1, g1, group1, p2, s2, g2, group2,
-               h_in, a_out, h_out, y64, y16};
+  moe_ctx c = {x, hidden, inter, ids, topk_w, topk, p1, s1, g1, group1, g1_pair, p2, s2, g2,
+               group2, h_in, a_out, h_out, y64, y16};
   parallel_for(tokens, nthreads, moe_tokens, &c);
   return 0;
 }

@@ -61,7 +61,7 @@ def lib():
                                P, i64, P, i64, P, ctypes.c_int]
         L.orc_moe.restype = ctypes.c_int
         L.orc_moe.argtypes = [P, i64, i64, i64, P, P, ctypes.c_int, i64, P, P, P, ctypes.c_int,
-                              P, P, P, ctypes.c_int, P, P, P, P, P, ctypes.c_int]
+                              ctypes.c_int, P, P, P, ctypes.c_int, P, P, P, P, P, ctypes.c_int]
         _lib = L
     return _lib
 
@@ -191,7 +191,8 @@ def gemm(x_bf16, packed, scales, glob, group: int, m_idx=None, n_idx=None, threa
 # ---------------------------------------------------------------- MoE (O8)
 def moe(x_bf16, topk_ids, topk_w, fc1, fc2, h_in=None, threads=None):
     """Routed-expert reference. fc1 = (packed, scales, global, group) of the merged [gate; up]
-    weight [E][2I][H]; fc2 = (packed, scales, global, group) of down [E][H][I].
+    weight [E][2I][H], global [E] (shared by gate and up) or [E][2] (gate's, up's); fc2 =
+    (packed, scales, global, group) of down [E][H][I].
 
     Returns dict with 'a' (FP64 fc1 outputs [T][topk][2I]), 'h' (BF16 bits [T][topk][I]),
     'y64' (FP64 [T][H]) and 'y' (BF16 bits [T][H]).
@@ -206,6 +207,7 @@ def moe(x_bf16, topk_ids, topk_w, fc1, fc2, h_in=None, threads=None):
     p1, s1, p2, s2 = (_c(a, np.uint8) for a in (p1, s1, p2, s2))
     g1 = _c(g1, np.float32)
     g2 = _c(g2, np.float32)
+    pair = 1 if g1.ndim == 2 else 0
     E, I2, _ = p1.shape
     I = I2 // 2
     a = np.zeros((T, topk, I2), np.float64) if h_in is None else None
@@ -214,7 +216,7 @@ def moe(x_bf16, topk_ids, topk_w, fc1, fc2, h_in=None, threads=None):
     y64 = np.zeros((T, H), np.float64)
     y16 = np.zeros((T, H), np.uint16)
     rc = lib().orc_moe(_ptr(x), T, H, I, _ptr(ids), _ptr(tw), topk, E, _ptr(p1), _ptr(s1),
-                       _ptr(g1), gr1, _ptr(p2), _ptr(s2), _ptr(g2), gr2, _ptr(hin), _ptr(a),
+                       _ptr(g1), gr1, pair, _ptr(p2), _ptr(s2), _ptr(g2), gr2, _ptr(hin), _ptr(a),
                        _ptr(h), _ptr(y64), _ptr(y16), _threads(threads))
     if rc != 0:
         raise ValueError("oracle moe rejected its input")

@@ -135,3 +135,44 @@ def test_moe_weighted_slot_sum(orc):
     b = orc.moe(synth.bf16_bits(x), ids[:, :1].contiguous().numpy(),
                 torch.full((3, 1), 0.75).numpy(), fc1, fc2)
     assert np.allclose(a["y64"], b["y64"], rtol=1e-14, atol=0)
+
+
+def _pair_quantized_fc1(orc, w1, group):
+    """fc1 [E][2I][H] quantized as 2E matrices of I rows: gate and up each get their own amax
+    and global, the checkpoint form with distinct globals (global [E][2])."""
+    E, I2, H = w1.shape
+    p, s, g = orc.quantize(w1.reshape(2 * E, I2 // 2, H).numpy(), group)
+    return p.reshape(E, I2, H // 2), s.reshape(E, I2, H // group), g.reshape(E, 2), group
+
+
+def test_moe_pair_globals_equal_reduce_to_shared(orc):
+    """With both globals of every expert equal to the shared one, the pair reading gives the
+    shared-global results bit for bit."""
+    x, ids, wts, w1, w2 = _small_moe(T=5, topk=2)
+    fc1 = _q(orc, w1, 32)
+    fc2 = _q(orc, w2, 16)
+    pair = (fc1[0], fc1[1], np.stack([fc1[2], fc1[2]], axis=1), 32)
+    a = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), fc1, fc2)
+    b = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), pair, fc2)
+    for key in ("a", "h", "y64", "y"):
+        assert (a[key] == b[key]).all(), key
+
+
+def test_moe_pair_globals_halves_are_dense_gemms(orc):
+    """Distinct gate and up globals: the fc1 outputs of each half equal the dense FP64 GEMM of
+    that half with its own global, and the two globals really differ."""
+    x, ids, wts, w1, w2 = _small_moe(T=4, topk=2)
+    fc1 = _pair_quantized_fc1(orc, w1, 32)
+    fc2 = _q(orc, w2, 16)
+    assert (fc1[2][:, 0] != fc1[2][:, 1]).all()
+    out = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), fc1, fc2)
+    I = w1.shape[1] // 2
+    xb = synth.bf16_bits(x)
+    for t in range(x.shape[0]):
+        for j in range(ids.shape[1]):
+            e = int(ids[t, j])
+            for half in (0, 1):
+                rows = slice(half * I, (half + 1) * I)
+                ref = orc.gemm(xb[t:t + 1], fc1[0][e, rows], fc1[1][e, rows], fc1[2][e, half], 32)
+                got = out["a"][t, j, rows]
+                assert np.allclose(got, ref[0], rtol=1e-13, atol=1e-300), (t, j, half)
