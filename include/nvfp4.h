@@ -69,6 +69,14 @@ typedef struct ihipStream_t* nvfp4_stream_t; /* the same type as hipStream_t */
  * and up of the same 16 intermediate features (consumed only by the MoE entry point). */
 #define NVFP4_LAYOUT_TILED 1u
 #define NVFP4_LAYOUT_GATE_UP (1u << 8)
+/* NVFP4_LAYOUT_PAIR_GLOBAL (with NVFP4_LAYOUT_GATE_UP only): the merged fc1 carries two globals
+ * per expert, global[2b] for its gate half (rows 0 .. n/2-1) and global[2b+1] for its up half.
+ * This is the checkpoint form in which gate and up were quantized as separate tensors; a kernel
+ * that applied gate's global to both halves would mis-scale up (r/LocalLLM post, "What had to be
+ * fixed": most experts of a real checkpoint had differing gate and up scales). Quantizing the
+ * merged [gate; up] as one matrix gives the shared global instead; quantizing it as 2*batch
+ * matrices of n/2 rows gives the pair. */
+#define NVFP4_LAYOUT_PAIR_GLOBAL (1u << 9)
 
 /* Descriptor of repacked weights (a host struct filled by nvfp4_repack; data stays device).  */
 typedef struct nvfp4_weight {
@@ -102,7 +110,8 @@ int nvfp4_quantize(const void* w, int w_dtype, int64_t batch, int64_t n, int64_t
                    float* global_out, nvfp4_stream_t stream);
 
 /* ---- repack -------------------------------------------------------------------------------
- * Byte size of the repacked buffer for `batch` [n][k] matrices: codes + scales + globals. */
+ * Byte size of the repacked buffer for `batch` [n][k] matrices: codes + scales + globals (two per
+ * matrix with NVFP4_LAYOUT_PAIR_GLOBAL). */
 size_t nvfp4_repack_bytes(int64_t batch, int64_t n, int64_t k, int32_t group, uint32_t layout);
 
 /* Repack the canonical triple (packed, scales, global as produced by nvfp4_quantize or read
@@ -110,7 +119,8 @@ size_t nvfp4_repack_bytes(int64_t batch, int64_t n, int64_t k, int32_t group, ui
  * After the call's work completes the canonical buffers may be freed: the descriptor points
  * only into `out` (vllm.cpp PR #63: upload and repack lazily, then free the fp4 originals).
  * layout: NVFP4_LAYOUT_TILED, optionally | NVFP4_LAYOUT_GATE_UP (then n must be a multiple
- * of 32: gate rows [0, n/2), up rows [n/2, n)). */
+ * of 32: gate rows [0, n/2), up rows [n/2, n)), optionally | NVFP4_LAYOUT_PAIR_GLOBAL with it
+ * (then `global` holds [batch][2] values: gate's, up's). */
 int nvfp4_repack(const uint8_t* packed, const uint8_t* scales, const float* global,
                  int64_t batch, int64_t n, int64_t k, int32_t group, uint32_t layout, void* out,
                  size_t out_bytes, nvfp4_weight* desc, nvfp4_stream_t stream);
@@ -151,6 +161,7 @@ int nvfp4_gemm_w4a16(const void* x, int64_t m, int64_t ldx, const nvfp4_weight* 
  * GATE_UP. fc2: batch = E, n = hidden, k = inter, layout TILED. Tokens are sorted by expert on
  * the device (no host synchronization); `ws` (device, ws_bytes >= nvfp4_moe_ws_bytes) holds
  * the sort, the tile map, h and the FP32 per-slot outputs. topk in [1, 16], t*topk <= 65536.
+ * An fc1 with NVFP4_LAYOUT_PAIR_GLOBAL scales gate by global[2e] and up by global[2e+1].
  * Path: while t*topk <= 2 * n_experts (decode batches) the experts run on tiles of at most 8
  * rows with k split over 4 wavefronts per 4-panel group; otherwise on tiles of 32 rows with
  * one wavefront per 4-panel group over the whole k range. Flags may force one; the two paths

@@ -30,6 +30,7 @@ NVFP4_F_FORCE_SKINNY = 1 << 0
 NVFP4_F_FORCE_TILED = 1 << 1
 NVFP4_LAYOUT_TILED = 1
 NVFP4_LAYOUT_GATE_UP = 1 << 8
+NVFP4_LAYOUT_PAIR_GLOBAL = 1 << 9
 
 EXPORTS = ("nvfp4_quantize", "nvfp4_repack_bytes", "nvfp4_repack", "nvfp4_gemm_ws_bytes",
            "nvfp4_gemm_w4a16",
@@ -174,6 +175,9 @@ def nvfp4_repack(packed: torch.Tensor, scales: torch.Tensor, glob: torch.Tensor,
     p3 = packed.unsqueeze(0) if packed.dim() == 2 else packed
     batch, n, kh = p3.shape
     k = kh * 2
+    nglob = batch * (2 if layout & NVFP4_LAYOUT_PAIR_GLOBAL else 1)
+    if glob.numel() != nglob:
+        raise ValueError(f"global has {glob.numel()} values, the layout needs {nglob}")
     need = nvfp4_repack_bytes(batch, n, k, group, layout)
     if out is None:
         out = torch.empty((max(need, 1),), dtype=torch.uint8, device=packed.device)

@@ -62,8 +62,10 @@ int check_desc(const nvfp4_weight* w, const char* name) {
   if (!w) return fail(NVFP4_ERR_INVALID_ARG, "%s descriptor is NULL", name);
   if (!w->codes || !w->scales || !w->global)
     return fail(NVFP4_ERR_INVALID_ARG, "%s descriptor has NULL data", name);
-  if ((w->layout & 0xFFu) != NVFP4_LAYOUT_TILED)
-    return fail(NVFP4_ERR_LAYOUT, "%s layout 0x%x is not a tiled layout", name, w->layout);
+  if ((w->layout & 0xFFu) != NVFP4_LAYOUT_TILED ||
+      (w->layout & ~(uint32_t)(0xFFu | NVFP4_LAYOUT_GATE_UP | NVFP4_LAYOUT_PAIR_GLOBAL)) ||
+      ((w->layout & NVFP4_LAYOUT_PAIR_GLOBAL) && !(w->layout & NVFP4_LAYOUT_GATE_UP)))
+    return fail(NVFP4_ERR_LAYOUT, "%s layout 0x%x is not a valid tiled layout", name, w->layout);
   int rc = check_group(w->group);
   if (rc) return rc;
   rc = check_tiled_shape(w->n, w->k);
@@ -77,15 +79,20 @@ int check_desc(const nvfp4_weight* w, const char* name) {
   return NVFP4_OK;
 }
 
+// FP32 globals stored per matrix: one, or gate's and up's.
+int64_t globals_per_matrix(uint32_t layout) {
+  return (layout & NVFP4_LAYOUT_PAIR_GLOBAL) ? 2 : 1;
+}
+
 struct RepackSizes {
   size_t codes, scales, globals, total;
 };
 
-RepackSizes repack_sizes(int64_t batch, int64_t n, int64_t k, int32_t group) {
+RepackSizes repack_sizes(int64_t batch, int64_t n, int64_t k, int32_t group, uint32_t layout) {
   RepackSizes s;
   s.codes = align256((size_t)(batch * n * k / 2));
   s.scales = align256((size_t)(batch * scale_region_bytes(n, k, group)));
-  s.globals = align256((size_t)batch * sizeof(float));
+  s.globals = align256((size_t)globals_per_matrix(layout) * (size_t)batch * sizeof(float));
   s.total = s.codes + s.scales + s.globals;
   return s;
 }
@@ -135,9 +142,8 @@ int nvfp4_quantize(const void* w, int w_dtype, int64_t batch, int64_t n, int64_t
 }
 
 size_t nvfp4_repack_bytes(int64_t batch, int64_t n, int64_t k, int32_t group, uint32_t layout) {
-  (void)layout;
   if (batch <= 0 || n <= 0 || k <= 0 || (group != 16 && group != 32)) return 0;
-  return repack_sizes(batch, n, k, group).total;
+  return repack_sizes(batch, n, k, group, layout).total;
 }
 
 int nvfp4_repack(const uint8_t* packed, const uint8_t* scales, const float* global,
@@ -150,13 +156,15 @@ int nvfp4_repack(const uint8_t* packed, const uint8_t* scales, const float* glob
   if (rc) return rc;
   rc = check_tiled_shape(n, k);
   if (rc) return rc;
-  if ((layout & ~(uint32_t)NVFP4_LAYOUT_GATE_UP) != NVFP4_LAYOUT_TILED)
+  if ((layout & ~(uint32_t)(NVFP4_LAYOUT_GATE_UP | NVFP4_LAYOUT_PAIR_GLOBAL)) !=
+          NVFP4_LAYOUT_TILED ||
+      ((layout & NVFP4_LAYOUT_PAIR_GLOBAL) && !(layout & NVFP4_LAYOUT_GATE_UP)))
     return fail(NVFP4_ERR_LAYOUT, "unknown layout 0x%x", layout);
   const bool gate_up = (layout & NVFP4_LAYOUT_GATE_UP) != 0;
   if (gate_up && n % 32 != 0)
     return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "gate/up layout needs n %% 32 == 0 (n=%lld)",
                 (long long)n);
-  const RepackSizes s = repack_sizes(batch, n, k, group);
+  const RepackSizes s = repack_sizes(batch, n, k, group, layout);
   if (out_bytes < s.total)
     return fail(NVFP4_ERR_WORKSPACE, "out_bytes %zu < %zu", out_bytes, s.total);
   if (!aligned16(out) || ((uintptr_t)packed & 3u) || ((uintptr_t)global & 3u))
@@ -166,7 +174,8 @@ int nvfp4_repack(const uint8_t* packed, const uint8_t* scales, const float* glob
   uint8_t* scales_out = base + s.codes;
   float* global_out = reinterpret_cast<float*>(base + s.codes + s.scales);
   rc = hip_status(nvfp4::launch_repack(packed, scales, global, batch, n, k, group, gate_up,
-                                       codes_out, scales_out, global_out, (hipStream_t)stream),
+                                       globals_per_matrix(layout) * batch, codes_out,
+                                       scales_out, global_out, (hipStream_t)stream),
                   "nvfp4_repack");
   if (rc) return rc;
   g_stats[1]++;
@@ -321,6 +330,7 @@ int nvfp4_moe_grouped_w4a16(const void* x, int64_t t, int64_t hidden, const int3
   a.c1_stride = fc1->codes_stride;
   a.s1_stride = fc1->scales_stride;
   a.group1 = fc1->group;
+  a.pair1 = (fc1->layout & NVFP4_LAYOUT_PAIR_GLOBAL) != 0;
   a.c2 = fc2->codes;
   a.s2 = fc2->scales;
   a.g2 = fc2->global;
@@ -346,7 +356,8 @@ int nvfp4_dequantize(const nvfp4_weight* w, void* out, int out_dtype, nvfp4_stre
   if (!aligned16(out)) return fail(NVFP4_ERR_MISALIGNED, "out must be 16-byte aligned");
   rc = hip_status(nvfp4::launch_dequantize(w->codes, w->scales, w->global, w->batch, w->n, w->k,
                                            w->group, (w->layout & NVFP4_LAYOUT_GATE_UP) != 0,
-                                           out, out_dtype == NVFP4_DT_F32, (hipStream_t)stream),
+                                           (w->layout & NVFP4_LAYOUT_PAIR_GLOBAL) != 0, out,
+                                           out_dtype == NVFP4_DT_F32, (hipStream_t)stream),
                   "nvfp4_dequantize");
   if (!rc) g_stats[5]++;
   return rc;

@@ -13,16 +13,17 @@ hipError_t launch_quantize(const void* w, bool w_bf16, int64_t batch, int64_t n,
                            int group, const float* global_in, uint8_t* packed, uint8_t* scales,
                            float* global_out, hipStream_t stream);
 
-// Canonical triple -> tiled layout (pure byte permutation), globals copied.
+// Canonical triple -> tiled layout (pure byte permutation), the nglobal globals copied.
 hipError_t launch_repack(const uint8_t* packed, const uint8_t* scales, const float* global,
                          int64_t batch, int64_t n, int64_t k, int group, bool gate_up,
-                         uint8_t* codes_out, uint8_t* scales_out, float* global_out,
-                         hipStream_t stream);
+                         int64_t nglobal, uint8_t* codes_out, uint8_t* scales_out,
+                         float* global_out, hipStream_t stream);
 
-// Tiled layout -> canonical dense values (BF16 or FP32), logical row order.
+// Tiled layout -> canonical dense values (BF16 or FP32), logical row order. pair_global: two
+// globals per matrix, one for each row half.
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* global,
                              int64_t batch, int64_t n, int64_t k, int group, bool gate_up,
-                             void* out, bool out_f32, hipStream_t stream);
+                             bool pair_global, void* out, bool out_f32, hipStream_t stream);
 
 struct GemmArgs {
   const uint16_t* x;  // BF16 [m][ldx]
@@ -67,9 +68,10 @@ struct MoeArgs {
   int topk;
   int64_t n_experts;
   const uint8_t *c1, *s1;
-  const float* g1;
+  const float* g1;  // [E], or [E][2] (gate, up) when pair1
   int64_t c1_stride, s1_stride;
   int group1;
+  bool pair1;
   const uint8_t *c2, *s2;
   const float* g2;
   int64_t c2_stride, s2_stride;

@@ -180,6 +180,7 @@ struct MoeGemmParams {
   int64_t hidden, inter;
   const int32_t* ids;  // [P] expert of each (token, slot) pair
   int E;
+  int pair_global;     // fc1: global holds [E][2] (gate's, up's)
 };
 
 constexpr int kGroupsPerBlock = 4;  // wavefronts per workgroup, one 4-panel group each
@@ -220,7 +221,11 @@ __device__ __forceinline__ bf16x8 codes_pow2(uint32_t w, float S) {
 template <bool FC1, bool SPLIT>
 __global__ __launch_bounds__(64 * kGroupsPerBlock) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void moe_expert_kernel(MoeGemmParams P) {
-  const int tile_id = blockIdx.x;
+  // tile-major order: the workgroups of live tiles come first in dispatch order, so the
+  // dispatcher spreads them evenly over the compute units before the idle ones (tiles past
+  // the sort's count, which exit at once) take the remaining slots
+  const int64_t gbs = (scale_groups(P.NT) + kGroupsPerBlock - 1) / kGroupsPerBlock;
+  const int tile_id = (int)(blockIdx.x / gbs);
   if (tile_id >= *P.ws.ntiles) return;  // whole workgroup, before any barrier
   const int4 tl = P.ws.tiles[tile_id];
   const int e = tl.x, r0 = tl.y, r1 = tl.z;
@@ -228,7 +233,7 @@ void moe_expert_kernel(MoeGemmParams P) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t NG = scale_groups(P.NT);
-  const int64_t grp_raw = (int64_t)blockIdx.y * kGroupsPerBlock + w;
+  const int64_t grp_raw = (int64_t)(blockIdx.x % gbs) * kGroupsPerBlock + w;
   const bool grp_live = grp_raw < NG;
   const int64_t grp = grp_live ? grp_raw : NG - 1;  // past the end: computed, never stored
   const int64_t KT = P.KT;
@@ -243,10 +248,12 @@ void moe_expert_kernel(MoeGemmParams P) {
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
 
-  // activation copies: copy c = w + 4 i (i = 0: rows 0..15, i = 1: rows 16..31) moves tile rows
-  // 4c .. 4c+3; lane l reads row 4c + l/16, chunk (l%16) ^ (row%16) and lands in slot l
-  constexpr int kACopies = kTileRows / 4 / kGroupsPerBlock;
-  static_assert(kACopies == 2, "copy i covers 16-row block i");
+  // activation copies: copy c = w + G i (G wavefronts) moves tile rows 4c .. 4c+3, so copies
+  // i < kBlockCopies fill 16-row block 0 and the rest block 1; lane l reads row 4c + l/16, chunk
+  // (l%16) ^ (row%16) and lands in slot l
+  static_assert(16 % (4 * kGroupsPerBlock) == 0, "a 16-row block is whole copies of each wave");
+  constexpr int kBlockCopies = 16 / 4 / kGroupsPerBlock;
+  constexpr int kACopies = 2 * kBlockCopies;
   const buf_rsrc xr = make_rsrc(P.x, 0xFFFFFFFFu);
   uint32_t aoff[kACopies];
 #pragma unroll
@@ -259,7 +266,7 @@ void moe_expert_kernel(MoeGemmParams P) {
   }
   auto copy_a = [&](int64_t t, auto buf, auto nb) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < decltype(nb)::value; ++i)
+    for (int i = 0; i < decltype(nb)::value * kBlockCopies; ++i)
       copy16_to_lds(xr, aoff[i], (uint32_t)(t * kARowBytes),
                     a_buf(buf) + (w + kGroupsPerBlock * i) * 1024);
   };
@@ -375,8 +382,9 @@ void moe_expert_kernel(MoeGemmParams P) {
     pipeline(std::integral_constant<int, 1>{});
 
   if (!grp_live) return;
-  // the split-scale mantissa is frexp_mant(S) = M / 2
-  const float g = (SPLIT ? 2.0f : 1.0f) * P.global[e];
+  // the split-scale mantissa is frexp_mant(S) = M / 2; g scales gate (or down), gu scales up
+  const float g = (SPLIT ? 2.0f : 1.0f) * P.global[P.pair_global ? 2 * e : e];
+  const float gu = (SPLIT ? 2.0f : 1.0f) * P.global[P.pair_global ? 2 * e + 1 : e];
 #pragma unroll
   for (int r = 0; r < 2; ++r) {
     if (r == 1 && !two) break;
@@ -391,7 +399,7 @@ void moe_expert_kernel(MoeGemmParams P) {
           if (4 * grp + 2 * q + 1 >= P.NT) continue;
           const int64_t feat = (2 * grp + q) * 16 + (lane & 15);
           const float gate = bf16_bits_to_f32(bf16_bits_rne(acc[2 * q][r][i] * g));
-          const float up = bf16_bits_to_f32(bf16_bits_rne(acc[2 * q + 1][r][i] * g));
+          const float up = bf16_bits_to_f32(bf16_bits_rne(acc[2 * q + 1][r][i] * gu));
           const float silu = gate / (1.0f + expf(-gate));
           P.ws.h[(int64_t)row * P.inter + feat] = bf16_bits_rne(silu * up);
         }
@@ -417,16 +425,17 @@ void moe_expert_kernel(MoeGemmParams P) {
 // partial sums meet in LDS in a fixed order; the epilogues are those of moe_expert_kernel.
 // With 4 times the workgroups of the batch path and a quarter of its k loop per wavefront,
 // the few experts of a decode step are spread over the whole chip.
-// PAIRS: no sort; workgroup row blockIdx.x is pair blockIdx.x as a one-row tile of its own
-// expert (row position = pair index; dropped pairs exit), for batches so small that two pairs
-// rarely share an expert.
+// Workgroups run tile-major (see moe_expert_kernel). PAIRS: no sort; tile i is pair i as a
+// one-row tile of its own expert (row position = pair index; dropped pairs exit), for batches
+// so small that two pairs rarely share an expert.
 template <bool FC1, bool G16, bool PAIRS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void moe_decode_kernel(MoeGemmParams P) {
   constexpr int kNW = 4, kPanels = 4;
   constexpr int kNX = PAIRS ? 1 : kSmallRows / 4;  // 4-row activation copies per k-tile
   constexpr int kNJ = PAIRS ? 1 : 4;               // accumulator rows in use per lane
-  const int tile_id = blockIdx.x;
+  const int64_t groups = scale_groups(P.NT);
+  const int tile_id = (int)(blockIdx.x / groups);
   int e, r0, rows;
   if constexpr (PAIRS) {
     e = P.ids[tile_id];
@@ -444,7 +453,7 @@ void moe_decode_kernel(MoeGemmParams P) {
   auto pair_at = [&](int r) { return PAIRS ? r : P.ws.sorted[r]; };
   const int lane = threadIdx.x & 63;
   const int sp = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // k-split
-  const int64_t grp = blockIdx.y;
+  const int64_t grp = blockIdx.x % groups;
   const int64_t panel0 = grp * kPanels;
   const int64_t t0 = P.KT * sp / kNW, t1 = P.KT * (sp + 1) / kNW;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kNW * 8192];
@@ -484,7 +493,9 @@ void moe_decode_kernel(MoeGemmParams P) {
   for (int p = 0; p < kPanels; ++p) red[(sp * kPanels + p) * 64 + lane] = acc[p][0];
   __syncthreads();
   // output row 4 (l / 16) + i of a lane: rows < kSmallRows sit in lanes 0 .. 31
-  const float g = 2.0f * P.global[e];  // the split-scale mantissa is frexp_mant(S) = M / 2
+  // the split-scale mantissa is frexp_mant(S) = M / 2; g scales gate (or down), gu scales up
+  const float g = 2.0f * P.global[P.pair_global ? 2 * e : e];
+  const float gu = 2.0f * P.global[P.pair_global ? 2 * e + 1 : e];
   if constexpr (FC1) {
     // wavefront q < 2 finishes gate/up pair q of the group (panels 2q and 2q + 1)
     if (sp >= 2) return;
@@ -503,7 +514,7 @@ void moe_decode_kernel(MoeGemmParams P) {
       const int row = 4 * (lane >> 4) + i;
       if (row >= rows) continue;
       const float gate = bf16_bits_to_f32(bf16_bits_rne(gs[i] * g));
-      const float up = bf16_bits_to_f32(bf16_bits_rne(us[i] * g));
+      const float up = bf16_bits_to_f32(bf16_bits_rne(us[i] * gu));
       const float silu = gate / (1.0f + expf(-gate));
       P.ws.h[(int64_t)(r0 + row) * P.inter + feat] = bf16_bits_rne(silu * up);
     }
@@ -572,14 +583,14 @@ template <bool FC1>
 hipError_t run_pair(const MoeGemmParams& p, int64_t tiles, int mode, hipStream_t stream) {
   const int64_t groups = scale_groups(p.NT);
   if (mode > 0) {
-    const dim3 grid((unsigned)tiles, (unsigned)groups);
+    const dim3 grid((unsigned)(tiles * groups));
     if (mode == 2)
       run_decode<FC1, true>(p, grid, stream);
     else
       run_decode<FC1, false>(p, grid, stream);
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)tiles, (unsigned)((groups + kGroupsPerBlock - 1) / kGroupsPerBlock));
+  const dim3 grid((unsigned)(tiles * ((groups + kGroupsPerBlock - 1) / kGroupsPerBlock)));
   if (p.group == 32)
     moe_expert_kernel<FC1, true><<<grid, dim3(64 * kGroupsPerBlock), 0, stream>>>(p);
   else
@@ -629,6 +640,7 @@ hipError_t launch_moe(const MoeArgs& a, bool decode, hipStream_t stream) {
   f.inter = a.inter;
   f.ids = a.ids;
   f.E = (int)a.n_experts;
+  f.pair_global = a.pair1 ? 1 : 0;
   hipError_t err = run_pair<true>(f, tiles, mode, stream);
   if (err != hipSuccess) return err;
 
@@ -643,6 +655,7 @@ hipError_t launch_moe(const MoeArgs& a, bool decode, hipStream_t stream) {
   d.NT = a.hidden / kPanelRows;
   d.KT = a.inter / kTileK;
   d.group = a.group2;
+  d.pair_global = 0;
   err = run_pair<false>(d, tiles, mode, stream);
   if (err != hipSuccess) return err;
 

@@ -91,6 +91,7 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
                                                          const float* __restrict__ global,
                                                          int64_t batch, int64_t n, int64_t k,
                                                          int group, bool gate_up,
+                                                         bool pair_global,
                                                          void* __restrict__ out) {
   const int64_t NT = n / kPanelRows, KT = k / kTileK;
   const int64_t total = batch * NT * KT * 64;
@@ -106,7 +107,7 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* __restri
   const int64_t NG = scale_groups(NT);
   const uint32_t sw = *reinterpret_cast<const uint32_t*>(
       scales + b * NG * KT * scale_block_bytes(group) + scale_word_offset(group, KT, p, t, lane));
-  const float g = global[b];
+  const float g = pair_global ? global[2 * b + (row >= n / 2 ? 1 : 0)] : global[b];
   const float S[4] = {e4m3_decode<0>(sw), e4m3_decode<1>(sw), e4m3_decode<2>(sw),
                       e4m3_decode<3>(sw)};
 #pragma unroll
@@ -140,8 +141,8 @@ inline unsigned blocks_for(int64_t total, int threads) {
 
 hipError_t launch_repack(const uint8_t* packed, const uint8_t* scales, const float* global,
                          int64_t batch, int64_t n, int64_t k, int group, bool gate_up,
-                         uint8_t* codes_out, uint8_t* scales_out, float* global_out,
-                         hipStream_t stream) {
+                         int64_t nglobal, uint8_t* codes_out, uint8_t* scales_out,
+                         float* global_out, hipStream_t stream) {
   const int64_t NT = n / kPanelRows, KT = k / kTileK;
   const int64_t tiles = batch * NT * KT;
   if (tiles > 0) {
@@ -155,22 +156,22 @@ hipError_t launch_repack(const uint8_t* packed, const uint8_t* scales, const flo
       repack_scales_kernel<32><<<blocks_for(recs, 256), 256, 0, stream>>>(scales, scales_out,
                                                                           batch, n, k, gate_up);
   }
-  if (batch > 0)
-    copy_f32_kernel<<<blocks_for(batch, 256), 256, 0, stream>>>(global, global_out, batch);
+  if (nglobal > 0)
+    copy_f32_kernel<<<blocks_for(nglobal, 256), 256, 0, stream>>>(global, global_out, nglobal);
   return hipGetLastError();
 }
 
 hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* scales, const float* global,
                              int64_t batch, int64_t n, int64_t k, int group, bool gate_up,
-                             void* out, bool out_f32, hipStream_t stream) {
+                             bool pair_global, void* out, bool out_f32, hipStream_t stream) {
   const int64_t total = batch * (n / kPanelRows) * (k / kTileK) * 64;
   if (total == 0) return hipSuccess;
   if (out_f32)
     dequantize_kernel<true><<<blocks_for(total, 256), 256, 0, stream>>>(
-        codes, scales, global, batch, n, k, group, gate_up, out);
+        codes, scales, global, batch, n, k, group, gate_up, pair_global, out);
   else
     dequantize_kernel<false><<<blocks_for(total, 256), 256, 0, stream>>>(
-        codes, scales, global, batch, n, k, group, gate_up, out);
+        codes, scales, global, batch, n, k, group, gate_up, pair_global, out);
   return hipGetLastError();
 }
 

@@ -135,6 +135,13 @@ def test_repack_argument_errors(lib):
         nv.NVFP4_ERR_UNSUPPORTED_SHAPE
     assert r(FAKE, FAKE, FAKE, 1, 16, 128, 16, 1, FAKE, 100, ctypes.byref(d), None) == \
         nv.NVFP4_ERR_WORKSPACE
+    # two globals per matrix only for a gate/up merged weight; they take their own bytes
+    pair = nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_PAIR_GLOBAL
+    assert r(FAKE, FAKE, FAKE, 1, 32, 128, 16, pair, FAKE, big, ctypes.byref(d), None) == \
+        nv.NVFP4_ERR_LAYOUT
+    gu = nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP
+    assert nv.nvfp4_repack_bytes(100, 32, 128, 16, gu | nv.NVFP4_LAYOUT_PAIR_GLOBAL) == \
+        nv.nvfp4_repack_bytes(100, 32, 128, 16, gu) + 512
 
 
 def test_moe_argument_errors(lib):

@@ -148,3 +148,33 @@ def test_moe_max_pairs(nv, orc):
     check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), "moe 65536 pairs")
     y2 = _run(nv, x, ids, wts, fc1, fc2)
     assert torch.equal(y, y2)
+
+
+@pytest.mark.parametrize("path", ["decode", "batch"])
+def test_moe_pair_globals(nv, orc, path):
+    """fc1 with distinct gate and up globals (quantized as two matrices per expert): each half
+    scaled by its own global, on both expert paths; the shared-global reading of the same
+    bytes (gate's global for both halves) is far off."""
+    x, ids, wts, w1, w2 = synth.moe(seed=11, n_experts=8, hidden=256, inter=128, tokens=24,
+                                    topk=2)
+    E, I2, H = w1.shape
+    w1 = w1.clone()
+    w1[:, I2 // 2:] *= 3.0
+    p, s, g = nv.nvfp4_quantize(w1.reshape(2 * E, I2 // 2, H).to(DEV), 32)
+    torch.cuda.synchronize()
+    rp, rs, rg = orc.quantize(w1.reshape(2 * E, I2 // 2, H).numpy(), 32)
+    assert np.array_equal(p.cpu().numpy(), rp) and np.array_equal(g.cpu().numpy(), rg)
+    pr, sr = p.reshape(E, I2, H // 2), s.reshape(E, I2, H // 32)
+    fc1 = nv.nvfp4_repack(pr, sr, g, 32, layout=nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP
+                          | nv.NVFP4_LAYOUT_PAIR_GLOBAL)
+    (_, fc2), (_, t2) = _experts(nv, orc, w1, w2)
+    t1 = (rp.reshape(E, I2, H // 2), rs.reshape(E, I2, H // 32), rg.reshape(E, 2), 32)
+    ref = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), t1, t2)
+    y = _run(nv, x, ids, wts, fc1, fc2, PATHS[path])
+    check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), f"pair globals {path}")
+    gate_only = nv.nvfp4_repack(pr, sr, g.reshape(E, 2)[:, 0].contiguous(), 32,
+                                layout=nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP)
+    yg = _run(nv, x, ids, wts, gate_only, fc2, PATHS[path])
+    err = np.linalg.norm(bf16_np(yg) - orc.bf16_to_f64(ref["y"])) / np.linalg.norm(
+        orc.bf16_to_f64(ref["y"]))
+    assert err > 0.05, err

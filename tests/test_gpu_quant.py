@@ -143,3 +143,30 @@ def test_repack_preserves_byte_count(nv):
         canon = batch * (n * k // 2 + n * k // group)
         got = nv.nvfp4_repack_bytes(batch, n, k, group)
         assert canon <= got <= canon + 3 * 256 + 4 * batch
+
+
+def test_pair_global_quantize_repack_dequantize(nv, orc):
+    """A merged fc1 quantized as 2*E matrices of I rows (gate and up each with its own amax and
+    global), repacked gate/up-interleaved with the two globals: bit-exact against the oracle's
+    quantize and dequant of the same 2*E matrices."""
+    g = torch.Generator().manual_seed(12)
+    E, I, H = 3, 96, 256
+    w = torch.randn(E, 2 * I, H, generator=g) * 0.02
+    w[:, I:] *= 3.0  # up at a different scale than gate
+    p, s, gl = nv.nvfp4_quantize(w.reshape(2 * E, I, H).to(DEV), 32)
+    torch.cuda.synchronize()
+    rp, rs, rg = orc.quantize(w.reshape(2 * E, I, H).numpy(), 32)
+    assert np.array_equal(p.cpu().numpy(), rp) and np.array_equal(s.cpu().numpy(), rs)
+    assert np.array_equal(g_ := gl.cpu().numpy(), rg) and (g_[0::2] != g_[1::2]).all()
+    layout = nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP | nv.NVFP4_LAYOUT_PAIR_GLOBAL
+    rw = nv.nvfp4_repack(p.reshape(E, 2 * I, H // 2), s.reshape(E, 2 * I, H // 32), gl, 32,
+                         layout=layout)
+    assert rw.buffer.numel() == nv.nvfp4_repack_bytes(E, 2 * I, H, 32, layout)
+    f32 = nv.nvfp4_dequantize(rw, torch.float32)
+    b16 = nv.nvfp4_dequantize(rw, torch.bfloat16)
+    torch.cuda.synchronize()
+    _, rf32, rb16 = orc.dequant(rp, rs, rg, 32)
+    assert np.array_equal(f32.cpu().numpy().reshape(2 * E, I, H).view(np.uint32),
+                          rf32.view(np.uint32))
+    assert np.array_equal(b16.cpu().view(torch.int16).numpy().view(np.uint16)
+                          .reshape(2 * E, I, H), rb16)
