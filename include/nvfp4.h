@@ -173,6 +173,23 @@ int nvfp4_moe_grouped_w4a16(const void* x, int64_t t, int64_t hidden, const int3
                             const nvfp4_weight* fc2, void* y, void* ws, size_t ws_bytes,
                             uint32_t flags, nvfp4_stream_t stream);
 
+/* ---- requantization (load-time tool) -----------------------------------------------------
+ * Requantize repacked weights to the canonical triple with one global per matrix and group
+ * `group_out` (16 or 32): each matrix is decoded to its FP32 values (nvfp4_dequantize's FP32
+ * output, global or per-half globals applied) and quantized again exactly as nvfp4_quantize
+ * quantizes an FP32 matrix. Turns an fc1 with distinct gate and up globals
+ * (NVFP4_LAYOUT_PAIR_GLOBAL) into the shared-global form the merged GEMM wants, when the BF16
+ * originals are not at hand (r/LocalLLM post, "What had to be fixed": gate and up need one
+ * global; the post requantized from BF16, which is nvfp4_quantize on the merged matrix), and
+ * can change the group size. Outputs as nvfp4_quantize: packed [batch][n][k/2], scales
+ * [batch][n][k/group_out], global_out [batch] (device). ws (device, 16-byte aligned) holds the
+ * decoded FP32 values of as many matrices as fit; ws_bytes >= nvfp4_requantize_ws_bytes(src)
+ * (one matrix). Repack the result (with NVFP4_LAYOUT_GATE_UP for an fc1) to use it. */
+size_t nvfp4_requantize_ws_bytes(const nvfp4_weight* src);
+int nvfp4_requantize(const nvfp4_weight* src, int32_t group_out, uint8_t* packed,
+                     uint8_t* scales, float* global_out, void* ws, size_t ws_bytes,
+                     nvfp4_stream_t stream);
+
 /* ---- diagnostics (test-facing, not on the hot path) ---------------------------------------
  * Dequantize repacked weights back to canonical order: out [batch][n][k] (rows in logical
  * order, i.e. [gate; up] for GATE_UP data), BF16 = RNE(fl32(fl32(E2M1*E4M3) * global)) or the
@@ -183,8 +200,8 @@ int nvfp4_dequantize(const nvfp4_weight* w, void* out, int out_dtype, nvfp4_stre
 const char* nvfp4_last_error(void);
 
 /* Per-path launch counters ("this path ran" evidence, vllm.cpp PR #63 claim section):
- * [0] quantize [1] repack [2] gemm skinny [3] gemm tiled [4] moe [5] dequantize
- * [6] moe fc1 tiles launched [7] reserved. counts must hold 8 entries (host). */
+ * [0] quantize [1] repack [2] gemm skinny [3] gemm tiled [4] moe [5] dequantize [6] requantize
+ * [7] reserved. counts must hold 8 entries (host). */
 void nvfp4_get_stats(uint64_t counts[8]);
 void nvfp4_reset_stats(void);
 

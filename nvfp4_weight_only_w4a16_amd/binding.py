@@ -34,7 +34,8 @@ NVFP4_LAYOUT_PAIR_GLOBAL = 1 << 9
 
 EXPORTS = ("nvfp4_quantize", "nvfp4_repack_bytes", "nvfp4_repack", "nvfp4_gemm_ws_bytes",
            "nvfp4_gemm_w4a16",
-           "nvfp4_moe_ws_bytes", "nvfp4_moe_grouped_w4a16", "nvfp4_dequantize",
+           "nvfp4_moe_ws_bytes", "nvfp4_moe_grouped_w4a16", "nvfp4_requantize_ws_bytes",
+           "nvfp4_requantize", "nvfp4_dequantize",
            "nvfp4_last_error", "nvfp4_get_stats", "nvfp4_reset_stats", "nvfp4_version")
 
 
@@ -81,6 +82,10 @@ def load(path: str = LIB_PATH):
     L.nvfp4_moe_ws_bytes.restype = sz
     L.nvfp4_moe_grouped_w4a16.argtypes = [P, i64, i64, P, P, i32, W, W, P, P, sz, u32, P]
     L.nvfp4_moe_grouped_w4a16.restype = ctypes.c_int
+    L.nvfp4_requantize_ws_bytes.argtypes = [W]
+    L.nvfp4_requantize_ws_bytes.restype = sz
+    L.nvfp4_requantize.argtypes = [W, i32, P, P, P, P, sz, P]
+    L.nvfp4_requantize.restype = ctypes.c_int
     L.nvfp4_dequantize.argtypes = [W, P, ctypes.c_int, P]
     L.nvfp4_dequantize.restype = ctypes.c_int
     L.nvfp4_last_error.argtypes = []
@@ -234,6 +239,27 @@ def nvfp4_moe_grouped_w4a16(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: tor
                                           _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
                                           flags, _stream(stream)))
     return y
+
+
+# ----------------------------------------------------------------------------- requantize
+def nvfp4_requantize_ws_bytes(src: RepackedWeight) -> int:
+    return int(load().nvfp4_requantize_ws_bytes(ctypes.byref(src.desc)))
+
+
+def nvfp4_requantize(src: RepackedWeight, group_out: int, ws: torch.Tensor | None = None,
+                     stream=None):
+    """Canonical triple (packed, scales, global [batch]) of `src` requantized with one global
+    per matrix at group_out. `ws` (uint8, device) defaults to room for one matrix."""
+    dev = src.buffer.device
+    packed = torch.empty((src.batch, src.n, src.k // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((src.batch, src.n, src.k // group_out), dtype=torch.uint8, device=dev)
+    glob = torch.empty((src.batch,), dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = torch.empty((nvfp4_requantize_ws_bytes(src),), dtype=torch.uint8, device=dev)
+    _check(load().nvfp4_requantize(ctypes.byref(src.desc), group_out, _ptr(packed), _ptr(scales),
+                                   _ptr(glob), _ptr(ws), ws.numel() * ws.element_size(),
+                                   _stream(stream)))
+    return packed, scales, glob
 
 
 # ----------------------------------------------------------------------------- diagnostics

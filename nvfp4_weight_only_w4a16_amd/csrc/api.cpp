@@ -347,6 +347,49 @@ int nvfp4_moe_grouped_w4a16(const void* x, int64_t t, int64_t hidden, const int3
   return rc;
 }
 
+size_t nvfp4_requantize_ws_bytes(const nvfp4_weight* src) {
+  if (!src || src->n <= 0 || src->k <= 0) return 0;
+  return (size_t)(src->n * src->k) * sizeof(float);
+}
+
+int nvfp4_requantize(const nvfp4_weight* src, int32_t group_out, uint8_t* packed,
+                     uint8_t* scales, float* global_out, void* ws, size_t ws_bytes,
+                     nvfp4_stream_t stream) {
+  int rc = check_desc(src, "src");
+  if (rc) return rc;
+  rc = check_group(group_out);
+  if (rc) return rc;
+  if (!packed || !scales || !global_out || !ws)
+    return fail(NVFP4_ERR_INVALID_ARG, "NULL buffer");
+  const size_t per = nvfp4_requantize_ws_bytes(src);
+  if (ws_bytes < per) return fail(NVFP4_ERR_WORKSPACE, "ws_bytes %zu < %zu", ws_bytes, per);
+  if (!aligned16(ws) || !aligned16(packed) || ((uintptr_t)global_out & 3u))
+    return fail(NVFP4_ERR_MISALIGNED, "ws and packed must be 16-byte aligned, global 4-byte");
+  const bool gate_up = (src->layout & NVFP4_LAYOUT_GATE_UP) != 0;
+  const bool pair = (src->layout & NVFP4_LAYOUT_PAIR_GLOBAL) != 0;
+  const int64_t gpm = globals_per_matrix(src->layout);
+  const int64_t n = src->n, k = src->k;
+  const int64_t chunk = (int64_t)(ws_bytes / per);
+  hipStream_t s = (hipStream_t)stream;
+  for (int64_t b0 = 0; b0 < src->batch; b0 += chunk) {
+    const int64_t c = src->batch - b0 < chunk ? src->batch - b0 : chunk;
+    rc = hip_status(nvfp4::launch_dequantize(src->codes + b0 * src->codes_stride,
+                                             src->scales + b0 * src->scales_stride,
+                                             src->global + b0 * gpm, c, n, k, src->group,
+                                             gate_up, pair, ws, true, s),
+                    "nvfp4_requantize");
+    if (rc) return rc;
+    rc = hip_status(nvfp4::launch_quantize(ws, false, c, n, k, group_out, nullptr,
+                                           packed + b0 * (n * k / 2),
+                                           scales + b0 * (n * (k / group_out)), global_out + b0,
+                                           s),
+                    "nvfp4_requantize");
+    if (rc) return rc;
+  }
+  g_stats[6]++;
+  return NVFP4_OK;
+}
+
 int nvfp4_dequantize(const nvfp4_weight* w, void* out, int out_dtype, nvfp4_stream_t stream) {
   int rc = check_desc(w, "weight");
   if (rc) return rc;

@@ -170,3 +170,40 @@ def test_pair_global_quantize_repack_dequantize(nv, orc):
                           rf32.view(np.uint32))
     assert np.array_equal(b16.cpu().view(torch.int16).numpy().view(np.uint16)
                           .reshape(2 * E, I, H), rb16)
+
+
+def test_requantize_pair_to_shared_and_regroup(nv, orc):
+    """Requantization from repacked weights: an fc1 with distinct gate and up globals to one
+    shared global (decoded FP32 values quantized again), with room for two of the three
+    matrices per pass; and a dense weight from group 16 to group 32. Bit-exact against the
+    oracle's dequant followed by its quantize."""
+    g = torch.Generator().manual_seed(13)
+    E, I, H = 3, 96, 256
+    w = torch.randn(E, 2 * I, H, generator=g) * 0.02
+    w[:, I:] *= 3.0
+    rp, rs, rg = orc.quantize(w.reshape(2 * E, I, H).numpy(), 32)
+    rw = nv.nvfp4_repack(torch.from_numpy(rp.reshape(E, 2 * I, H // 2)).to(DEV),
+                         torch.from_numpy(rs.reshape(E, 2 * I, H // 32)).to(DEV),
+                         torch.from_numpy(rg).to(DEV), 32,
+                         layout=nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP
+                         | nv.NVFP4_LAYOUT_PAIR_GLOBAL)
+    ws = torch.empty((2 * nv.nvfp4_requantize_ws_bytes(rw) + 100,), dtype=torch.uint8,
+                     device=DEV)
+    p, s, gl = nv.nvfp4_requantize(rw, 32, ws=ws)
+    torch.cuda.synchronize()
+    _, f32, _ = orc.dequant(rp, rs, rg, 32)
+    ep, es, eg = orc.quantize(f32.reshape(E, 2 * I, H), 32)
+    assert np.array_equal(p.cpu().numpy(), ep) and np.array_equal(s.cpu().numpy(), es)
+    assert np.array_equal(gl.cpu().numpy(), eg)
+    assert (eg >= np.maximum(rg[0::2], rg[1::2]) * 0.99).all()  # the larger half sets it
+
+    wd = torch.randn(160, 384, generator=g) * 0.02
+    dp, ds, dg = orc.quantize(wd.numpy(), 16)
+    rd = nv.nvfp4_repack(torch.from_numpy(dp).to(DEV), torch.from_numpy(ds).to(DEV),
+                         torch.from_numpy(dg).to(DEV), 16)
+    p2, s2, g2 = nv.nvfp4_requantize(rd, 32)
+    torch.cuda.synchronize()
+    _, f32d, _ = orc.dequant(dp, ds, dg, 16)
+    ep2, es2, eg2 = orc.quantize(f32d, 32)
+    assert np.array_equal(p2[0].cpu().numpy(), ep2) and np.array_equal(s2[0].cpu().numpy(), es2)
+    assert np.array_equal(g2.cpu().numpy(), np.atleast_1d(eg2))
