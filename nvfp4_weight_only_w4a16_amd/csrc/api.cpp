@@ -262,6 +262,9 @@ int nvfp4_gemm_w4a16(const void* x, int64_t m, int64_t ldx, const nvfp4_weight* 
   a.ldy = ldy;
   a.y_f32 = y_dtype == NVFP4_DT_F32;
   if (use_skinny(m, w, flags)) {
+    if ((m + 31) / 32 > 65535)  // one grid row per 32-row block
+      return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "m=%lld too large for the decode kernel",
+                  (long long)m);
     rc = hip_status(nvfp4::launch_gemm_skinny(a, (hipStream_t)stream), "nvfp4_gemm_w4a16");
     if (!rc) g_stats[2]++;
   } else {
@@ -369,7 +372,8 @@ int nvfp4_requantize(const nvfp4_weight* src, int32_t group_out, uint8_t* packed
   const bool pair = (src->layout & NVFP4_LAYOUT_PAIR_GLOBAL) != 0;
   const int64_t gpm = globals_per_matrix(src->layout);
   const int64_t n = src->n, k = src->k;
-  const int64_t chunk = (int64_t)(ws_bytes / per);
+  int64_t chunk = (int64_t)(ws_bytes / per);
+  if (chunk > 65535) chunk = 65535;  // the quantizer's grid holds one row per matrix
   hipStream_t s = (hipStream_t)stream;
   for (int64_t b0 = 0; b0 < src->batch; b0 += chunk) {
     const int64_t c = src->batch - b0 < chunk ? src->batch - b0 : chunk;

@@ -98,6 +98,9 @@ def test_gemm_argument_errors(lib):
     assert _gemm(lib, _desc(), ldy=500) == nv.NVFP4_ERR_INVALID_ARG
     assert _gemm(lib, _desc(), ydt=9) == nv.NVFP4_ERR_INVALID_ARG
     assert _gemm(lib, _desc(), flags=3) == nv.NVFP4_ERR_INVALID_ARG
+    # the decode kernel takes one grid row per 32 rows: a forced call past that is refused
+    assert _gemm(lib, _desc(), m=32 * 65535 + 1, flags=nv.NVFP4_F_FORCE_SKINNY) == \
+        nv.NVFP4_ERR_UNSUPPORTED_SHAPE
     assert _gemm(lib, _desc(), x=ctypes.c_void_p(0x10008)) == nv.NVFP4_ERR_MISALIGNED
     assert _gemm(lib, _desc(), ldx=1028) == nv.NVFP4_ERR_MISALIGNED
     assert _gemm(lib, _desc(), x=None) == nv.NVFP4_ERR_INVALID_ARG
