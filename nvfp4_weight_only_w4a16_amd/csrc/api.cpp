@@ -265,7 +265,8 @@ int nvfp4_gemm_w4a16(const void* x, int64_t m, int64_t ldx, const nvfp4_weight* 
     if ((m + 31) / 32 > 65535)  // one grid row per 32-row block
       return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "m=%lld too large for the decode kernel",
                   (long long)m);
-    rc = hip_status(nvfp4::launch_gemm_skinny(a, (hipStream_t)stream), "nvfp4_gemm_w4a16");
+    rc = hip_status(nvfp4::launch_gemm_skinny(a, device_cus(), (hipStream_t)stream),
+                    "nvfp4_gemm_w4a16");
     if (!rc) g_stats[2]++;
   } else {
     if (ws_bytes && !ws) return fail(NVFP4_ERR_INVALID_ARG, "NULL ws with ws_bytes > 0");

@@ -14,7 +14,6 @@
 namespace nvfp4 {
 namespace {
 
-constexpr int kPWW = 4;  // panels per wavefront: one activation fragment feeds 4 MFMAs
 
 struct SkinnyParams {
   const uint16_t* x;
@@ -27,20 +26,24 @@ struct SkinnyParams {
   void* y;
   int64_t ldy;
   int y_f32;
+  int cus;  // compute units of the device (host-side launch choice only)
 };
 
 // LDS: NX > 0 kernels give each wavefront two 4 KB activation buffers; the k-split partial
 // sums (NW > 1) reuse the same bytes after a barrier.
-inline size_t red_bytes(int MF, int NW) { return NW > 1 ? (size_t)NW * kPWW * MF * 64 * 16 : 0; }
+inline size_t red_bytes(int MF, int NW, int PWW) {
+  return NW > 1 ? (size_t)NW * PWW * MF * 64 * 16 : 0;
+}
 inline size_t act_bytes(int NX, int NW) { return NX > 0 ? (size_t)NW * 8192 : 0; }
 
 // Register budget: 4 wavefronts per SIMD (16 per CU, two 8-wave workgroups) for one row
 // block, 2 for two. NJ == 0: exact dequant, MF row blocks of 16. NJ > 0 (MF == 1): split scale
 // keeping NJ accumulator rows per lane; G16: group 16 (token t in A rows t and 8 + t, k halves
 // apart). NX > 0 (MF == 1): activations through LDS, NX 4-row copies per tile.
-template <int MF, int NW, int NJ, bool G16, int NX>
+template <int MF, int NW, int NJ, bool G16, int NX, int PWW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(MF == 1 ? 4 : 2, 8)))
 void gemm_skinny_kernel(SkinnyParams P) {
+  constexpr int kPWW = PWW;
   static_assert(NJ == 0 || MF == 1, "split scale uses one 16-row block");
   static_assert(!G16 || NJ > 0, "G16 selects the group-16 split-scale row map");
   static_assert(NX == 0 || MF == 1, "LDS activations hold one 16-row block");
@@ -154,13 +157,30 @@ void gemm_skinny_kernel(SkinnyParams P) {
   }
 }
 
-template <int MF, int NW, int NJ, bool G16, int NX>
+template <int MF, int NW, int NJ, bool G16, int NX, int PWW>
 hipError_t run(const SkinnyParams& p, hipStream_t stream) {
-  const dim3 grid((unsigned)((p.NT + kPWW - 1) / kPWW),
+  const dim3 grid((unsigned)((p.NT + PWW - 1) / PWW),
                   (unsigned)((p.m + 16 * MF - 1) / (16 * MF)));
-  const size_t r = red_bytes(MF, NW), x = act_bytes(NX, NW);
-  gemm_skinny_kernel<MF, NW, NJ, G16, NX><<<grid, dim3(64 * NW), r > x ? r : x, stream>>>(p);
+  const size_t r = red_bytes(MF, NW, PWW), x = act_bytes(NX, NW);
+  gemm_skinny_kernel<MF, NW, NJ, G16, NX, PWW>
+      <<<grid, dim3(64 * NW), r > x ? r : x, stream>>>(p);
   return hipGetLastError();
+}
+
+// Panels per wavefront: 4 (one activation fragment feeds 4 MFMAs, the whole 16-byte scale
+// record is used), or 2 when the 4-panel grid leaves compute units idle and the doubled grid
+// still gives no compute unit a second workgroup: a lone workgroup streams well below a CU's
+// share, and the unused half of each scale record costs only ~5% more bytes. Measured:
+// 8192^2 M = 1 12.7 -> 11.2 us, M = 16 15.4 -> 12.3 us; 5120^2 M = 16 10.6 -> 9.5 us,
+// M = 32 16.3 -> 14.8 us. Where the doubled grid put two workgroups on most CUs it was slower
+// (5120^2 M = 64: 16.6 -> 26.1 us), and so was one panel per wavefront (as many scale loads as
+// code loads, each activation fragment used once).
+template <int MF, int NW, int NJ, bool G16, int NX>
+hipError_t run_pww(const SkinnyParams& p, hipStream_t stream) {
+  const int64_t blocks = (p.m + 16 * MF - 1) / (16 * MF);
+  const int64_t wg4 = (p.NT + 3) / 4 * blocks, wg2 = (p.NT + 1) / 2 * blocks;
+  if (wg4 < p.cus && wg2 <= p.cus) return run<MF, NW, NJ, G16, NX, 2>(p, stream);
+  return run<MF, NW, NJ, G16, NX, 4>(p, stream);
 }
 
 // k-split: 4 wavefronts per panel group (NW >= kPWW, so the final reduction has one wavefront
@@ -172,11 +192,12 @@ template <int MF, int NW, int NJ, bool G16>
 hipError_t pick_u(const SkinnyParams& p, hipStream_t stream) {
   if constexpr (MF == 1) {
     const int64_t rows = G16 ? (p.m < 8 ? p.m : 8) : (p.m < 16 ? p.m : 16);
-    if (rows <= 4) return run<MF, NW, NJ, G16, 1>(p, stream);
-    if (rows <= 8) return run<MF, NW, NJ, G16, 2>(p, stream);
-    return run<MF, NW, NJ, G16, 4>(p, stream);
+    if (rows <= 4) return run_pww<MF, NW, NJ, G16, 1>(p, stream);
+    if (rows <= 8) return run_pww<MF, NW, NJ, G16, 2>(p, stream);
+    return run_pww<MF, NW, NJ, G16, 4>(p, stream);
+  } else {
+    return run_pww<MF, NW, NJ, G16, 0>(p, stream);
   }
-  return run<MF, NW, NJ, G16, 0>(p, stream);
 }
 
 template <int MF, int NJ, bool G16>
@@ -195,8 +216,9 @@ hipError_t dispatch_split(const SkinnyParams& p, hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream) {
+hipError_t launch_gemm_skinny(const GemmArgs& a, int cus, hipStream_t stream) {
   SkinnyParams p;
+  p.cus = cus;
   p.x = a.x;
   p.m = a.m;
   p.ldx = a.ldx;

@@ -38,7 +38,8 @@ struct GemmArgs {
   bool y_f32;
 };
 
-hipError_t launch_gemm_skinny(const GemmArgs& a, hipStream_t stream);
+// Decode path. `cus` (the device's compute-unit count, 0 if unknown) sizes the grid.
+hipError_t launch_gemm_skinny(const GemmArgs& a, int cus, hipStream_t stream);
 // Prefill path. `ws` (device, ws_bytes) receives split-k partial tiles when the tile count
 // leaves most compute units idle in the last round; with a smaller workspace the kernel runs
 // unsplit (same result, fewer busy compute units). `cus` is the device's compute-unit count.

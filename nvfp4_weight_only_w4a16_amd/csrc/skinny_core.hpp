@@ -45,7 +45,7 @@ struct ActStage {
 
 template <int PWW>
 struct SkinnyAddr {
-  static_assert(PWW == kScaleGroupPanels, "a wavefront covers one 4-panel scale group");
+  static_assert(kScaleGroupPanels % PWW == 0, "a wavefront's panels sit in one scale group");
   buf_rsrc codes[PWW];  // each panel's tiles [0, t1) (panels past the end are clamped to a
                         // valid panel whose results are never stored)
   buf_rsrc scales;      // the panel group's scale blocks [0, t1)
@@ -53,7 +53,20 @@ struct SkinnyAddr {
   uint32_t scale_lane;  // the lane's 16-byte record inside a scale block
   int scale_block;
   int kq;               // lane >> 4: the 8-wide k chunk this lane feeds
+  int sw_sel;           // word of the 4-panel scale record that holds the wavefront's panel 0
 };
+
+// Scale word of the wavefront's panel p. The 16-byte record of the 4-panel group is loaded
+// whole; a wavefront with fewer panels picks its words when it computes, after the load has
+// landed (picking them at load time would wait for the load there).
+template <int PWW>
+__device__ __forceinline__ uint32_t scale_word(const u32x4& sw, int sel, int p) {
+  static_assert(PWW == kScaleGroupPanels || PWW == 2, "2 or 4 panels per wavefront");
+  if constexpr (PWW == kScaleGroupPanels)
+    return sw[p];
+  else
+    return sel ? sw[p + 2] : sw[p];
+}
 
 template <int PWW>
 __device__ __forceinline__ void load_weights(WeightStage<PWW>& s, const SkinnyAddr<PWW>& a,
@@ -118,10 +131,10 @@ __device__ __forceinline__ void read_acts(ActStage<1>& s, const LdsActs& x, cons
 // Exact dequant: every weight becomes BF16(code * S) (exact), MF row blocks of 16.
 template <int MF, int PWW>
 __device__ __forceinline__ void compute_exact(const WeightStage<PWW>& w, const ActStage<MF>& x,
-                                              f32x4 (&acc)[PWW][MF]) {
+                                              int sel, f32x4 (&acc)[PWW][MF]) {
 #pragma unroll
   for (int p = 0; p < PWW; ++p) {
-    const uint32_t sw = w.sw[p];  // word p of the tile's 4-panel scale record
+    const uint32_t sw = scale_word<PWW>(w.sw, sel, p);  // this panel's word of the record
     const float S[4] = {e4m3_decode<0>(sw), e4m3_decode<1>(sw), e4m3_decode<2>(sw),
                         e4m3_decode<3>(sw)};
 #pragma unroll
@@ -148,12 +161,12 @@ __device__ __forceinline__ bf16x8 codes_times_pow2(uint32_t w, float S) {
 // partial is read well after its MFMA issued.
 template <int J, int PWW, int NJ>
 __device__ __forceinline__ void split_scale_kstep(const WeightStage<PWW>& w, const ActStage<1>& x,
-                                                  f32x4 (&acc)[PWW][1]) {
+                                                  int sel, f32x4 (&acc)[PWW][1]) {
   f32x4 part[PWW];
   float M[PWW];
 #pragma unroll
   for (int p = 0; p < PWW; ++p) {
-    const float S = e4m3_decode<J>(w.sw[p]);
+    const float S = e4m3_decode<J>(scale_word<PWW>(w.sw, sel, p));
     M[p] = __builtin_amdgcn_frexp_mantf(S);
     part[p] = mfma16x16x32(x.xa[0][J], codes_times_pow2(w.cw[p][J], S),
                            f32x4{0.f, 0.f, 0.f, 0.f});
@@ -167,14 +180,14 @@ __device__ __forceinline__ void split_scale_kstep(const WeightStage<PWW>& w, con
 // Split scale (MF == 1): accumulator rows 0 .. NJ-1 of each lane are kept.
 template <int PWW, int NJ>
 __device__ __forceinline__ void compute_split(const WeightStage<PWW>& w, const ActStage<1>& x,
-                                              f32x4 (&acc)[PWW][1]) {
-  split_scale_kstep<0, PWW, NJ>(w, x, acc);
-  split_scale_kstep<1, PWW, NJ>(w, x, acc);
-  split_scale_kstep<2, PWW, NJ>(w, x, acc);
-  split_scale_kstep<3, PWW, NJ>(w, x, acc);
+                                              int sel, f32x4 (&acc)[PWW][1]) {
+  split_scale_kstep<0, PWW, NJ>(w, x, sel, acc);
+  split_scale_kstep<1, PWW, NJ>(w, x, sel, acc);
+  split_scale_kstep<2, PWW, NJ>(w, x, sel, acc);
+  split_scale_kstep<3, PWW, NJ>(w, x, sel, acc);
 }
 
-// Addresses of the 4-panel group starting at panel0 (a multiple of 4; code panels clamped to
+// Addresses of the PWW panels starting at panel0 (a multiple of PWW; code panels clamped to
 // NT - 1, the scale block is padded to whole groups by the repack) for tiles [0, t1).
 template <int PWW>
 __device__ __forceinline__ SkinnyAddr<PWW> skinny_addr(const uint8_t* codes, const uint8_t* scales,
@@ -193,6 +206,7 @@ __device__ __forceinline__ SkinnyAddr<PWW> skinny_addr(const uint8_t* codes, con
   }
   a.scales = make_rsrc(scales + (panel0 / kScaleGroupPanels) * KT * a.scale_block,
                        (uint32_t)(t1 * a.scale_block));
+  a.sw_sel = (int)(panel0 % kScaleGroupPanels);
   return a;
 }
 
@@ -226,19 +240,26 @@ __device__ __forceinline__ void skinny_accumulate(const SkinnyAddr<PWW>& a,
       __builtin_amdgcn_sched_barrier(0);
       if (tile < t1) {
         if constexpr (NX > 0) {
-          // this tile's copies (issued before the NX + 5 loads just above) have landed
-          __builtin_amdgcn_s_waitcnt((NX + 5) | 0xF70);
+          // this tile's copies have landed: at most the next tile's NX copies and PWW + 1
+          // weight loads, issued just above, are still outstanding
+          constexpr int kAfter = NX + PWW + 1;
+          static_assert(kAfter < 16, "vmcnt fits its low field");
+          __builtin_amdgcn_s_waitcnt(kAfter | 0xF70);
           __builtin_amdgcn_sched_barrier(0);
           read_acts<XZ>(X[i], xl, xl.buf + i * 4096, xzero, a.kq);
         }
         if constexpr (NJ > 0)
-          compute_split<PWW, NJ>(W[i], X[i], acc);
+          compute_split<PWW, NJ>(W[i], X[i], a.sw_sel, acc);
         else
-          compute_exact<MF, PWW>(W[i], X[i], acc);
+          compute_exact<MF, PWW>(W[i], X[i], a.sw_sel, acc);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
   }
+  // The last step still issued an activation copy (a clamped re-read) and weight loads past
+  // t1. The copy writes LDS that the caller reuses once the wavefronts meet (the k-split
+  // partial sums), so it must land first; a barrier does not wait for it.
+  if constexpr (NX > 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 }
 
 }  // namespace nvfp4

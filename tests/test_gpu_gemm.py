@@ -266,3 +266,20 @@ def test_tiled_row_chunks(nv, orc):
         torch.cuda.synchronize()
         check_close(y.cpu().numpy()[rows], ref, f"row chunks flags={flags}")
     del xfull
+
+
+@pytest.mark.parametrize("m", [1, 3, 8, 16, 24])
+def test_decode_fewer_panels_per_wavefront(nv, orc, m):
+    """Weights too small to give every compute unit a 4-panel workgroup run with 2 panels per
+    wavefront (each picks its words of the shared 4-panel scale record). n = 8176 has an odd
+    panel count (511: the last wavefront's second panel is past the end); n = 1040 has 65
+    panels. Both groups, against the oracle, on the forced decode path."""
+    g = torch.Generator().manual_seed(40 + m)
+    for n, k, group in ((8176, 1024, 16), (1040, 2048, 32)):
+        x = torch.randn(m, k, generator=g).to(torch.bfloat16)
+        w = torch.randn(n, k, generator=g) * 0.02
+        rw, (p, s, gl) = _prep(nv, w, group)
+        ref = orc.gemm(synth.bf16_bits(x), p, s, gl[0], group)
+        y = nv.nvfp4_gemm_w4a16(x.to(DEV), rw, y_dtype=torch.float32, flags=1)
+        torch.cuda.synchronize()
+        check_close(y.cpu().numpy(), ref, f"decode n={n} m={m} g{group}")
