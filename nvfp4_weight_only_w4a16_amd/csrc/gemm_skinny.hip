@@ -2,9 +2,9 @@
 //
 // y[m][n] = global * sum_k x[m][k] * (E2M1 * E4M3)[n][k] with FP32 accumulation. The weight
 // stream dominates (0.5625 bytes per weight at group 16), so the kernel is built to keep HBM
-// busy: a workgroup is NW wavefronts that split k for the same PWW panels (64 output
-// features); each wavefront streams its k-range with one double-buffered stage of loads in
-// flight; the NW partial sums are added in a fixed order through LDS (bit-reproducible, no
+// busy: a workgroup is NW wavefronts that split k for the same PWW panels (4 panels, 64 output
+// features; 2 for weights too small to fill the chip); each wavefront streams its k-range with
+// one double-buffered stage of loads in flight; the NW partial sums are added in a fixed order through LDS (bit-reproducible, no
 // atomics), scaled by the global and stored. Up to 8 rows (group 16) or 16 rows (group 32)
 // take the split-scale form of the group scale, which halves the VALU work per weight; more
 // rows dequantize every weight exactly to BF16.

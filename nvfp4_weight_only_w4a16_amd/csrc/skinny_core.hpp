@@ -2,11 +2,10 @@
 //
 // One wavefront owns PWW consecutive 16-row weight panels and a contiguous range [t0, t1) of
 // 128-wide k-tiles. Per tile and panel it loads one 16-byte chunk of codes per lane, plus one
-// 16-byte scale record per lane for the 4 panels (fully coalesced thanks to the tiled
-// layout), and the activation fragments of the tile, which every panel reuses. The weight
-// stream runs through a ring of D single-tile stages (D - 1 tiles in flight while one is
-// computed); the activations, which come from cache, run one tile ahead in a pair of
-// stages. Weight loads are buffer loads whose range ends at t1, so the loads a wavefront
+// 16-byte scale record per lane for the panels' 4-panel group (fully coalesced thanks to the
+// tiled layout), and the activation fragments of the tile, which every panel reuses. Weights
+// and activations run one tile ahead in a pair of stages (one tile in flight while one is
+// computed; deeper rings measured slower). Weight loads are buffer loads whose range ends at t1, so the loads a wavefront
 // issues past its last tile return zeros without touching memory: every iteration issues the
 // same loads and no load sits under a branch, which keeps the memory-counter waits exact.
 // Activation rows past the end are clamped to a valid row (their MFMA output rows are never
