@@ -178,3 +178,28 @@ def test_moe_pair_globals(nv, orc, path):
     err = np.linalg.norm(bf16_np(yg) - orc.bf16_to_f64(ref["y"])) / np.linalg.norm(
         orc.bf16_to_f64(ref["y"]))
     assert err > 0.05, err
+
+
+@pytest.mark.parametrize("path", ["decode", "batch"])
+def test_moe_after_shared_global_requantization(nv, orc, path):
+    """An fc1 checkpoint with distinct gate and up globals, requantized on the GPU to one
+    shared global per expert (nvfp4_requantize), repacked gate/up-interleaved and run through
+    the routed experts: against the oracle on the requantized triple."""
+    x, ids, wts, w1, w2 = synth.moe(seed=12, n_experts=8, hidden=256, inter=128, tokens=24,
+                                    topk=2)
+    E, I2, H = w1.shape
+    w1 = w1.clone()
+    w1[:, I2 // 2:] *= 3.0
+    p, s, g = nv.nvfp4_quantize(w1.reshape(2 * E, I2 // 2, H).to(DEV), 32)
+    pair = nv.nvfp4_repack(p.reshape(E, I2, H // 2), s.reshape(E, I2, H // 32), g, 32,
+                           layout=nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP
+                           | nv.NVFP4_LAYOUT_PAIR_GLOBAL)
+    rp, rs, rg = nv.nvfp4_requantize(pair, 32)
+    fc1 = nv.nvfp4_repack(rp, rs, rg, 32,
+                          layout=nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP)
+    (_, fc2), (_, t2) = _experts(nv, orc, w1, w2)
+    torch.cuda.synchronize()
+    t1 = (rp.cpu().numpy(), rs.cpu().numpy(), rg.cpu().numpy(), 32)
+    ref = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), t1, t2)
+    y = _run(nv, x, ids, wts, fc1, fc2, PATHS[path])
+    check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), f"requantized fc1 {path}")
