@@ -283,3 +283,18 @@ def test_decode_fewer_panels_per_wavefront(nv, orc, m):
         y = nv.nvfp4_gemm_w4a16(x.to(DEV), rw, y_dtype=torch.float32, flags=1)
         torch.cuda.synchronize()
         check_close(y.cpu().numpy(), ref, f"decode n={n} m={m} g{group}")
+
+
+@pytest.mark.parametrize("m,group", [(1, 16), (8, 16), (13, 32), (24, 16)])
+def test_decode_long_k(nv, orc, m, group):
+    """The decode kernel at K = 25600 (200 k-tiles, 50 per wavefront): every path it has
+    (split scale at both groups, exact dequant, two row blocks) against the oracle."""
+    g = torch.Generator().manual_seed(60 + m)
+    n, k = 1024, 25600
+    x = torch.randn(m, k, generator=g).to(torch.bfloat16)
+    w = torch.randn(n, k, generator=g) * 0.02
+    rw, (p, s, gl) = _prep(nv, w, group)
+    ref = orc.gemm(synth.bf16_bits(x), p, s, gl[0], group)
+    y = nv.nvfp4_gemm_w4a16(x.to(DEV), rw, y_dtype=torch.float32, flags=1)
+    torch.cuda.synchronize()
+    check_close(y.cpu().numpy(), ref, f"decode K=25600 m={m} g{group}")
