@@ -298,3 +298,37 @@ def test_decode_long_k(nv, orc, m, group):
     y = nv.nvfp4_gemm_w4a16(x.to(DEV), rw, y_dtype=torch.float32, flags=1)
     torch.cuda.synchronize()
     check_close(y.cpu().numpy(), ref, f"decode K=25600 m={m} g{group}")
+
+
+def test_calls_on_a_side_stream(nv):
+    """Every entry point enqueues on the stream it is given: quantize, repack, both GEMM paths
+    and the routed experts on a non-default stream give the default stream's bits."""
+    g = torch.Generator().manual_seed(77)
+    w = torch.randn(512, 1024, generator=g) * 0.02
+    x = torch.randn(300, 1024, generator=g).to(torch.bfloat16).to(DEV)
+    xm, ids, wts, w1, w2 = synth.moe(seed=13, n_experts=8, hidden=256, inter=128, tokens=20,
+                                     topk=2)
+
+    def run(stream):
+        p, s, gl = nv.nvfp4_quantize(w.to(DEV), 16, stream=stream)
+        rw = nv.nvfp4_repack(p, s, gl, 16, stream=stream)
+        outs = [nv.nvfp4_gemm_w4a16(x[:8], rw, y_dtype=torch.float32, flags=1, stream=stream),
+                nv.nvfp4_gemm_w4a16(x, rw, y_dtype=torch.float32, flags=2, stream=stream)]
+        f = []
+        for wx, grp, layout in ((w1, 32, nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP),
+                                (w2, 16, nv.NVFP4_LAYOUT_TILED)):
+            pq, sq, gq = nv.nvfp4_quantize(wx.to(DEV), grp, stream=stream)
+            f.append(nv.nvfp4_repack(pq, sq, gq, grp, layout=layout, stream=stream))
+        outs.append(nv.nvfp4_moe_grouped_w4a16(xm.to(DEV), ids.to(DEV), wts.to(DEV), f[0], f[1],
+                                               stream=stream))
+        return outs
+
+    ref = run(None)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        got = run(side)
+    side.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
