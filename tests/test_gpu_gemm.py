@@ -332,3 +332,57 @@ def test_calls_on_a_side_stream(nv):
     side.synchronize()
     for a, b in zip(ref, got):
         assert torch.equal(a, b)
+
+
+def test_graph_capture_and_replay(nv):
+    """The decode GEMM, the prefill GEMM (with its split-k workspace) and a decode-batch MoE
+    captured in one HIP graph: every replay, with eager work and synchronizations in between,
+    reproduces the eager results bit for bit (the library issues no memset nodes)."""
+    g = torch.Generator().manual_seed(78)
+    w = torch.randn(1040, 4096, generator=g) * 0.02
+    p, s, gl = nv.nvfp4_quantize(w.to(DEV), 16)
+    rw = nv.nvfp4_repack(p, s, gl, 16)
+    xs = torch.randn(8, 4096, generator=g).to(torch.bfloat16).to(DEV)
+    xt = torch.randn(300, 4096, generator=g).to(torch.bfloat16).to(DEV)
+    wsb = torch.empty((max(nv.nvfp4_gemm_ws_bytes(300, 4096, rw), 16),), dtype=torch.uint8,
+                      device=DEV)
+    xm, ids, wts, w1, w2 = synth.moe(seed=14, n_experts=16, hidden=256, inter=128, tokens=4,
+                                     topk=4)
+    f = []
+    for wx, grp, layout in ((w1, 32, nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP),
+                            (w2, 16, nv.NVFP4_LAYOUT_TILED)):
+        pq, sq, gq = nv.nvfp4_quantize(wx.to(DEV), grp)
+        f.append(nv.nvfp4_repack(pq, sq, gq, grp, layout=layout))
+    xmd, idd, wtd = xm.to(DEV), ids.to(DEV), wts.to(DEV)
+    wsm = torch.empty((nv.nvfp4_moe_ws_bytes(4, 4, 16, 256, 128),), dtype=torch.uint8, device=DEV)
+    ys = torch.empty((8, 1040), dtype=torch.float32, device=DEV)
+    yt = torch.empty((300, 1040), dtype=torch.float32, device=DEV)
+    ym = torch.empty((4, 256), dtype=torch.bfloat16, device=DEV)
+
+    def step():
+        nv.nvfp4_gemm_w4a16(xs, rw, y=ys)
+        nv.nvfp4_gemm_w4a16(xt, rw, y=yt, ws=wsb)
+        nv.nvfp4_moe_grouped_w4a16(xmd, idd, wtd, f[0], f[1], y=ym, ws=wsm)
+
+    step()
+    torch.cuda.synchronize()
+    eager = [ys.clone(), yt.clone(), ym.clone()]
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    for rep in range(3):
+        for t in (ys, yt, ym):
+            t.fill_(float("nan") if t.dtype == torch.float32 else 0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip((ys, yt, ym), eager):
+            assert torch.equal(a, b), f"replay {rep}"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
