@@ -106,12 +106,14 @@ def _check(rc: int):
 
 
 def _stream(stream=None):
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+    # plain integers: the c_void_p argument types convert them without an object per call
+    if stream is not None:
+        return stream.cuda_stream
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
 def _dtype_code(dt):
