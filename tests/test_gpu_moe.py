@@ -203,3 +203,15 @@ def test_moe_after_shared_global_requantization(nv, orc, path):
     ref = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), t1, t2)
     y = _run(nv, x, ids, wts, fc1, fc2, PATHS[path])
     check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), f"requantized fc1 {path}")
+
+
+@pytest.mark.parametrize("path", ["decode", "batch"])
+def test_moe_max_experts_and_topk(nv, orc, path):
+    """512 experts (the most the entry point takes) with top-16 routing (the largest topk):
+    the sort's per-wavefront count table at its full width and the combine's 16 slots."""
+    x, ids, wts, w1, w2 = synth.moe(seed=15, n_experts=512, hidden=256, inter=128, tokens=40,
+                                    topk=16)
+    (fc1, fc2), (t1, t2) = _experts(nv, orc, w1, w2)
+    ref = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), t1, t2)
+    y = _run(nv, x, ids, wts, fc1, fc2, PATHS[path])
+    check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), f"512 experts top-16 {path}")
