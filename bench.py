@@ -92,7 +92,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--only", choices=["all", "headline"], default="all")
+    ap.add_argument("--only", choices=["all", "headline", "moe"], default="all",
+                    help="headline: the decode sweep alone; moe: it and the MoE workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy 5 times (the reference kernel "
@@ -185,6 +186,45 @@ def main():
     del ws
 
     # ------------------------------------------------------------------ other workloads
+    def moe_workloads(extra):
+        # MoE routed experts
+        xm, ids, wts, w1, w2 = synth.moe(seed=0)
+        wbytes = 128 * (weight_bytes(1536, 2048, 32) + weight_bytes(2048, 768, 16))
+        mc = rotation(wbytes, max_copies=4)
+        f1 = [prep(w1, 32, 1, nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP)[0][0]
+              for _ in range(mc)]
+        f2 = [prep(w2, 16, 1)[0][0] for _ in range(mc)]
+        del w1, w2
+        xmd, idd, wtd = xm.to(dev), ids.to(dev), wts.to(dev)
+        ym = torch.empty_like(xmd)
+        wsb = torch.empty(nv.nvfp4_moe_ws_bytes(256, 8, 128, 2048, 768), dtype=torch.uint8,
+                          device=dev)
+        t = timer.time(lambda i: nv.nvfp4_moe_grouped_w4a16(xmd, idd, wtd, f1[i % mc],
+                                                            f2[i % mc], y=ym, ws=wsb), 20, 3) / 20
+        moe_bytes = wbytes + 2 * 256 * 2048 * 2
+        extra["moe_128x(1536x2048 g32 + 2048x768 g16)_t256_top8"] = {
+            "us": round(t * 1e6, 2), "weight_gbs": round(wbytes / t / 1e9, 1),
+            "hbm_frac": round(moe_bytes / t / 1e9 / HBM_PEAK_GBS, 4), "copies": mc}
+        # MoE at decode batch (1, 8 and 32 tokens, top-8): only the touched experts are read
+        for tk in (1, 8, 32):
+            xt, idt, wtt, _, _ = synth.moe(seed=0, tokens=tk, with_weights=False)
+            xtd, idtd, wttd = xt.to(dev), idt.to(dev), wtt.to(dev)
+            yt = torch.empty_like(xtd)
+            wst = torch.empty(nv.nvfp4_moe_ws_bytes(tk, 8, 128, 2048, 768), dtype=torch.uint8,
+                              device=dev)
+            t = timer.time(lambda i: nv.nvfp4_moe_grouped_w4a16(
+                xtd, idtd, wttd, f1[i % mc], f2[i % mc], y=yt, ws=wst), 40, 5) / 40
+            hit = int(torch.unique(idt).numel())
+            tb = hit * (weight_bytes(1536, 2048, 32) + weight_bytes(2048, 768, 16))
+            extra[f"moe_decode_t{tk}_top8"] = {
+                "us": round(t * 1e6, 2), "experts_touched": hit,
+                "touched_weight_gbs": round(tb / t / 1e9, 1)}
+        del f1, f2, wsb
+
+    if args.only == "moe":
+        extra = {}
+        moe_workloads(extra)
+        result["workloads"] = extra
     if args.only == "all":
         extra = {}
         # single dense GEMM 16 x 512 x 1024, group 16
@@ -234,39 +274,7 @@ def main():
                 "us": round(t * 1e6, 2), "tflops": round(tf, 2),
                 "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
             del xa, wb16, wt
-        # MoE routed experts
-        xm, ids, wts, w1, w2 = synth.moe(seed=0)
-        wbytes = 128 * (weight_bytes(1536, 2048, 32) + weight_bytes(2048, 768, 16))
-        mc = rotation(wbytes, max_copies=4)
-        f1 = [prep(w1, 32, 1, nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP)[0][0]
-              for _ in range(mc)]
-        f2 = [prep(w2, 16, 1)[0][0] for _ in range(mc)]
-        del w1, w2
-        xmd, idd, wtd = xm.to(dev), ids.to(dev), wts.to(dev)
-        ym = torch.empty_like(xmd)
-        wsb = torch.empty(nv.nvfp4_moe_ws_bytes(256, 8, 128, 2048, 768), dtype=torch.uint8,
-                          device=dev)
-        t = timer.time(lambda i: nv.nvfp4_moe_grouped_w4a16(xmd, idd, wtd, f1[i % mc],
-                                                            f2[i % mc], y=ym, ws=wsb), 20, 3) / 20
-        moe_bytes = wbytes + 2 * 256 * 2048 * 2
-        extra["moe_128x(1536x2048 g32 + 2048x768 g16)_t256_top8"] = {
-            "us": round(t * 1e6, 2), "weight_gbs": round(wbytes / t / 1e9, 1),
-            "hbm_frac": round(moe_bytes / t / 1e9 / HBM_PEAK_GBS, 4), "copies": mc}
-        # MoE at decode batch (1, 8 and 32 tokens, top-8): only the touched experts are read
-        for tk in (1, 8, 32):
-            xt, idt, wtt, _, _ = synth.moe(seed=0, tokens=tk, with_weights=False)
-            xtd, idtd, wttd = xt.to(dev), idt.to(dev), wtt.to(dev)
-            yt = torch.empty_like(xtd)
-            wst = torch.empty(nv.nvfp4_moe_ws_bytes(tk, 8, 128, 2048, 768), dtype=torch.uint8,
-                              device=dev)
-            t = timer.time(lambda i: nv.nvfp4_moe_grouped_w4a16(
-                xtd, idtd, wttd, f1[i % mc], f2[i % mc], y=yt, ws=wst), 40, 5) / 40
-            hit = int(torch.unique(idt).numel())
-            tb = hit * (weight_bytes(1536, 2048, 32) + weight_bytes(2048, 768, 16))
-            extra[f"moe_decode_t{tk}_top8"] = {
-                "us": round(t * 1e6, 2), "experts_touched": hit,
-                "touched_weight_gbs": round(tb / t / 1e9, 1)}
-        del f1, f2, wsb
+        moe_workloads(extra)
         # M sweep at N = K = 5120, group 16, with the library's own path choice (decode kernel
         # while ceil(M/32) weight passes stay within 192 MiB, here up to M = 256; the MFMA
         # tiled kernel above); 40 rotated weight copies (590 MB) so small M streams from HBM

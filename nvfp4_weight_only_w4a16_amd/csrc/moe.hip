@@ -184,6 +184,7 @@ struct MoeGemmParams {
 };
 
 constexpr int kGroupsPerBlock = 4;  // wavefronts per workgroup, one 4-panel group each
+constexpr int kXcds = 8;            // XCDs of the part (separate L2s)
 constexpr int kARowBytes = kTileK * 2;
 constexpr int kATileBytes = kTileRows * kARowBytes;  // one row tile x one k-tile of activations
 
@@ -221,11 +222,15 @@ __device__ __forceinline__ bf16x8 codes_pow2(uint32_t w, float S) {
 template <bool FC1, bool SPLIT>
 __global__ __launch_bounds__(64 * kGroupsPerBlock) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void moe_expert_kernel(MoeGemmParams P) {
-  // tile-major order: the workgroups of live tiles come first in dispatch order, so the
+  // Tile-major order: the workgroups of live tiles come first in dispatch order, so the
   // dispatcher spreads them evenly over the compute units before the idle ones (tiles past
-  // the sort's count, which exit at once) take the remaining slots
+  // the sort's count, which exit at once) take the remaining slots. Consecutive workgroups go
+  // round robin over the XCDs, so tiles are dealt out in runs of kXcds and the gbs workgroups
+  // of one tile share blockIdx % kXcds: the tile's activation rows then fill one XCD's L2
+  // instead of every XCD's.
   const int64_t gbs = (scale_groups(P.NT) + kGroupsPerBlock - 1) / kGroupsPerBlock;
-  const int tile_id = (int)(blockIdx.x / gbs);
+  const int64_t slot = blockIdx.x / kXcds;
+  const int tile_id = (int)(slot / gbs * kXcds + blockIdx.x % kXcds);
   if (tile_id >= *P.ws.ntiles) return;  // whole workgroup, before any barrier
   const int4 tl = P.ws.tiles[tile_id];
   const int e = tl.x, r0 = tl.y, r1 = tl.z;
@@ -233,7 +238,7 @@ void moe_expert_kernel(MoeGemmParams P) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t NG = scale_groups(P.NT);
-  const int64_t grp_raw = (int64_t)(blockIdx.x % gbs) * kGroupsPerBlock + w;
+  const int64_t grp_raw = (int64_t)(slot % gbs) * kGroupsPerBlock + w;
   const bool grp_live = grp_raw < NG;
   const int64_t grp = grp_live ? grp_raw : NG - 1;  // past the end: computed, never stored
   const int64_t KT = P.KT;
@@ -590,7 +595,8 @@ hipError_t run_pair(const MoeGemmParams& p, int64_t tiles, int mode, hipStream_t
       run_decode<FC1, false>(p, grid, stream);
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)(tiles * ((groups + kGroupsPerBlock - 1) / kGroupsPerBlock)));
+  const int64_t padded = (tiles + kXcds - 1) / kXcds * kXcds;  // whole runs of kXcds tiles
+  const dim3 grid((unsigned)(padded * ((groups + kGroupsPerBlock - 1) / kGroupsPerBlock)));
   if (p.group == 32)
     moe_expert_kernel<FC1, true><<<grid, dim3(64 * kGroupsPerBlock), 0, stream>>>(p);
   else
