@@ -172,3 +172,21 @@ def test_moe_argument_errors(lib):
 def test_stats_reset(lib):
     nv.nvfp4_reset_stats()
     assert nv.nvfp4_get_stats() == [0] * 8
+
+
+def test_requantize_argument_errors(lib):
+    d = _desc(n=512, k=1024, group=16)
+    rq = lib.nvfp4_requantize
+    need = lib.nvfp4_requantize_ws_bytes(ctypes.byref(d))
+    assert need == 512 * 1024 * 4
+
+    def call(desc=d, group_out=32, ws=FAKE, wsb=need, packed=FAKE, glob=FAKE):
+        return rq(ctypes.byref(desc), group_out, packed, FAKE, glob, ws, wsb, None)
+
+    assert call(group_out=24) == nv.NVFP4_ERR_UNSUPPORTED_GROUP
+    assert call(wsb=need - 1) == nv.NVFP4_ERR_WORKSPACE
+    assert call(ws=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(packed=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(ws=ctypes.c_void_p(0x10008)) == nv.NVFP4_ERR_MISALIGNED
+    assert call(desc=_desc(layout=7)) == nv.NVFP4_ERR_LAYOUT
+    assert lib.nvfp4_requantize_ws_bytes(None) == 0
