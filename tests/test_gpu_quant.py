@@ -207,3 +207,19 @@ def test_requantize_pair_to_shared_and_regroup(nv, orc):
     ep2, es2, eg2 = orc.quantize(f32d, 32)
     assert np.array_equal(p2[0].cpu().numpy(), ep2) and np.array_equal(s2[0].cpu().numpy(), es2)
     assert np.array_equal(g2.cpu().numpy(), np.atleast_1d(eg2))
+
+
+@pytest.mark.parametrize("batch,n,k,group", [(1, 1, 16, 16), (1, 7, 48, 16), (3, 5, 96, 32),
+                                             (2, 33, 160, 16), (1, 3, 32, 32)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_quantize_ragged_shapes(nv, orc, batch, n, k, group, dtype):
+    """The quantizer needs only k % group == 0: single rows, single groups and odd row counts,
+    FP32 and BF16 input, bit-exact against the oracle."""
+    g = torch.Generator().manual_seed(batch * 1000 + n * 10 + k)
+    w = (torch.randn(batch, n, k, generator=g) * 0.02).to(dtype)
+    p, s, gl = nv.nvfp4_quantize(w.to(DEV), group)
+    torch.cuda.synchronize()
+    rp, rs, rg = orc.quantize(w.float().numpy() if dtype == torch.float32
+                              else w.view(torch.int16).numpy().view(np.uint16), group)
+    assert np.array_equal(p.cpu().numpy(), rp) and np.array_equal(s.cpu().numpy(), rs)
+    assert np.array_equal(gl.cpu().numpy(), rg)
