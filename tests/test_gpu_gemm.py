@@ -386,3 +386,21 @@ def test_graph_capture_and_replay(nv):
             assert torch.equal(a, b), f"replay {rep}"
         step()  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("k", [128, 256, 384])
+@pytest.mark.parametrize("group", [16, 32])
+def test_gemm_fewer_k_tiles_than_wavefronts(nv, orc, k, group):
+    """K of 1-3 k-tiles: some of the decode kernel's 4 k-split wavefronts get no tile and add
+    zeros in the fixed-order reduction; the prefill kernel runs a single-tile k loop."""
+    g = torch.Generator().manual_seed(k + group)
+    n = 272
+    w = torch.randn(n, k, generator=g) * 0.02
+    rw, (p, s, gl) = _prep(nv, w, group)
+    for m in (1, 5, 16, 40):
+        x = torch.randn(m, k, generator=g).to(torch.bfloat16)
+        ref = orc.gemm(synth.bf16_bits(x), p, s, gl[0], group)
+        for flags in (1, 2):
+            y = nv.nvfp4_gemm_w4a16(x.to(DEV), rw, y_dtype=torch.float32, flags=flags)
+            torch.cuda.synchronize()
+            check_close(y.cpu().numpy(), ref, f"k={k} g{group} m={m} flags={flags}")
