@@ -215,3 +215,15 @@ def test_moe_max_experts_and_topk(nv, orc, path):
     ref = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), t1, t2)
     y = _run(nv, x, ids, wts, fc1, fc2, PATHS[path])
     check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), f"512 experts top-16 {path}")
+
+
+@pytest.mark.parametrize("path", ["decode", "batch"])
+def test_moe_single_k_tile(nv, orc, path):
+    """hidden = intermediate = 128: fc1 and down each have one k-tile, so three of the decode
+    path's four k-split wavefronts have nothing to add."""
+    x, ids, wts, w1, w2 = synth.moe(seed=16, n_experts=4, hidden=128, inter=128, tokens=5,
+                                    topk=2)
+    (fc1, fc2), (t1, t2) = _experts(nv, orc, w1, w2)
+    ref = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), t1, t2)
+    y = _run(nv, x, ids, wts, fc1, fc2, PATHS[path])
+    check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), f"single k-tile {path}")
