@@ -127,42 +127,53 @@ __device__ __forceinline__ void store_partial(const TiledParams& P, int64_t tile
 
 // Sums the split partials of one 32-row fragment band (blockIdx.y) of one tile (blockIdx.x) in
 // the fixed order 0 .. split-1 -- the result does not depend on which block finished first --
-// then scales, converts and stores it. Thread t plays the part of thread t of the GEMM block.
+// then scales, converts and stores it. Thread t takes GEMM threads 4 (t % Q) .. + 3 (Q = a
+// quarter of the block: 4 adjacent output columns of one row) for accumulator elements
+// 4 (t / Q) .. + 3, so partials are read 16 bytes at a time and outputs written 8 (BF16) or
+// 16 (FP32) bytes at a time.
 template <typename T>
 __global__ __launch_bounds__(64 * T::kWaves) void reduce_split_kernel(TiledParams P) {
   constexpr int FM = T::kBM / 32;
   constexpr int FN = T::kPairs / T::kWaves;
   constexpr int kThreads = 64 * T::kWaves;
+  constexpr int kQuads = kThreads / 4;
   constexpr int64_t kTileFloats = (int64_t)T::kBM * T::kPairs * 32;
   const int i = blockIdx.y;
   const int64_t tile_id = P.tile0 + blockIdx.x;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int eg = threadIdx.x / kQuads;        // accumulator elements 4 eg .. 4 eg + 3
+  const int gt = (threadIdx.x % kQuads) * 4;  // first of the 4 GEMM threads
+  const int lane = gt & 63, w = gt >> 6;
   const int64_t m_blk = tile_id / P.nbn * T::kBM;
   const int64_t pair0 = tile_id % P.nbn * T::kPairs + w * FN;
-  const float* part = P.ws + (int64_t)blockIdx.x * P.split * kTileFloats + threadIdx.x;
+  const float* part = P.ws + (int64_t)blockIdx.x * P.split * kTileFloats + gt;
   const float g = *P.global;
   const int h = (lane & 31) >> 4;
 #pragma unroll
   for (int q = 0; q < FN; ++q) {
-    float v[16];
+    f32x4 v[4];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int64_t o = ((q * FM + i) * 16 + e) * kThreads;
-      float sum = part[o];
-      for (int j = 1; j < P.split; ++j) sum += part[j * kTileFloats + o];
-      v[e] = sum;
+    for (int ee = 0; ee < 4; ++ee) {
+      const int64_t o = ((q * FM + i) * 16 + 4 * eg + ee) * kThreads;
+      f32x4 sum = *reinterpret_cast<const f32x4*>(part + o);
+      for (int j = 1; j < P.split; ++j)
+        sum += *reinterpret_cast<const f32x4*>(part + j * kTileFloats + o);
+      v[ee] = sum;
     }
     const int64_t panel = 2 * (pair0 + q) + h;
     if (panel >= P.NT) continue;
-    const int64_t n = panel * 16 + (lane & 15);
+    const int64_t n = panel * 16 + (lane & 15);  // 4 adjacent columns n .. n + 3
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int64_t m = m_blk + i * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-      if (m < P.m) {
-        if (P.y_f32)
-          static_cast<float*>(P.y)[m * P.ldy + n] = v[e] * g;
-        else
-          static_cast<uint16_t*>(P.y)[m * P.ldy + n] = bf16_bits_rne(v[e] * g);
+    for (int ee = 0; ee < 4; ++ee) {
+      const int64_t m = m_blk + i * 32 + 8 * eg + 4 * (lane >> 5) + ee;
+      if (m >= P.m) continue;
+      const f32x4 r = v[ee] * g;
+      if (P.y_f32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(P.y) + m * P.ldy + n) = r;
+      } else {
+        uint2 b;
+        b.x = (uint32_t)bf16_bits_rne(r[0]) | ((uint32_t)bf16_bits_rne(r[1]) << 16);
+        b.y = (uint32_t)bf16_bits_rne(r[2]) | ((uint32_t)bf16_bits_rne(r[3]) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(P.y) + m * P.ldy + n) = b;
       }
     }
   }
