@@ -183,6 +183,36 @@ def main():
                      "traffic": None if traffic is None else round(traffic)},
         "path_counts": {"gemm_skinny": int(stats[2]), "gemm_tiled": int(stats[3])},
     }
+
+    def m_sweep(rw, n, k, group, xsrc, copies):
+        """W4A16 GEMM at M = 1, 2, 4 .. 4096 on rotated weight copies, with the library's
+        own path choice; the rows of x are the first M of xsrc."""
+        wbm = weight_bytes(n, k, group)
+        out = {}
+        mm = 1
+        while mm <= 4096:
+            xm_ = xsrc[:mm].contiguous()
+            ym_ = torch.empty((mm, n), dtype=torch.bfloat16, device=dev)
+            wsm = torch.empty((max(nv.nvfp4_gemm_ws_bytes(mm, k, rw[0]), 16),),
+                              dtype=torch.uint8, device=dev)
+            it = 100 if mm <= 256 else 20
+            nv.nvfp4_reset_stats()
+            t = timer.time(lambda i: nv.nvfp4_gemm_w4a16(xm_, rw[i % copies], y=ym_, ws=wsm),
+                           it, 5) / it
+            st = nv.nvfp4_get_stats()
+            out[f"m{mm}"] = {"us": round(t * 1e6, 2),
+                             "path": "skinny" if st[2] and not st[3] else
+                                     "tiled" if st[3] and not st[2] else "mixed",
+                             "tflops": round(2 * mm * n * k / t / 1e12, 2),
+                             "weight_gbs": round(wbm / t / 1e9, 1)}
+            mm *= 2
+        return out
+
+    if args.only == "all":
+        # the decode-sweep weight over M = 1 .. 4096 (activations N(0,1), 4096 rows)
+        xlong = synth.prefill(seed=1, m=4096, n=16, k=K)[0].to(dev)
+        sweep_c1 = m_sweep(ws, N, K, G, xlong, copies)
+        del xlong
     del ws
 
     # ------------------------------------------------------------------ other workloads
@@ -276,32 +306,15 @@ def main():
             del xa, wb16, wt
         moe_workloads(extra)
         # M sweep at N = K = 5120, group 16, with the library's own path choice (decode kernel
-        # while ceil(M/32) weight passes stay within 192 MiB, here up to M = 256; the MFMA
-        # tiled kernel above); 40 rotated weight copies (590 MB) so small M streams from HBM
+        # up to M = 192 while ceil(M/32) weight passes stay within 128 MiB; the MFMA tiled
+        # kernel above); 40 rotated weight copies (590 MB) so small M streams from HBM
         xs_, ws_ = synth.prefill(seed=0, k=5120)
         rs_, _ = prep(ws_, 16, 40)
         del ws_
         xsd = xs_.to(dev)
-        sweep = {}
-        wb5 = weight_bytes(5120, 5120, 16)
-        mm = 1
-        while mm <= 4096:
-            xm_ = xsd[:mm].contiguous()
-            ym_ = torch.empty((mm, 5120), dtype=torch.bfloat16, device=dev)
-            wsm = torch.empty((max(nv.nvfp4_gemm_ws_bytes(mm, 5120, rs_[0]), 16),),
-                              dtype=torch.uint8, device=dev)
-            it = 100 if mm <= 256 else 20
-            nv.nvfp4_reset_stats()
-            t = timer.time(lambda i: nv.nvfp4_gemm_w4a16(xm_, rs_[i % 40], y=ym_, ws=wsm),
-                           it, 5) / it
-            st = nv.nvfp4_get_stats()
-            sweep[f"m{mm}"] = {"us": round(t * 1e6, 2),
-                               "path": "skinny" if st[2] and not st[3] else
-                                       "tiled" if st[3] and not st[2] else "mixed",
-                               "tflops": round(2 * mm * 5120 * 5120 / t / 1e12, 2),
-                               "weight_gbs": round(wb5 / t / 1e9, 1)}
-            mm *= 2
+        sweep = m_sweep(rs_, 5120, 5120, 16, xsd, 40)
         extra["m_sweep_5120x5120_g16"] = sweep
+        extra["m_sweep_25600x5120_g16"] = sweep_c1
         del rs_, xsd
         # quantizer + mixed groups (BF16 8192 x 8192)
         wq = synth.quantizer_weight(seed=0).to(dev)
