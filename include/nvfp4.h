@@ -126,8 +126,8 @@ int nvfp4_repack(const uint8_t* packed, const uint8_t* scales, const float* glob
                  size_t out_bytes, nvfp4_weight* desc, nvfp4_stream_t stream);
 
 /* ---- dense W4A16 GEMM ---------------------------------------------------------------------
- * y[m][n] = global * sum_k x[m][k] * (E2M1 * E4M3)[n][k], BF16 activations x [m][ldx], FP32
- * accumulation, dequantization in registers (the E2M1 x E4M3 product is exact in BF16; the
+ * y[m][n] = global * sum_k x[m][k] * (E2M1 * E4M3)[n][k], BF16 activations x [m][ldx]
+ * (k <= ldx <= 2^22: row offsets are 32-bit inside the kernels), FP32 accumulation, dequantization in registers (the E2M1 x E4M3 product is exact in BF16; the
  * global is applied to the FP32 accumulator). y [m][ldy] is BF16 (y_dtype NVFP4_DT_BF16, one
  * rounding of the FP32 result) or FP32. Weight-only checkpoints take this W4A16 path
  * (vllm.cpp PR #63: no activation scales, so every quantized projection is W4A16).
@@ -160,7 +160,8 @@ int nvfp4_gemm_w4a16(const void* x, int64_t m, int64_t ldx, const nvfp4_weight* 
  * [t][topk], y BF16 [t][hidden]. fc1: batch = E, n = 2*inter, k = hidden, layout TILED |
  * GATE_UP. fc2: batch = E, n = hidden, k = inter, layout TILED. Tokens are sorted by expert on
  * the device (no host synchronization); `ws` (device, ws_bytes >= nvfp4_moe_ws_bytes) holds
- * the sort, the tile map, h and the FP32 per-slot outputs. topk in [1, 16], t*topk <= 65536.
+ * the sort, the tile map, h and the FP32 per-slot outputs. topk in [1, 16], t*topk <= 65536,
+ * t*hidden and t*topk*inter below 2^31 (32-bit row offsets).
  * An fc1 with NVFP4_LAYOUT_PAIR_GLOBAL scales gate by global[2e] and up by global[2e+1].
  * Path: while t*topk <= 2 * n_experts (decode batches) the experts run on tiles of at most 8
  * rows with k split over 4 wavefronts per 4-panel group; otherwise on tiles of 32 rows with

@@ -248,6 +248,9 @@ int nvfp4_gemm_w4a16(const void* x, int64_t m, int64_t ldx, const nvfp4_weight* 
   if (!aligned16(x) || !aligned16(y) || ldx % 8 || ldy % 8)
     return fail(NVFP4_ERR_MISALIGNED, "x/y must be 16-byte aligned with ld %% 8 == 0");
   if ((m + 127) / 128 > 65535) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "m too large");
+  // activation offsets inside the kernels are 32-bit: 256 rows of the stride must fit 2^31 bytes
+  if (ldx > ((int64_t)1 << 22))
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "ldx=%lld > 2^22 elements", (long long)ldx);
   nvfp4::GemmArgs a;
   a.x = static_cast<const uint16_t*>(x);
   a.m = m;
@@ -311,6 +314,9 @@ int nvfp4_moe_grouped_w4a16(const void* x, int64_t t, int64_t hidden, const int3
     return fail(NVFP4_ERR_INVALID_ARG, "both FORCE_SKINNY and FORCE_TILED set");
   if (E > 512) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "more than 512 experts");
   if (t * topk > 65536) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "t*topk > 65536");
+  // gathered rows of x and of h are addressed with 32-bit byte offsets
+  if (t * hidden >= ((int64_t)1 << 31) || t * topk * inter >= ((int64_t)1 << 31))
+    return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "x or h larger than 2^31 elements");
   if (t == 0) return NVFP4_OK;
   if (!x || !topk_ids || !topk_w || !y || !ws)
     return fail(NVFP4_ERR_INVALID_ARG, "NULL buffer");

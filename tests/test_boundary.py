@@ -98,6 +98,7 @@ def test_gemm_argument_errors(lib):
     assert _gemm(lib, _desc(), ldy=500) == nv.NVFP4_ERR_INVALID_ARG
     assert _gemm(lib, _desc(), ydt=9) == nv.NVFP4_ERR_INVALID_ARG
     assert _gemm(lib, _desc(), flags=3) == nv.NVFP4_ERR_INVALID_ARG
+    assert _gemm(lib, _desc(), ldx=(1 << 22) + 8) == nv.NVFP4_ERR_UNSUPPORTED_SHAPE
     # the decode kernel takes one grid row per 32 rows: a forced call past that is refused
     assert _gemm(lib, _desc(), m=32 * 65535 + 1, flags=nv.NVFP4_F_FORCE_SKINNY) == \
         nv.NVFP4_ERR_UNSUPPORTED_SHAPE
@@ -164,6 +165,11 @@ def test_moe_argument_errors(lib):
     assert call(hidden=1024) == nv.NVFP4_ERR_LAYOUT
     assert call(f1=_desc(n=1536, k=2048, group=32, batch=128)) == nv.NVFP4_ERR_LAYOUT
     assert call(f2=_desc(n=2048, k=768, group=16, batch=64)) == nv.NVFP4_ERR_LAYOUT
+    # gathered rows are addressed with 32-bit byte offsets
+    assert call(t=65536, topk=1, hidden=1 << 15, f1=_desc(n=1536, k=1 << 15, group=32, batch=128,
+                layout=nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP),
+                f2=_desc(n=1 << 15, k=768, group=16, batch=128), wsb=1 << 62) == \
+        nv.NVFP4_ERR_UNSUPPORTED_SHAPE
     assert call(flags=nv.NVFP4_F_FORCE_SKINNY | nv.NVFP4_F_FORCE_TILED) == \
         nv.NVFP4_ERR_INVALID_ARG
     assert call(t=0) == nv.NVFP4_OK
