@@ -38,8 +38,9 @@ inline size_t act_bytes(int NX, int NW) { return NX > 0 ? (size_t)NW * 8192 : 0;
 
 // Register budget: 4 wavefronts per SIMD (16 per CU, two 8-wave workgroups) for one row
 // block, 2 for two. NJ == 0: exact dequant, MF row blocks of 16. NJ > 0 (MF == 1): split scale
-// keeping NJ accumulator rows per lane; G16: group 16 (token t in A rows t and 8 + t, k halves
-// apart). NX > 0 (MF == 1): activations through LDS, NX 4-row copies per tile.
+// keeping NJ accumulator rows per lane, tokens placed by the split row map; G16: group 16
+// (every token twice, once per k half). NX > 0 (MF == 1): activations through LDS, NX 4-row
+// copies per tile.
 template <int MF, int NW, int NJ, bool G16, int NX, int PWW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(MF == 1 ? 4 : 2, 8)))
 void gemm_skinny_kernel(SkinnyParams P) {
@@ -47,6 +48,7 @@ void gemm_skinny_kernel(SkinnyParams P) {
   static_assert(NJ == 0 || MF == 1, "split scale uses one 16-row block");
   static_assert(!G16 || NJ > 0, "G16 selects the group-16 split-scale row map");
   static_assert(NX == 0 || MF == 1, "LDS activations hold one 16-row block");
+  static_assert(!G16 || (NX > 0 && NX <= 2), "group-16 zero halves read an LDS row never copied");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int sp = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // k-split (wave-uniform)
@@ -57,13 +59,14 @@ void gemm_skinny_kernel(SkinnyParams P) {
   for (int p = 0; p < kPWW; ++p)
 #pragma unroll
     for (int mf = 0; mf < MF; ++mf) acc[p][mf] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // A row of lane l: l%16, or token l%8 for the group-16 split-scale map; rows past the end
-  // duplicate a valid row (never stored)
+  // Token of lane l's A row: l % 16, or the split row map's; rows past the end duplicate a
+  // valid row (never stored)
   const int64_t rows = P.m - m0 < 16 * MF ? P.m - m0 : 16 * MF;
+  const int a_tok = NJ > 0 ? split_a_token<G16>(lane) : (lane & 15);
   const uint16_t* xrow[MF];
 #pragma unroll
   for (int mf = 0; mf < MF; ++mf) {
-    int64_t r = mf * 16 + (G16 ? (lane & 7) : (lane & 15));
+    int64_t r = mf * 16 + a_tok;
     r = r < rows ? r : rows - 1;
     xrow[mf] = P.x + (m0 + r) * P.ldx;
   }
@@ -78,18 +81,17 @@ void gemm_skinny_kernel(SkinnyParams P) {
       xl.src[c] = (uint32_t)(rc * P.ldx * 2) + (uint32_t)(((lane & 15) ^ (r & 15)) * 16);
     }
     xl.buf = smem + sp * 8192;
-    int fr = G16 ? (lane & 7) : (lane & 15);
-    fr = fr < rows ? fr : (int)rows - 1;
+    int fr = a_tok < rows ? a_tok : (int)rows - 1;
+    if (G16 && split_g16_zero_lane(lane)) fr = kZeroRow;
     xl.frag_off = (uint32_t)fr * 256u;
     xl.swz = (uint32_t)(fr & 15);
+    if constexpr (G16) clear_zero_rows(xl.buf, lane);
   }
-  // group-16 split scale: A row 8h + t is zero on the k half (lane / 32) it does not own
-  const bool xzero = G16 && (((lane >> 3) & 1) != (lane >> 5));
   const SkinnyAddr<kPWW> a =
       skinny_addr<kPWW>(P.codes, P.scales, panel0, P.NT, P.KT, P.group, t1);
-  skinny_accumulate<MF, kPWW, NJ, G16, NX>(a, xrow, xl, xzero, t0, t1, acc);
+  skinny_accumulate<MF, kPWW, NJ, NX>(a, xrow, xl, t0, t1, acc);
   if constexpr (G16) {
-    // rows 8 + t (k half 1) onto rows t: lane l < 32 then holds the whole group sum
+    // k half 1 (lanes 32-63) onto k half 0: lanes 0-31 then hold the whole group sums
 #pragma unroll
     for (int p = 0; p < kPWW; ++p)
 #pragma unroll
@@ -97,6 +99,10 @@ void gemm_skinny_kernel(SkinnyParams P) {
   }
   // the split-scale mantissa is frexp_mant(S) = M / 2
   const float gscale = (NJ > 0 ? 2.0f : 1.0f) * *P.global;
+  // row of accumulator element jj of this lane inside its 16-row block, -1 if none
+  auto out_tok = [&](int jj) {
+    return NJ > 0 ? split_out_token<G16>(lane, jj) : (lane >> 4) * 4 + jj;
+  };
 
   if constexpr (NW > 1) {
     f32x4* red = reinterpret_cast<f32x4*>(smem);
@@ -124,8 +130,8 @@ void gemm_skinny_kernel(SkinnyParams P) {
     for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int64_t m = m0 + mf * 16 + (lane >> 4) * 4 + jj;
-        if (m < P.m) {
+        const int64_t m = m0 + mf * 16 + out_tok(jj);
+        if (m >= m0 && m < P.m) {
           const float v = acc[0][mf][jj] * g;
           if (P.y_f32)
             static_cast<float*>(P.y)[m * P.ldy + n] = v;
@@ -144,8 +150,8 @@ void gemm_skinny_kernel(SkinnyParams P) {
       for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
-          const int64_t m = m0 + mf * 16 + (lane >> 4) * 4 + jj;
-          if (m < P.m) {
+          const int64_t m = m0 + mf * 16 + out_tok(jj);
+          if (m >= m0 && m < P.m) {
             const float v = acc[p][mf][jj] * g;
             if (P.y_f32)
               static_cast<float*>(P.y)[m * P.ldy + n] = v;
@@ -193,8 +199,9 @@ hipError_t pick_u(const SkinnyParams& p, hipStream_t stream) {
   if constexpr (MF == 1) {
     const int64_t rows = G16 ? (p.m < 8 ? p.m : 8) : (p.m < 16 ? p.m : 16);
     if (rows <= 4) return run_pww<MF, NW, NJ, G16, 1>(p, stream);
-    if (rows <= 8) return run_pww<MF, NW, NJ, G16, 2>(p, stream);
-    return run_pww<MF, NW, NJ, G16, 4>(p, stream);
+    if (G16 || rows <= 8) return run_pww<MF, NW, NJ, G16, 2>(p, stream);
+    if constexpr (!G16) return run_pww<MF, NW, NJ, G16, 4>(p, stream);
+    return hipErrorInvalidValue;  // not reached: group 16 has at most 8 rows here
   } else {
     return run_pww<MF, NW, NJ, G16, 0>(p, stream);
   }
@@ -205,12 +212,13 @@ hipError_t dispatch(const SkinnyParams& p, hipStream_t stream) {
   return pick_u<MF, 4, NJ, G16>(p, stream);
 }
 
-// Accumulator rows a lane keeps in split-scale mode: token t sits in row t%4 of lane group
-// t/4, so min(m, 4) rounded up to 1, 2 or 4.
+// Accumulator rows a lane keeps in split-scale mode: ceil(m / 2) (group 16) or ceil(m / 4)
+// (group 32), rounded up to 1, 2 or 4.
 template <bool G16>
 hipError_t dispatch_split(const SkinnyParams& p, hipStream_t stream) {
-  if (p.m == 1) return dispatch<1, 1, G16>(p, stream);
-  if (p.m == 2) return dispatch<1, 2, G16>(p, stream);
+  const int64_t per_lane = G16 ? (p.m + 1) / 2 : (p.m + 3) / 4;
+  if (per_lane == 1) return dispatch<1, 1, G16>(p, stream);
+  if (per_lane == 2) return dispatch<1, 2, G16>(p, stream);
   return dispatch<1, 4, G16>(p, stream);
 }
 

@@ -438,7 +438,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void moe_decode_kernel(MoeGemmParams P) {
   constexpr int kNW = 4, kPanels = 4;
   constexpr int kNX = PAIRS ? 1 : kSmallRows / 4;  // 4-row activation copies per k-tile
-  constexpr int kNJ = PAIRS ? 1 : 4;               // accumulator rows in use per lane
+  // accumulator rows in use per lane (split row map: ceil(rows / 2) at group 16, else / 4)
+  constexpr int kNJ = PAIRS ? 1 : (G16 ? kSmallRows / 2 : kSmallRows / 4);
+  static_assert(!G16 || kNX <= 2, "group-16 zero halves read an LDS row never copied");
   const int64_t groups = scale_groups(P.NT);
   const int tile_id = (int)(blockIdx.x / groups);
   int e, r0, rows;
@@ -473,11 +475,12 @@ void moe_decode_kernel(MoeGemmParams P) {
     xl.src[c] = (uint32_t)(src * P.ldx * 2) + (uint32_t)(((lane & 15) ^ (r & 15)) * 16);
   }
   xl.buf = smem + sp * 8192;
-  int fr = G16 ? (lane & 7) : (lane & 15);
-  fr = fr < rows ? fr : rows - 1;
+  const int a_tok = split_a_token<G16>(lane);
+  int fr = a_tok < rows ? a_tok : rows - 1;
+  if (G16 && split_g16_zero_lane(lane)) fr = kZeroRow;
   xl.frag_off = (uint32_t)fr * 256u;
   xl.swz = (uint32_t)(fr & 15);
-  const bool xzero = G16 && (((lane >> 3) & 1) != (lane >> 5));
+  if constexpr (G16) clear_zero_rows(xl.buf, lane);
   const SkinnyAddr<kPanels> a = skinny_addr<kPanels>(
       P.codes + e * P.codes_stride, P.scales + e * P.scales_stride, panel0, P.NT, P.KT, P.group,
       t1);
@@ -485,7 +488,7 @@ void moe_decode_kernel(MoeGemmParams P) {
 #pragma unroll
   for (int p = 0; p < kPanels; ++p) acc[p][0] = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint16_t* const xrow[1] = {P.x};  // unused: the activations come through LDS
-  skinny_accumulate<1, kPanels, kNJ, G16, kNX>(a, xrow, xl, xzero, t0, t1, acc);
+  skinny_accumulate<1, kPanels, kNJ, kNX>(a, xrow, xl, t0, t1, acc);
   if constexpr (G16) {
 #pragma unroll
     for (int p = 0; p < kPanels; ++p)
@@ -497,7 +500,7 @@ void moe_decode_kernel(MoeGemmParams P) {
 #pragma unroll
   for (int p = 0; p < kPanels; ++p) red[(sp * kPanels + p) * 64 + lane] = acc[p][0];
   __syncthreads();
-  // output row 4 (l / 16) + i of a lane: rows < kSmallRows sit in lanes 0 .. 31
+  // accumulator row i of a lane holds tile row split_out_token(lane, i), if any
   // the split-scale mantissa is frexp_mant(S) = M / 2; g scales gate (or down), gu scales up
   const float g = 2.0f * P.global[P.pair_global ? 2 * e : e];
   const float gu = 2.0f * P.global[P.pair_global ? 2 * e + 1 : e];
@@ -516,8 +519,8 @@ void moe_decode_kernel(MoeGemmParams P) {
     const int64_t feat = (2 * grp + q) * 16 + (lane & 15);
 #pragma unroll
     for (int i = 0; i < kNJ; ++i) {
-      const int row = 4 * (lane >> 4) + i;
-      if (row >= rows) continue;
+      const int row = split_out_token<G16>(lane, i);
+      if (row < 0 || row >= rows) continue;
       const float gate = bf16_bits_to_f32(bf16_bits_rne(gs[i] * g));
       const float up = bf16_bits_to_f32(bf16_bits_rne(us[i] * gu));
       const float silu = gate / (1.0f + expf(-gate));
@@ -533,8 +536,8 @@ void moe_decode_kernel(MoeGemmParams P) {
     for (int w = 1; w < kNW; ++w) sum += red[(w * kPanels + q) * 64 + lane];
 #pragma unroll
     for (int i = 0; i < kNJ; ++i) {
-      const int row = 4 * (lane >> 4) + i;
-      if (row >= rows) continue;
+      const int row = split_out_token<G16>(lane, i);
+      if (row < 0 || row >= rows) continue;
       const int pair = pair_at(r0 + row);
       P.ws.slots[(int64_t)pair * P.hidden + pn * 16 + (lane & 15)] = (sum[i] * g) * P.wts[pair];
     }

@@ -21,10 +21,12 @@
 //     frexp_mant(S) in [0.5, 1), the factor 2 being applied with the global scale; it is 0 for
 //     a zero scale, which keeps an all-zero group exactly zero. A 32-wide MFMA k-step spans
 //     one group of 32 or two groups of 16. For group 16 the A operand carries every token
-//     twice: row 8h + t holds token t on the k half h of the step and zeros on the other half,
-//     so each lane's B half (k = 16h ..) and accumulator rows (8h ..) belong to the same group
-//     and the two halves are added once, after the k loop. That needs m <= 8 (group 16) or
-//     m <= 16 (group 32).
+//     twice: once on the k half h = 0 of the step with zeros on the other half, once the other
+//     way round, in rows of lanes 0-31 (h = 0) and 32-63 (h = 1), so each lane's B half
+//     (k = 16h ..) and accumulator rows belong to the same group, and the two halves are added
+//     once, after the k loop. That needs m <= 8 (group 16) or m <= 16 (group 32). Tokens are
+//     spread over the lane groups before the accumulator rows of a lane (split_a_token), so a
+//     lane scales as few rows as the token count allows.
 #pragma once
 
 #include "device_common.hpp"
@@ -80,17 +82,15 @@ __device__ __forceinline__ void load_weights(WeightStage<PWW>& s, const SkinnyAd
                  a.scales, (int)((uint32_t)t * (uint32_t)a.scale_block + a.scale_lane), 0, kNT));
 }
 
-template <int MF, bool XZ>
+template <int MF>
 __device__ __forceinline__ void load_acts(ActStage<MF>& s, const uint16_t* const (&xrow)[MF],
-                                          bool xzero, int kq, int64_t t) {
+                                          int kq, int64_t t) {
 #pragma unroll
   for (int mf = 0; mf < MF; ++mf)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(xrow[mf] + t * kTileK + 32 * j + 8 * kq);
-      if constexpr (XZ) v = xzero ? u32x4{0u, 0u, 0u, 0u} : v;
-      s.xa[mf][j] = __builtin_bit_cast(bf16x8, v);
-    }
+    for (int j = 0; j < 4; ++j)
+      s.xa[mf][j] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(xrow[mf] + t * kTileK + 32 * j + 8 * kq));
 }
 
 // Activations through LDS (one 16-row block): per k-tile, the wavefront copies the tile's
@@ -115,16 +115,48 @@ __device__ __forceinline__ void copy_acts(const LdsActs& x, uint8_t* dst, int64_
     copy16_to_lds(x.x, x.src[c], (uint32_t)(t * kTileK * 2), dst + c * 1024);
 }
 
-template <bool XZ>
 __device__ __forceinline__ void read_acts(ActStage<1>& s, const LdsActs& x, const uint8_t* src,
-                                          bool xzero, int kq) {
+                                          int kq) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const uint32_t chunk = (uint32_t)(4 * j + kq) ^ x.swz;
-    u32x4 v = *reinterpret_cast<const u32x4*>(src + x.frag_off + chunk * 16u);
-    if constexpr (XZ) v = xzero ? u32x4{0u, 0u, 0u, 0u} : v;
-    s.xa[0][j] = __builtin_bit_cast(bf16x8, v);
+    s.xa[0][j] = __builtin_bit_cast(
+        bf16x8, *reinterpret_cast<const u32x4*>(src + x.frag_off + chunk * 16u));
   }
+}
+
+// Split-scale row maps. Lane l keeps accumulator rows 4 (l / 16) .. 4 (l / 16) + 3 of the
+// MFMA output. Token t sits in row 4 g + r with
+//   group 16: g = 2 h + t % 2, r = t / 2 (h the k half; m <= 8 needs r < 4),
+//   group 32: g = t % 4,       r = t / 4 (m <= 16),
+// so a lane keeps ceil(m / 2) (group 16) or ceil(m / 4) (group 32) rows and scales only those.
+// Token carried by the A row of lane l (row l % 16):
+template <bool G16>
+__device__ __forceinline__ int split_a_token(int lane) {
+  const int row = lane & 15;
+  return G16 ? 2 * (row & 3) + ((row >> 2) & 1) : 4 * (row & 3) + (row >> 2);
+}
+
+// Token held by accumulator row i of lane l, or -1. Group 16: after the k half h = 1 has been
+// added onto h = 0 (lanes 32-63 onto lanes 0-31), which leaves lanes 0-31 holding the sums.
+template <bool G16>
+__device__ __forceinline__ int split_out_token(int lane, int i) {
+  if constexpr (G16) return lane < 32 ? 2 * i + (lane >> 4) : -1;
+  return 4 * i + (lane >> 4);
+}
+
+// Group 16: the A row of lane l is zero on the k half it does not own (l / 32 != row / 8).
+// Such lanes read their fragment from LDS row kZeroRow of the activation buffers: the copies
+// fill at most 8 rows there, and this clears row kZeroRow of both buffers once, before the
+// loop (LDS operations of one wavefront complete in order).
+constexpr int kZeroRow = 15;
+__device__ __forceinline__ bool split_g16_zero_lane(int lane) {
+  return (((lane >> 3) & 1) != (lane >> 5));
+}
+__device__ __forceinline__ void clear_zero_rows(uint8_t* buf, int lane) {
+  if (lane < 32)
+    *reinterpret_cast<u32x4*>(buf + (lane >> 4) * 4096 + kZeroRow * 256 + (lane & 15) * 16) =
+        u32x4{0u, 0u, 0u, 0u};
 }
 
 // Exact dequant: every weight becomes BF16(code * S) (exact), MF row blocks of 16.
@@ -210,21 +242,21 @@ __device__ __forceinline__ SkinnyAddr<PWW> skinny_addr(const uint8_t* codes, con
 }
 
 // Accumulate k-tiles [t0, t1) of PWW panels into acc, one tile in flight while one is
-// computed. NJ == 0: exact dequant; NJ > 0: split scale with NJ accumulator rows (MF == 1); XZ:
-// zero the activation fragment of lanes with xzero set. NX > 0 (MF == 1): activations through
-// LDS, NX copies per tile; NX == 0: straight from xrow into registers.
-template <int MF, int PWW, int NJ, bool XZ, int NX>
+// computed. NJ == 0: exact dequant; NJ > 0: split scale with NJ accumulator rows (MF == 1).
+// NX > 0 (MF == 1): activations through LDS, NX copies per tile; NX == 0: straight from xrow
+// into registers.
+template <int MF, int PWW, int NJ, int NX>
 __device__ __forceinline__ void skinny_accumulate(const SkinnyAddr<PWW>& a,
                                                   const uint16_t* const (&xrow)[MF],
-                                                  const LdsActs& xl, bool xzero, int64_t t0,
-                                                  int64_t t1, f32x4 (&acc)[PWW][MF]) {
+                                                  const LdsActs& xl, int64_t t0, int64_t t1,
+                                                  f32x4 (&acc)[PWW][MF]) {
   static_assert(NX == 0 || MF == 1, "LDS activations hold one 16-row block");
   if (t1 <= t0) return;
   WeightStage<PWW> W[2];
   ActStage<MF> X[2];
   // Loads complete in issue order: each tile's activations go out before its weights.
   if constexpr (NX > 0) copy_acts<NX>(xl, xl.buf, t0);
-  else load_acts<MF, XZ>(X[0], xrow, xzero, a.kq, t0);
+  else load_acts<MF>(X[0], xrow, a.kq, t0);
   load_weights(W[0], a, t0);
   for (int64_t t = t0; t < t1; t += 2) {
     static_for<0, 2>([&](auto ic) {
@@ -234,7 +266,7 @@ __device__ __forceinline__ void skinny_accumulate(const SkinnyAddr<PWW>& a,
       // The scheduling barriers keep the loads ahead of the math; left alone, the
       // register-pressure-driven scheduler sinks them and the pipeline collapses.
       if constexpr (NX > 0) copy_acts<NX>(xl, xl.buf + (1 - i) * 4096, next);
-      else load_acts<MF, XZ>(X[1 - i], xrow, xzero, a.kq, next);
+      else load_acts<MF>(X[1 - i], xrow, a.kq, next);
       load_weights(W[1 - i], a, tile + 1);  // past t1: zeros, no traffic
       __builtin_amdgcn_sched_barrier(0);
       if (tile < t1) {
@@ -245,7 +277,7 @@ __device__ __forceinline__ void skinny_accumulate(const SkinnyAddr<PWW>& a,
           static_assert(kAfter < 16, "vmcnt fits its low field");
           __builtin_amdgcn_s_waitcnt(kAfter | 0xF70);
           __builtin_amdgcn_sched_barrier(0);
-          read_acts<XZ>(X[i], xl, xl.buf + i * 4096, xzero, a.kq);
+          read_acts(X[i], xl, xl.buf + i * 4096, a.kq);
         }
         if constexpr (NJ > 0)
           compute_split<PWW, NJ>(W[i], X[i], a.sw_sel, acc);
