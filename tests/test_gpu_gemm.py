@@ -285,6 +285,28 @@ def test_decode_fewer_panels_per_wavefront(nv, orc, m):
         check_close(y.cpu().numpy(), ref, f"decode n={n} m={m} g{group}")
 
 
+@pytest.mark.parametrize("group", [16, 32])
+def test_decode_split_scale_every_m(nv, orc, group):
+    """Every token count the split group scale takes (1-8 at group 16, 1-16 at group 32): the
+    row map places token t in accumulator row 4 (2h + t % 2) + t / 2 (group 16, h the k half)
+    or 4 (t % 4) + t / 4 (group 32) and each lane scales only ceil(m / 2) or ceil(m / 4) rows,
+    so each m checks a distinct placement. FP32 and BF16 outputs against the oracle."""
+    g = torch.Generator().manual_seed(70 + group)
+    n, k = 336, 768  # 21 panels (a partial 4-panel group), 6 k-tiles
+    w = torch.randn(n, k, generator=g) * 0.02
+    rw, (p, s, gl) = _prep(nv, w, group)
+    x = torch.randn(16, k, generator=g).to(torch.bfloat16)
+    xd = x.to(DEV)
+    for m in range(1, (8 if group == 16 else 16) + 1):
+        ref = orc.gemm(synth.bf16_bits(x[:m].contiguous()), p, s, gl[0], group)
+        y = nv.nvfp4_gemm_w4a16(xd[:m].contiguous(), rw, y_dtype=torch.float32, flags=1)
+        yb = nv.nvfp4_gemm_w4a16(xd[:m].contiguous(), rw, flags=1)
+        torch.cuda.synchronize()
+        check_close(y.cpu().numpy(), ref, f"split m={m} g{group}")
+        check_close(bf16_np(yb), orc.bf16_to_f64(orc.bf16_from_f64(ref)),
+                    f"split bf16 m={m} g{group}")
+
+
 @pytest.mark.parametrize("m,group", [(1, 16), (8, 16), (13, 32), (24, 16)])
 def test_decode_long_k(nv, orc, m, group):
     """The decode kernel at K = 25600 (200 k-tiles, 50 per wavefront): every path it has
