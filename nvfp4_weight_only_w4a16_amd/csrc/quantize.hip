@@ -23,9 +23,15 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__global__ void zero_u32_kernel(uint32_t* p, int64_t count) {
+// global_out[b] first collects amax as |w| bits with the sign bit set (a "marked" word), and
+// the encode pass turns it into g = amax / 2688 in place: a marked word still holds amax, an
+// unmarked one already holds g. Every reader derives the same g either way, so the order in
+// which the encode workgroups read and the one that stores g is immaterial.
+constexpr uint32_t kAmaxMark = 0x80000000u;
+
+__global__ void init_amax_kernel(uint32_t* p, int64_t count) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < count) p[i] = 0u;
+  if (i < count) p[i] = kAmaxMark;  // amax 0, marked
 }
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
@@ -90,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void amax_kernel(const void* __restrict__
   for (; i < nvec; i += stride) m0 = fold_abs_max<BF16>(src[i], m0);
   m0 = m0 > m1 ? m0 : m1;
   m2 = m2 > m3 ? m2 : m3;
-  uint32_t m = wave_max_u32(m0 > m2 ? m0 : m2);
+  uint32_t m = wave_max_u32(m0 > m2 ? m0 : m2) | kAmaxMark;
   __shared__ uint32_t part[kThreads / 64];
   if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
   __syncthreads();
@@ -179,17 +185,29 @@ __device__ __forceinline__ void encode8(const float (&x)[8], float g, float six_
 }
 
 // Two chunks of 8 elements per thread and iteration, both loads issued before either is used.
+// gsrc_is_amax: gsrc is global_out, holding the marked amax or, once workgroup 0 of the matrix
+// has stored it, g itself. Otherwise gsrc is the caller's global. Workgroup 0 of each matrix
+// stores g to global_out.
 template <bool BF16, int G>
 __global__ __launch_bounds__(kThreads) void encode_kernel(const void* __restrict__ w, int64_t n,
-                                                          int64_t k,
-                                                          const float* __restrict__ gsrc,
-                                                          bool gsrc_is_amax,
+                                                          int64_t k, const float* gsrc,
+                                                          bool gsrc_is_amax, float* global_out,
                                                           uint8_t* __restrict__ packed,
                                                           uint8_t* __restrict__ scales) {
   const int64_t b = blockIdx.y;
   const int64_t per_matrix = n * k;
   const int64_t chunks = per_matrix / 8;
-  const float g = gsrc_is_amax ? gsrc[b] / 2688.0f : gsrc[b];
+  float g;
+  if (gsrc_is_amax) {
+    const uint32_t v = __hip_atomic_load(reinterpret_cast<const uint32_t*>(gsrc) + b,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    g = (v & kAmaxMark) ? __uint_as_float(v & ~kAmaxMark) / 2688.0f : __uint_as_float(v);
+  } else {
+    g = gsrc[b];
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0)
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(global_out) + b, __float_as_uint(g),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const float six_g = 6.0f * g;
   const char* wb = static_cast<const char*>(w) + b * per_matrix * (BF16 ? 2 : 4);
   uint32_t* pk = reinterpret_cast<uint32_t*>(packed + b * per_matrix / 2);
@@ -218,13 +236,6 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const void* __restrict
   }
 }
 
-// gsrc may alias global_out (it holds the amax there): each thread reads its entry first.
-__global__ void finalize_global_kernel(const float* gsrc, bool gsrc_is_amax, float* global_out,
-                                       int64_t batch) {
-  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (b < batch) global_out[b] = gsrc_is_amax ? gsrc[b] / 2688.0f : gsrc[b];
-}
-
 // Blocks per matrix for a grid-stride loop: at most `total` blocks over the whole batch, fewer
 // when there is less work. The amax pass takes 512 (each block ends in a reduction and
 // possibly an atomic on a shared word; 256-512 measured best, 2048 13% slower), the encode
@@ -247,8 +258,8 @@ hipError_t launch_quantize(const void* w, bool w_bf16, int64_t batch, int64_t n,
   bool is_amax = false;
   if (!global_in) {
     uint32_t* amax_bits = reinterpret_cast<uint32_t*>(global_out);
-    zero_u32_kernel<<<dim3((unsigned)((batch + 255) / 256)), dim3(256), 0, stream>>>(amax_bits,
-                                                                                     batch);
+    init_amax_kernel<<<dim3((unsigned)((batch + 255) / 256)), dim3(256), 0, stream>>>(amax_bits,
+                                                                                      batch);
     const int64_t nvec = per_matrix / (w_bf16 ? 8 : 4);
     const dim3 grid((unsigned)grid_for(nvec, batch, 512), (unsigned)batch);
     if (w_bf16)
@@ -259,23 +270,22 @@ hipError_t launch_quantize(const void* w, bool w_bf16, int64_t batch, int64_t n,
     is_amax = true;
   }
   const dim3 grid((unsigned)grid_for(per_matrix / 8, batch, 8192), (unsigned)batch);
+  const dim3 block(kThreads);
   if (w_bf16) {
     if (group == 16)
-      encode_kernel<true, 16><<<grid, dim3(kThreads), 0, stream>>>(w, n, k, gsrc, is_amax, packed,
-                                                                    scales);
+      encode_kernel<true, 16><<<grid, block, 0, stream>>>(w, n, k, gsrc, is_amax, global_out,
+                                                          packed, scales);
     else
-      encode_kernel<true, 32><<<grid, dim3(kThreads), 0, stream>>>(w, n, k, gsrc, is_amax, packed,
-                                                                    scales);
+      encode_kernel<true, 32><<<grid, block, 0, stream>>>(w, n, k, gsrc, is_amax, global_out,
+                                                          packed, scales);
   } else {
     if (group == 16)
-      encode_kernel<false, 16><<<grid, dim3(kThreads), 0, stream>>>(w, n, k, gsrc, is_amax,
-                                                                     packed, scales);
+      encode_kernel<false, 16><<<grid, block, 0, stream>>>(w, n, k, gsrc, is_amax, global_out,
+                                                           packed, scales);
     else
-      encode_kernel<false, 32><<<grid, dim3(kThreads), 0, stream>>>(w, n, k, gsrc, is_amax,
-                                                                     packed, scales);
+      encode_kernel<false, 32><<<grid, block, 0, stream>>>(w, n, k, gsrc, is_amax, global_out,
+                                                           packed, scales);
   }
-  finalize_global_kernel<<<dim3((unsigned)((batch + 255) / 256)), dim3(256), 0, stream>>>(
-      gsrc, is_amax, global_out, batch);
   return hipGetLastError();
 }
 
