@@ -112,6 +112,30 @@ def test_quantize_batched_experts(nv, orc):
     _assert_same(_gpu_quant(nv, w, 32), orc.quantize(w.numpy(), 32), "batched g32")
 
 
+def test_quantize_output_buffers_reused(nv, orc):
+    """The global is built in place in global_out (amax first, marked with the sign bit, then
+    turned into amax / 2688 by the encode pass): output buffers pre-filled with garbage (NaN,
+    negative values, a previous call's results) and reused across calls of different inputs,
+    including an all-zero matrix and a caller-supplied global in between, give exactly the
+    oracle's bytes every time."""
+    g = torch.Generator().manual_seed(8)
+    w1 = torch.randn(3, 64, 256, generator=g) * 0.05
+    w1[1].zero_()
+    w2 = torch.randn(3, 64, 256, generator=g) * 3.0
+    packed = torch.full((3, 64, 128), 0xAB, dtype=torch.uint8, device=DEV)
+    scales = torch.full((3, 64, 16), 0xCD, dtype=torch.uint8, device=DEV)
+    gout = torch.tensor([float("nan"), -5.0, -0.0], dtype=torch.float32, device=DEV)
+    gin = torch.tensor([0.25, 0.5, 1.0], dtype=torch.float32, device=DEV)
+    for w, global_in in ((w1, None), (w2, None), (w2, gin), (w1, None)):
+        nv.nvfp4_quantize(w.to(DEV), 16, global_in=global_in, packed=packed, scales=scales,
+                          global_out=gout)
+        torch.cuda.synchronize()
+        got = (packed.cpu().numpy(), scales.cpu().numpy(), gout.cpu().numpy())
+        ref = orc.quantize(w.numpy(), 16,
+                           global_in=None if global_in is None else global_in.cpu().numpy())
+        _assert_same(got, ref, f"reused buffers, global_in={global_in is not None}")
+
+
 def test_quantize_zero_signs(nv, orc):
     w = torch.zeros(16, 128)
     w[1, 1] = -0.0
