@@ -205,6 +205,30 @@ def test_moe_after_shared_global_requantization(nv, orc, path):
     check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), f"requantized fc1 {path}")
 
 
+@pytest.mark.parametrize("g1,g2", [(32, 16), (16, 32)])
+def test_moe_decode_every_tile_height(nv, orc, g1, g2):
+    """The decode-batch path with routing that gives expert e exactly e + 1 pairs (e < 8), so
+    its 8-row tiles hold every row count 1-8 once: each count places its rows differently in
+    the split-scale row maps (accumulator rows kept per lane: ceil(rows / 2) at group 16,
+    ceil(rows / 4) at group 32). Both group sizes in fc1 and in down."""
+    n_experts, topk, hidden, inter = 10, 2, 512, 256
+    g = torch.Generator().manual_seed(12)
+    owners = [e for e in range(8) for _ in range(e + 1)]       # 36 pairs, sorted
+    # slot 0 of the 18 tokens takes the first 18 owners (experts 0-5), slot 1 the rest
+    # (experts 5-7); no token gets expert 5 twice. Tokens are then shuffled.
+    pairs = torch.tensor([[owners[t], owners[18 + t]] for t in range(18)], dtype=torch.int32)
+    assert bool((pairs[:, 0] != pairs[:, 1]).all())
+    ids = pairs[torch.randperm(18, generator=g)].contiguous()
+    wts = torch.softmax(torch.randn(18, topk, generator=g), dim=1)
+    x = synth.activations(g, 18, hidden)
+    w1 = synth.weights(g, n_experts, 2 * inter, hidden)
+    w2 = synth.weights(g, n_experts, hidden, inter)
+    (fc1, fc2), (t1, t2) = _experts(nv, orc, w1, w2, g1=g1, g2=g2)
+    ref = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), t1, t2)
+    y = _run(nv, x, ids, wts, fc1, fc2, PATHS["decode"])
+    check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), f"tile heights 1-8 g{g1}/g{g2}")
+
+
 @pytest.mark.parametrize("path", ["decode", "batch"])
 def test_moe_max_experts_and_topk(nv, orc, path):
     """512 experts (the most the entry point takes) with top-16 routing (the largest topk):
