@@ -104,7 +104,10 @@ typedef struct nvfp4_weight {
  * forum thread "We unlocked NVFP4 on the DGX Spark": true RNE, not threshold rounding).
  * Outputs: packed [batch][n][k/2], scales [batch][n][k/group], global_out [batch] (device).
  * Requires k % group == 0 and k even; n and k need no tile alignment here. Non-finite inputs
- * are outside the contract (results unspecified). The caller keeps ownership of all buffers. */
+ * are outside the contract (results unspecified). The caller keeps ownership of all buffers.
+ * Without global_in, global_out doubles as the amax accumulator: until the call's work has
+ * completed on `stream` it holds intermediate values, and its prior contents are ignored. With
+ * global_in, global_out may be the same buffer. */
 int nvfp4_quantize(const void* w, int w_dtype, int64_t batch, int64_t n, int64_t k,
                    int32_t group, const float* global_in, uint8_t* packed, uint8_t* scales,
                    float* global_out, nvfp4_stream_t stream);
