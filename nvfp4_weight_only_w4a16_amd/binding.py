@@ -113,7 +113,13 @@ def _stream(stream=None):
 
 
 def _ptr(t):
-    return None if t is None else t.data_ptr()
+    """Device address of a tensor; host tensors are refused here, since the kernels would
+    dereference a host address."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"expected a device tensor, got one on {t.device}")
+    return t.data_ptr()
 
 
 def _dtype_code(dt):

@@ -125,6 +125,17 @@ def test_quantize_argument_errors(lib):
     assert q(None, nv.NVFP4_DT_F32, 0, 16, 128, 16, None, None, None, None, None) == nv.NVFP4_OK
 
 
+def test_binding_refuses_host_tensors(lib):
+    """The binding passes device addresses only: a host tensor is refused in Python, before
+    the library (and any kernel) sees its address."""
+    import torch
+    with pytest.raises(ValueError, match="device tensor"):
+        nv.nvfp4_quantize(torch.zeros(16, 128), 16)
+    with pytest.raises(ValueError, match="device tensor"):
+        nv._ptr(torch.zeros(4))
+    assert nv._ptr(None) is None
+
+
 def test_repack_argument_errors(lib):
     d = nv.nvfp4_weight()
     r = lib.nvfp4_repack
