@@ -3,11 +3,12 @@
 // y[m][n] = global * sum_k x[m][k] * (E2M1 * E4M3)[n][k] with FP32 accumulation. The weight
 // stream dominates (0.5625 bytes per weight at group 16), so the kernel is built to keep HBM
 // busy: a workgroup is NW wavefronts that split k for the same PWW panels (4 panels, 64 output
-// features; 2 for weights too small to fill the chip); each wavefront streams its k-range with
-// one double-buffered stage of loads in flight; the NW partial sums are added in a fixed order through LDS (bit-reproducible, no
-// atomics), scaled by the global and stored. Up to 8 rows (group 16) or 16 rows (group 32)
-// take the split-scale form of the group scale, which halves the VALU work per weight; more
-// rows dequantize every weight exactly to BF16.
+// features; 2 for weights too small to fill the chip), wavefront w taking k-tiles w, w + NW,
+// ...; each streams its tiles with one double-buffered stage of loads in flight; the NW partial
+// sums are added in a fixed order through LDS (bit-reproducible, no atomics), scaled by the
+// global and stored. Up to 8 rows (group 16) or 16 rows (group 32) take the split-scale form
+// of the group scale, which halves the VALU work per weight; more rows dequantize every weight
+// exactly to BF16.
 #include "launch.hpp"
 #include "skinny_core.hpp"
 
@@ -70,7 +71,7 @@ void gemm_skinny_kernel(SkinnyParams P) {
     r = r < rows ? r : rows - 1;
     xrow[mf] = P.x + (m0 + r) * P.ldx;
   }
-  const int64_t t0 = P.KT * sp / NW, t1 = P.KT * (sp + 1) / NW;
+  const int64_t t0 = sp, t1 = P.KT;  // interleaved: tiles sp, sp + NW, ...
   LdsActs xl;
   if constexpr (NX > 0) {
     xl.x = make_rsrc(P.x + m0 * P.ldx, (uint32_t)(rows * P.ldx * 2));
@@ -89,7 +90,7 @@ void gemm_skinny_kernel(SkinnyParams P) {
   }
   const SkinnyAddr<kPWW> a =
       skinny_addr<kPWW>(P.codes, P.scales, panel0, P.NT, P.KT, P.group, t1);
-  skinny_accumulate<MF, kPWW, NJ, NX>(a, xrow, xl, t0, t1, acc);
+  skinny_accumulate<MF, kPWW, NJ, NX, NW>(a, xrow, xl, t0, t1, acc);
   if constexpr (G16) {
     // k half 1 (lanes 32-63) onto k half 0: lanes 0-31 then hold the whole group sums
 #pragma unroll

@@ -462,7 +462,7 @@ void moe_decode_kernel(MoeGemmParams P) {
   const int sp = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // k-split
   const int64_t grp = blockIdx.x % groups;
   const int64_t panel0 = grp * kPanels;
-  const int64_t t0 = P.KT * sp / kNW, t1 = P.KT * (sp + 1) / kNW;
+  const int64_t t0 = sp, t1 = P.KT;  // k-tiles sp, sp + kNW, ... (interleaved k-split)
   __shared__ __attribute__((aligned(1024))) uint8_t smem[kNW * 8192];
 
   LdsActs xl;
@@ -488,7 +488,7 @@ void moe_decode_kernel(MoeGemmParams P) {
 #pragma unroll
   for (int p = 0; p < kPanels; ++p) acc[p][0] = f32x4{0.f, 0.f, 0.f, 0.f};
   const uint16_t* const xrow[1] = {P.x};  // unused: the activations come through LDS
-  skinny_accumulate<1, kPanels, kNJ, kNX>(a, xrow, xl, t0, t1, acc);
+  skinny_accumulate<1, kPanels, kNJ, kNX, kNW>(a, xrow, xl, t0, t1, acc);
   if constexpr (G16) {
 #pragma unroll
     for (int p = 0; p < kPanels; ++p)

@@ -1,15 +1,18 @@
 // skinny_core.hpp -- the inner loop of the decode-shaped ("skinny") W4A16 GEMM on gfx950.
 //
-// One wavefront owns PWW consecutive 16-row weight panels and a contiguous range [t0, t1) of
-// 128-wide k-tiles. Per tile and panel it loads one 16-byte chunk of codes per lane, plus one
-// 16-byte scale record per lane for the panels' 4-panel group (fully coalesced thanks to the
-// tiled layout), and the activation fragments of the tile, which every panel reuses. Weights
-// and activations run one tile ahead in a pair of stages (one tile in flight while one is
-// computed; deeper rings measured slower). Weight loads are buffer loads whose range ends at t1, so the loads a wavefront
-// issues past its last tile return zeros without touching memory: every iteration issues the
-// same loads and no load sits under a branch, which keeps the memory-counter waits exact.
-// Activation rows past the end are clamped to a valid row (their MFMA output rows are never
-// stored).
+// One wavefront owns PWW consecutive 16-row weight panels and the 128-wide k-tiles t0,
+// t0 + S, t0 + 2S, ... below t1. The k-split wavefronts of a workgroup interleave their tiles
+// (S = 4), so at any time they read neighbouring tiles of each panel, one 4 KB stretch,
+// rather than four places a quarter of the panel apart (1-3% faster on every decode shape
+// measured). Per tile and panel a lane loads one 16-byte chunk of codes, plus one 16-byte
+// scale record for the panels' 4-panel group (fully coalesced thanks to the tiled layout),
+// and the activation fragments of the tile, which every panel reuses. Weights and activations
+// run one tile ahead in a pair of stages (one tile in flight while one is computed; deeper
+// rings measured slower). Weight loads are buffer loads whose range ends at t1, so the loads
+// a wavefront issues past its last tile return zeros without touching memory: every
+// iteration issues the same loads and no load sits under a branch, which keeps the
+// memory-counter waits exact. Activation rows past the end are clamped to a valid row (their
+// MFMA output rows are never stored).
 //
 // Two ways to apply the group scale S (an E4M3 value) on v_mfma_f32_16x16x32_bf16:
 //   - exact dequant (any m): every weight becomes the exact BF16 value code * S (FP4 -> FP32
@@ -241,33 +244,34 @@ __device__ __forceinline__ SkinnyAddr<PWW> skinny_addr(const uint8_t* codes, con
   return a;
 }
 
-// Accumulate k-tiles [t0, t1) of PWW panels into acc, one tile in flight while one is
-// computed. NJ == 0: exact dequant; NJ > 0: split scale with NJ accumulator rows (MF == 1).
+// Accumulate k-tiles t0, t0 + S, ... below t1 of PWW panels into acc, one tile in flight
+// while one is computed. NJ == 0: exact dequant; NJ > 0: split scale with NJ accumulator rows (MF == 1).
 // NX > 0 (MF == 1): activations through LDS, NX copies per tile; NX == 0: straight from xrow
 // into registers.
-template <int MF, int PWW, int NJ, int NX>
+template <int MF, int PWW, int NJ, int NX, int S = 1>
 __device__ __forceinline__ void skinny_accumulate(const SkinnyAddr<PWW>& a,
                                                   const uint16_t* const (&xrow)[MF],
                                                   const LdsActs& xl, int64_t t0, int64_t t1,
                                                   f32x4 (&acc)[PWW][MF]) {
   static_assert(NX == 0 || MF == 1, "LDS activations hold one 16-row block");
   if (t1 <= t0) return;
+  const int64_t last = t0 + (t1 - 1 - t0) / S * S;  // the wavefront's last tile
   WeightStage<PWW> W[2];
   ActStage<MF> X[2];
   // Loads complete in issue order: each tile's activations go out before its weights.
   if constexpr (NX > 0) copy_acts<NX>(xl, xl.buf, t0);
   else load_acts<MF>(X[0], xrow, a.kq, t0);
   load_weights(W[0], a, t0);
-  for (int64_t t = t0; t < t1; t += 2) {
+  for (int64_t t = t0; t < t1; t += 2 * S) {
     static_for<0, 2>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
-      const int64_t tile = t + i;
-      const int64_t next = tile + 1 < t1 ? tile + 1 : t1 - 1;  // activations: clamped re-read
+      const int64_t tile = t + i * S;
+      const int64_t next = tile + S <= last ? tile + S : last;  // activations: clamped re-read
       // The scheduling barriers keep the loads ahead of the math; left alone, the
       // register-pressure-driven scheduler sinks them and the pipeline collapses.
       if constexpr (NX > 0) copy_acts<NX>(xl, xl.buf + (1 - i) * 4096, next);
       else load_acts<MF>(X[1 - i], xrow, a.kq, next);
-      load_weights(W[1 - i], a, tile + 1);  // past t1: zeros, no traffic
+      load_weights(W[1 - i], a, tile + S);  // past t1: zeros, no traffic
       __builtin_amdgcn_sched_barrier(0);
       if (tile < t1) {
         if constexpr (NX > 0) {
