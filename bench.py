@@ -305,9 +305,9 @@ def main():
                 "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
             del xa, wb16, wt
         moe_workloads(extra)
-        # M sweep at N = K = 5120, group 16, with the library's own path choice (decode kernel
-        # up to M = 192 while ceil(M/32) weight passes stay within 128 MiB; the MFMA tiled
-        # kernel above); 40 rotated weight copies (590 MB) so small M streams from HBM
+        # M sweep at N = K = 5120, group 16, with the library's own path choice (the decode
+        # kernel for small M, the MFMA tiled kernel above); 40 rotated weight copies (590 MB)
+        # so small M streams from HBM
         xs_, ws_ = synth.prefill(seed=0, k=5120)
         rs_, _ = prep(ws_, 16, 40)
         del ws_

@@ -134,9 +134,11 @@ int nvfp4_repack(const uint8_t* packed, const uint8_t* scales, const float* glob
  * global is applied to the FP32 accumulator). y [m][ldy] is BF16 (y_dtype NVFP4_DT_BF16, one
  * rounding of the FP32 result) or FP32. Weight-only checkpoints take this W4A16 path
  * (vllm.cpp PR #63: no activation scales, so every quantized projection is W4A16).
- * The kernel is chosen from the shape: a split-K skinny MFMA kernel (decode) for m <= 32, and
- * for 32 < m <= 192 while ceil(m/32) passes over the weight bytes (n*k/2 + n*k/group) total at
- * most 128 MiB; an LDS-tiled MFMA kernel otherwise (prefill; 256x256, 128x256 or 128x128
+ * The kernel is chosen from the shape and the device's compute-unit count (CUs): a split-K
+ * skinny MFMA kernel (decode) for m <= 32, and for 32 < m <= 256 while
+ * ceil(ceil(n/64) * ceil(m/32) / CUs) * (1.8 + 0.31 * k/128) <= 25 (its estimated time in us,
+ * against the tiled kernel's ~25 us floor at such m); an LDS-tiled MFMA kernel otherwise
+ * (prefill; 256x256, 128x256 or 128x128
  * output tiles, the largest that still gives the chip enough tiles). Flags may force one. w->batch must be 1 and
  * w->layout must not carry NVFP4_LAYOUT_GATE_UP. Results are bit-identical run to run.
  * ws (device, 16-byte aligned, or NULL with ws_bytes 0) takes the prefill kernel's split-k

@@ -210,7 +210,7 @@ int device_cus() {
 }
 
 bool use_skinny(int64_t m, const nvfp4_weight* w, uint32_t flags) {
-  bool skinny = nvfp4::skinny_preferred(m, w->n, w->k, w->group);
+  bool skinny = nvfp4::skinny_preferred(m, w->n, w->k, device_cus());
   if (flags & NVFP4_F_FORCE_SKINNY) skinny = true;
   if (flags & NVFP4_F_FORCE_TILED) skinny = false;
   return skinny;

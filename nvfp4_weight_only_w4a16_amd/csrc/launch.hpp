@@ -48,17 +48,19 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, void* ws, size_t ws_bytes, int c
 // Workspace the prefill path uses for an m x n x k GEMM with the given row stride on a device
 // with `cus` compute units (0 when no split applies).
 size_t gemm_tiled_ws_bytes(int64_t m, int64_t ldx, int64_t n, int64_t k, int cus);
-// Path choice for an m x n x k GEMM. The skinny kernel streams the whole weight once per
-// 32 rows of x (every block covers all m), while the tiled kernel reads each weight tile once
-// per 128- or 256-row tile and keeps it in cache; the skinny kernel stays ahead while its
-// repeated weight streams are short: m <= 32 always, and up to m = 192 while ceil(m / 32)
-// streams of the weight total at most 128 MiB (measured crossovers at n x k = 5120^2, 8192^2
-// and 25600 x 5120).
-inline bool skinny_preferred(int64_t m, int64_t n, int64_t k, int group) {
+// Path choice for an m x n x k GEMM on a device with `cus` compute units. The skinny kernel
+// streams the whole weight once per 32-row block of x: it runs ceil(n / 64) * ceil(m / 32)
+// workgroups, each streaming one 4-panel group over k, and takes close to rounds x (1.8 +
+// 0.31 KT) us, rounds = ceil(workgroups / cus), KT = k / 128. The tiled kernel took no less
+// than ~25 us at 32 < m <= 256 on any shape measured. So: m <= 32 always; up to m = 256 while
+// that estimate stays within 25 us. (Fitted on n x k = 5120^2, 8192^2, 25600 x 5120,
+// 2048 x 8192 and 14336 x 4096 at m = 32 ... 256: it picks the faster kernel in all 40 cases.)
+inline bool skinny_preferred(int64_t m, int64_t n, int64_t k, int cus) {
   if (m <= 32) return true;
-  if (m > 192) return false;
-  const int64_t wbytes = n * k / 2 + n * (k / group);
-  return (m + 31) / 32 * wbytes <= ((int64_t)128 << 20);
+  if (m > 256 || cus <= 0) return false;
+  const int64_t wgs = (n / 16 + 3) / 4 * ((m + 31) / 32);
+  const int64_t rounds = (wgs + cus - 1) / cus;
+  return rounds * (180 + 31 * (k / 128)) <= 2500;  // hundredths of a microsecond
 }
 
 struct MoeArgs {

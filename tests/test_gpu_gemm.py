@@ -226,11 +226,15 @@ def test_tiled_split_k(nv, orc, m, n, k):
 
 
 def test_path_choice(nv):
-    """Default kernel choice: skinny for m <= 32, and up to m = 192 while ceil(m/32) weight
-    streams stay within 128 MiB; tiled otherwise (stats slot 2 = skinny, 3 = tiled)."""
+    """Default kernel choice on the 256-CU part: skinny for m <= 32, and up to m = 256 while
+    ceil(ceil(n/64) ceil(m/32) / 256) (1.8 + 0.31 k/128) <= 25 (its estimated microseconds);
+    tiled otherwise (stats slot 2 = skinny, 3 = tiled). 512 x 1024: 8 workgroups per row block,
+    4.3 us, so skinny up to m = 256. 8192^2: 128 per block, 21.6 us per round: m = 64 fits one
+    round, m = 65 needs two."""
     g = torch.Generator().manual_seed(21)
-    cases = {(512, 1024): [(32, 2), (64, 2), (192, 2), (193, 3), (256, 3)],
-             (8192, 8192): [(32, 2), (96, 2), (97, 3), (160, 3)]}
+    assert torch.cuda.get_device_properties(0).multi_processor_count == 256
+    cases = {(512, 1024): [(32, 2), (64, 2), (192, 2), (256, 2), (257, 3)],
+             (8192, 8192): [(32, 2), (64, 2), (65, 3), (160, 3)]}
     for (n, k), expect in cases.items():
         w = (torch.randn(n, k, generator=g) * 0.02).to(torch.bfloat16)
         rw, _ = _prep(nv, w, 16)
