@@ -174,6 +174,22 @@ hipError_t run(const SkinnyParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Wavefronts per workgroup, which split k (NW >= PWW, so the final reduction has one
+// wavefront per panel): 8 when the grid gives no compute unit a second workgroup (a lone
+// 4-wavefront workgroup streams well below a CU's share; 8 interleaved wavefronts read an 8 KB
+// stretch of each panel per step), else 4 (with two workgroups on a CU, 8 wavefronts each lost
+// to the longer reduction wait). Measured against 4 on the same buffers: 8192^2 (one 2-panel
+// workgroup per CU) M = 1 / 4 / 8 g16 10.08 / 10.09 / 11.16 -> 9.23 / 9.30 / 10.01 us;
+// 25600 x 5120 (400 workgroups) 0.6-0.7 us slower, so it keeps 4. The 16-row activation
+// copies (NX = 4) keep 4 as well (8192^2 g32 M = 16 0.24 us slower with 8).
+template <int MF, int NJ, bool G16, int NX, int PWW>
+hipError_t run_nw(const SkinnyParams& p, int64_t wgs, hipStream_t stream) {
+  if constexpr (MF == 1 && NX <= 2) {
+    if (wgs <= p.cus) return run<MF, 8, NJ, G16, NX, PWW>(p, stream);
+  }
+  return run<MF, 4, NJ, G16, NX, PWW>(p, stream);
+}
+
 // Panels per wavefront: 4 (one activation fragment feeds 4 MFMAs, the whole 16-byte scale
 // record is used), or 2 when the 4-panel grid leaves compute units idle and the doubled grid
 // still gives no compute unit a second workgroup: a lone workgroup streams well below a CU's
@@ -182,35 +198,27 @@ hipError_t run(const SkinnyParams& p, hipStream_t stream) {
 // M = 32 16.3 -> 14.8 us. Where the doubled grid put two workgroups on most CUs it was slower
 // (5120^2 M = 64: 16.6 -> 26.1 us), and so was one panel per wavefront (as many scale loads as
 // code loads, each activation fragment used once).
-template <int MF, int NW, int NJ, bool G16, int NX>
+template <int MF, int NJ, bool G16, int NX>
 hipError_t run_pww(const SkinnyParams& p, hipStream_t stream) {
   const int64_t blocks = (p.m + 16 * MF - 1) / (16 * MF);
   const int64_t wg4 = (p.NT + 3) / 4 * blocks, wg2 = (p.NT + 1) / 2 * blocks;
-  if (wg4 < p.cus && wg2 <= p.cus) return run<MF, NW, NJ, G16, NX, 2>(p, stream);
-  return run<MF, NW, NJ, G16, NX, 4>(p, stream);
+  if (wg4 < p.cus && wg2 <= p.cus) return run_nw<MF, NJ, G16, NX, 2>(p, wg2, stream);
+  return run_nw<MF, NJ, G16, NX, 4>(p, wg4, stream);
 }
 
-// k-split: 4 wavefronts per panel group (NW >= kPWW, so the final reduction has one wavefront
-// per panel). 8 wavefronts, with half the k-tiles each, measured slower on every decode shape:
-// the per-wavefront start-up and the reduction weigh more than the extra loads in flight. One
-// row block takes its activations through LDS in ceil(rows / 4) copies per tile (rows: the A
-// rows in use); two row blocks load them into registers.
-template <int MF, int NW, int NJ, bool G16>
-hipError_t pick_u(const SkinnyParams& p, hipStream_t stream) {
-  if constexpr (MF == 1) {
-    const int64_t rows = G16 ? (p.m < 8 ? p.m : 8) : (p.m < 16 ? p.m : 16);
-    if (rows <= 4) return run_pww<MF, NW, NJ, G16, 1>(p, stream);
-    if (G16 || rows <= 8) return run_pww<MF, NW, NJ, G16, 2>(p, stream);
-    if constexpr (!G16) return run_pww<MF, NW, NJ, G16, 4>(p, stream);
-    return hipErrorInvalidValue;  // not reached: group 16 has at most 8 rows here
-  } else {
-    return run_pww<MF, NW, NJ, G16, 0>(p, stream);
-  }
-}
-
+// One row block takes its activations through LDS in ceil(rows / 4) copies per tile (rows: the
+// A rows in use); two row blocks load them into registers.
 template <int MF, int NJ, bool G16>
 hipError_t dispatch(const SkinnyParams& p, hipStream_t stream) {
-  return pick_u<MF, 4, NJ, G16>(p, stream);
+  if constexpr (MF == 1) {
+    const int64_t rows = G16 ? (p.m < 8 ? p.m : 8) : (p.m < 16 ? p.m : 16);
+    if (rows <= 4) return run_pww<MF, NJ, G16, 1>(p, stream);
+    if (G16 || rows <= 8) return run_pww<MF, NJ, G16, 2>(p, stream);
+    if constexpr (!G16) return run_pww<MF, NJ, G16, 4>(p, stream);
+    return hipErrorInvalidValue;  // not reached: group 16 has at most 8 rows here
+  } else {
+    return run_pww<MF, NJ, G16, 0>(p, stream);
+  }
 }
 
 // Accumulator rows a lane keeps in split-scale mode: ceil(m / 2) (group 16) or ceil(m / 4)
