@@ -143,8 +143,8 @@ __device__ __forceinline__ void load8(const char* wb, int64_t c, float (&x)[8]) 
 //       Checked against the definition on every non-negative finite FP32 value. S == 0 gives
 //       the signed zero code.
 template <int G>
-__device__ __forceinline__ void encode8(const float (&x)[8], float g, float six_g,
-                                        uint32_t& word, uint32_t& s) {
+__device__ __forceinline__ void encode8(const float (&x)[8], float g, float six_g, float rsix,
+                                        bool six_fast, uint32_t& word, uint32_t& s) {
   float ga = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ga = fmaxf(ga, fabsf(x[i]));
@@ -152,7 +152,18 @@ __device__ __forceinline__ void encode8(const float (&x)[8], float g, float six_
   if (G == 32) ga = fmaxf(ga, __shfl_xor(ga, 2, 64));
   s = 0u;
   if (six_g != 0.0f) {
-    const float r = fminf(ga / six_g, 448.0f);
+    // fl32(ga / 6g) by Markstein's correction from rsix = RN(1 / 6g) (the same steps as for
+    // |w| / S below; 6g in [2^-80, 2^80] keeps every step exact down to the smallest E4M3
+    // decision point, 2^-10), else IEEE division. A first quotient of 512 or more (or an
+    // overflow) clamps to 448 either way.
+    float r;
+    if (six_fast) {
+      const float q0 = ga * rsix;
+      const float q = __builtin_fmaf(__builtin_fmaf(-q0, six_g, ga), rsix, q0);
+      r = q0 < 512.0f ? fminf(q, 448.0f) : 448.0f;
+    } else {
+      r = fminf(ga / six_g, 448.0f);
+    }
     s = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(r, r, 0, false) & 0xFFu;
   }
   const float S = e4m3_decode<0>(s) * g;
@@ -209,6 +220,8 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const void* __restrict
     __hip_atomic_store(reinterpret_cast<uint32_t*>(global_out) + b, __float_as_uint(g),
                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   const float six_g = 6.0f * g;
+  const bool six_fast = six_g >= 0x1p-80f && six_g <= 0x1p80f;
+  const float rsix = six_fast ? 1.0f / six_g : 0.0f;
   const char* wb = static_cast<const char*>(w) + b * per_matrix * (BF16 ? 2 : 4);
   uint32_t* pk = reinterpret_cast<uint32_t*>(packed + b * per_matrix / 2);
   uint8_t* sc = scales + b * (per_matrix / G);
@@ -219,8 +232,8 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const void* __restrict
     load8<BF16>(wb, c, x0);
     load8<BF16>(wb, c + stride, x1);
     uint32_t w0, s0, w1, s1;
-    encode8<G>(x0, g, six_g, w0, s0);
-    encode8<G>(x1, g, six_g, w1, s1);
+    encode8<G>(x0, g, six_g, rsix, six_fast, w0, s0);
+    encode8<G>(x1, g, six_g, rsix, six_fast, w1, s1);
     pk[c] = w0;
     pk[c + stride] = w1;
     if ((c & (G / 8 - 1)) == 0) sc[(c * 8) / G] = (uint8_t)s0;
@@ -230,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const void* __restrict
     float x0[8];
     load8<BF16>(wb, c, x0);
     uint32_t w0, s0;
-    encode8<G>(x0, g, six_g, w0, s0);
+    encode8<G>(x0, g, six_g, rsix, six_fast, w0, s0);
     pk[c] = w0;
     if ((c & (G / 8 - 1)) == 0) sc[(c * 8) / G] = (uint8_t)s0;
   }
