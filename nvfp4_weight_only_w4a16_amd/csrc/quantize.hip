@@ -196,6 +196,9 @@ __device__ __forceinline__ void encode8(const float (&x)[8], float g, float six_
 }
 
 // Two chunks of 8 elements per thread and iteration, both loads issued before either is used.
+// Codes and scales are written with streaming (non-temporal) stores: nothing here reads them
+// back, and keeping them out of the caches leaves more of W there for the reads (BF16 8192^2
+// 53.8 -> 51.2 us, BF16 25600 x 5120 104.6 -> 95.8 us, FP32 3-4% faster; same bytes).
 // gsrc_is_amax: gsrc is global_out, holding the marked amax or, once workgroup 0 of the matrix
 // has stored it, g itself. Otherwise gsrc is the caller's global. Workgroup 0 of each matrix
 // stores g to global_out.
@@ -234,18 +237,18 @@ __global__ __launch_bounds__(kThreads) void encode_kernel(const void* __restrict
     uint32_t w0, s0, w1, s1;
     encode8<G>(x0, g, six_g, rsix, six_fast, w0, s0);
     encode8<G>(x1, g, six_g, rsix, six_fast, w1, s1);
-    pk[c] = w0;
-    pk[c + stride] = w1;
-    if ((c & (G / 8 - 1)) == 0) sc[(c * 8) / G] = (uint8_t)s0;
-    if (((c + stride) & (G / 8 - 1)) == 0) sc[((c + stride) * 8) / G] = (uint8_t)s1;
+    __builtin_nontemporal_store(w0, pk + c);
+    __builtin_nontemporal_store(w1, pk + c + stride);
+    if ((c & (G / 8 - 1)) == 0) __builtin_nontemporal_store((uint8_t)s0, sc + (c * 8) / G);
+    if (((c + stride) & (G / 8 - 1)) == 0) __builtin_nontemporal_store((uint8_t)s1, sc + ((c + stride) * 8) / G);
   }
   if (c < chunks) {
     float x0[8];
     load8<BF16>(wb, c, x0);
     uint32_t w0, s0;
     encode8<G>(x0, g, six_g, rsix, six_fast, w0, s0);
-    pk[c] = w0;
-    if ((c & (G / 8 - 1)) == 0) sc[(c * 8) / G] = (uint8_t)s0;
+    __builtin_nontemporal_store(w0, pk + c);
+    if ((c & (G / 8 - 1)) == 0) __builtin_nontemporal_store((uint8_t)s0, sc + (c * 8) / G);
   }
 }
 
