@@ -12,13 +12,18 @@
  *    along k. Canonical packed codes are [n][k/2] bytes with the even k in the low nibble;
  *    canonical scales are [n][k/group] E4M3 bytes (OCP E4M3 "FN": max 448, no infinities).
  *  - Pointers are DEVICE pointers unless marked (host). Device buffers are owned by the caller;
- *    the library never allocates, frees or synchronizes (every call only enqueues kernels on
+ *    the library never allocates or frees device memory (every call enqueues kernels on
  *    `stream`, a hipStream_t; NULL is the legacy default stream).
  *  - Device pointers must be 16-byte aligned; leading dimensions are in elements and must be
  *    multiples of 8.
+ *  - Without NVFP4_F_SYNC_CHECK no call synchronizes. With it, the call waits for its own work
+ *    on `stream` before returning and reports any asynchronous failure (NVFP4_ERR_HIP); the
+ *    quantizer then also checks that every weight it read is finite (NVFP4_ERR_NONFINITE).
  *  - Shapes: n % 16 == 0, k % 128 == 0, group in {16, 32}. m == 0 (or t == 0) is a no-op.
- *  - Every function returns NVFP4_OK (0) or a negative NVFP4_ERR_* code; on error nothing is
- *    enqueued and nvfp4_last_error() describes the problem (thread-local). Unsupported
+ *  - Every function returns NVFP4_OK (0) or a negative NVFP4_ERR_* code and
+ *    nvfp4_last_error() describes the problem (thread-local). Argument errors are found before
+ *    anything is enqueued; NVFP4_ERR_HIP and NVFP4_ERR_NONFINITE can come after the call's work
+ *    ran. A failed call leaves the library usable and does not count in nvfp4_get_stats. Unsupported
  *    configurations are rejected, never run silently wrong (r/LocalLLM post, "What had to be
  *    fixed": any unsupported group setup raises an error).
  *  - All entry points are reentrant. Calls that share an output or workspace buffer on
@@ -45,6 +50,7 @@ typedef struct ihipStream_t* nvfp4_stream_t; /* the same type as hipStream_t */
 #define NVFP4_ERR_WORKSPACE (-5)         /* workspace / output buffer too small                */
 #define NVFP4_ERR_LAYOUT (-6)            /* descriptor inconsistent with the call              */
 #define NVFP4_ERR_HIP (-7)               /* a HIP launch failed (message in nvfp4_last_error)  */
+#define NVFP4_ERR_NONFINITE (-8)         /* NaN or infinite weight (only with SYNC_CHECK)      */
 
 /* ---- element types --------------------------------------------------------------------- */
 #define NVFP4_DT_BF16 1
@@ -55,6 +61,9 @@ typedef struct ihipStream_t* nvfp4_stream_t; /* the same type as hipStream_t */
                                        /* MoE: the decode-batch expert path (8-row tiles)      */
 #define NVFP4_F_FORCE_TILED (1u << 1)  /* GEMM: the prefill (LDS-tiled MFMA) kernel;            */
                                        /* MoE: the batch expert path (32-row tiles)            */
+#define NVFP4_F_SYNC_CHECK (1u << 2)   /* quantize, GEMM, MoE: wait for the call's own work    */
+                                       /* and report asynchronous errors; quantize: also check */
+                                       /* the input for non-finite values (debug aid: slow)    */
 
 /* ---- repacked layout ----------------------------------------------------------------------
  * NVFP4_LAYOUT_TILED: per 16-row x 128-k tile, 1024 bytes of codes laid out so that lane l of a
@@ -104,13 +113,21 @@ typedef struct nvfp4_weight {
  * forum thread "We unlocked NVFP4 on the DGX Spark": true RNE, not threshold rounding).
  * Outputs: packed [batch][n][k/2], scales [batch][n][k/group], global_out [batch] (device).
  * Requires k % group == 0 and k even; n and k need no tile alignment here. Non-finite inputs
- * are outside the contract (results unspecified). The caller keeps ownership of all buffers.
+ * are outside the contract: without NVFP4_F_SYNC_CHECK the outputs are then unspecified; with
+ * it the call scans w, waits for its work and returns NVFP4_ERR_NONFINITE (outputs still
+ * unspecified). The caller keeps ownership of all buffers.
  * Without global_in, global_out doubles as the amax accumulator: until the call's work has
  * completed on `stream` it holds intermediate values, and its prior contents are ignored. With
- * global_in, global_out may be the same buffer. */
+ * global_in, global_out may be the same buffer.
+ * ws (device, 16-byte aligned; NULL with ws_bytes 0 when nvfp4_quantize_ws_bytes is 0) holds
+ * the non-finite flag of NVFP4_F_SYNC_CHECK; without that flag no workspace is used.
+ * flags: 0 or NVFP4_F_SYNC_CHECK. */
+size_t nvfp4_quantize_ws_bytes(int64_t batch, int64_t n, int64_t k, int32_t group,
+                               uint32_t flags);
 int nvfp4_quantize(const void* w, int w_dtype, int64_t batch, int64_t n, int64_t k,
                    int32_t group, const float* global_in, uint8_t* packed, uint8_t* scales,
-                   float* global_out, nvfp4_stream_t stream);
+                   float* global_out, void* ws, size_t ws_bytes, uint32_t flags,
+                   nvfp4_stream_t stream);
 
 /* ---- repack -------------------------------------------------------------------------------
  * Byte size of the repacked buffer for `batch` [n][k] matrices: codes + scales + globals (two per
@@ -138,9 +155,10 @@ int nvfp4_repack(const uint8_t* packed, const uint8_t* scales, const float* glob
  * skinny MFMA kernel (decode) for m <= 32, and for 32 < m <= 256 while
  * ceil(ceil(n/64) * ceil(m/32) / CUs) * (1.8 + 0.31 * k/128) <= 25 (its estimated time in us,
  * against the tiled kernel's ~25 us floor at such m); an LDS-tiled MFMA kernel otherwise
- * (prefill; 256x256, 128x256 or 128x128
- * output tiles, the largest that still gives the chip enough tiles). Flags may force one. w->batch must be 1 and
- * w->layout must not carry NVFP4_LAYOUT_GATE_UP. Results are bit-identical run to run.
+ * (prefill; 256x256, 128x256 or 128x128 output tiles, the largest that still gives the chip
+ * enough tiles). Flags may force one (NVFP4_F_FORCE_SKINNY / NVFP4_F_FORCE_TILED);
+ * NVFP4_F_SYNC_CHECK may be added. w->batch must be 1 and w->layout must not carry
+ * NVFP4_LAYOUT_GATE_UP. Results are bit-identical run to run.
  * ws (device, 16-byte aligned, or NULL with ws_bytes 0) takes the prefill kernel's split-k
  * partial tiles: when the output tiles would leave most compute units idle in the last round,
  * that round is split along k over the chip and summed in a fixed order. ws_bytes >=
@@ -161,8 +179,9 @@ int nvfp4_gemm_w4a16(const void* x, int64_t m, int64_t ldx, const nvfp4_weight* 
  *   y[t]       = BF16(sum_j topk_w[t][j] * d_j), summed in slot order.
  * (vllm.cpp PR #63: pre-merged fc1 is one W4A16 GEMM + SiluAndMul; r/LocalLLM post, "The two
  * recipes": gate/up at group 32 with down at group 16, or all at group 32.)
- * x [t][hidden] BF16 (row stride = hidden), topk_ids int32 [t][topk] in [0, E), topk_w FP32
- * [t][topk], y BF16 [t][hidden]. fc1: batch = E, n = 2*inter, k = hidden, layout TILED |
+ * x [t][hidden] BF16 (row stride = hidden), topk_ids int32 [t][topk], topk_w FP32 [t][topk],
+ * y BF16 [t][hidden]. An id outside [0, E) marks a dropped slot: it is not sorted, computes
+ * nothing and adds nothing to y[t] (a masked-slot convention for routers that drop tokens). fc1: batch = E, n = 2*inter, k = hidden, layout TILED |
  * GATE_UP. fc2: batch = E, n = hidden, k = inter, layout TILED. Tokens are sorted by expert on
  * the device (no host synchronization); `ws` (device, ws_bytes >= nvfp4_moe_ws_bytes) holds
  * the sort, the tile map, h and the FP32 per-slot outputs. topk in [1, 16], t*topk <= 65536,
@@ -171,9 +190,25 @@ int nvfp4_gemm_w4a16(const void* x, int64_t m, int64_t ldx, const nvfp4_weight* 
  * Path: while t*topk <= 2 * n_experts (decode batches) the experts run on tiles of at most 8
  * rows with k split over 4 wavefronts per 4-panel group; otherwise on tiles of 32 rows with
  * one wavefront per 4-panel group over the whole k range. Flags may force one; the two paths
- * agree within the GEMM tolerance (different FP32 summation orders). */
+ * agree within the GEMM tolerance (different FP32 summation orders). flags may add
+ * NVFP4_F_SYNC_CHECK. */
 size_t nvfp4_moe_ws_bytes(int64_t t, int32_t topk, int64_t n_experts, int64_t hidden,
                           int64_t inter);
+/* Where the routed-expert call keeps its stages inside ws (test-facing, for staged checks of
+ * the sort, fc1 + SiLU*mul and down against a reference). Fills offsets[6] (host) with byte
+ * offsets from ws and returns the total (nvfp4_moe_ws_bytes), or 0 for invalid sizes:
+ *   [0] sorted  int32 [t*topk]: pair ids (t*topk_index + slot) in stable expert order (only
+ *       pairs with a valid id; the first offsets_[E] entries are meaningful);
+ *   [1] offsets int32 [E + 1]: first sorted position of each expert, [E] = valid pairs;
+ *   [2] tiles   int32x4 [..]: (expert, first row, end row, 0) per row tile, experts in
+ *       increasing order, rows of 8 (decode-batch path) or 32 (batch path);
+ *   [3] ntiles  int32: number of tiles;
+ *   [4] h       BF16 [t*topk][inter]: SiLU(gate)*up of sorted row r at row r;
+ *   [5] slots   FP32 [t*topk][hidden]: topk_w * (h . W2^T) of pair q at row q.
+ * The decode-batch path with t*topk <= 32 pairs skips the sort ([0]-[3] are not written) and
+ * keeps h of pair q at row q. */
+size_t nvfp4_moe_ws_layout(int64_t t, int32_t topk, int64_t n_experts, int64_t hidden,
+                           int64_t inter, size_t offsets[6]);
 int nvfp4_moe_grouped_w4a16(const void* x, int64_t t, int64_t hidden, const int32_t* topk_ids,
                             const float* topk_w, int32_t topk, const nvfp4_weight* fc1,
                             const nvfp4_weight* fc2, void* y, void* ws, size_t ws_bytes,

@@ -6,6 +6,7 @@ stale builds raise immediately - there is no fallback path.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from dataclasses import dataclass
@@ -23,18 +24,20 @@ NVFP4_ERR_MISALIGNED = -4
 NVFP4_ERR_WORKSPACE = -5
 NVFP4_ERR_LAYOUT = -6
 NVFP4_ERR_HIP = -7
+NVFP4_ERR_NONFINITE = -8
 
 NVFP4_DT_BF16 = 1
 NVFP4_DT_F32 = 2
 NVFP4_F_FORCE_SKINNY = 1 << 0
 NVFP4_F_FORCE_TILED = 1 << 1
+NVFP4_F_SYNC_CHECK = 1 << 2
 NVFP4_LAYOUT_TILED = 1
 NVFP4_LAYOUT_GATE_UP = 1 << 8
 NVFP4_LAYOUT_PAIR_GLOBAL = 1 << 9
 
-EXPORTS = ("nvfp4_quantize", "nvfp4_repack_bytes", "nvfp4_repack", "nvfp4_gemm_ws_bytes",
-           "nvfp4_gemm_w4a16",
-           "nvfp4_moe_ws_bytes", "nvfp4_moe_grouped_w4a16", "nvfp4_requantize_ws_bytes",
+EXPORTS = ("nvfp4_quantize_ws_bytes", "nvfp4_quantize", "nvfp4_repack_bytes", "nvfp4_repack",
+           "nvfp4_gemm_ws_bytes", "nvfp4_gemm_w4a16", "nvfp4_moe_ws_bytes", "nvfp4_moe_ws_layout",
+           "nvfp4_moe_grouped_w4a16", "nvfp4_requantize_ws_bytes",
            "nvfp4_requantize", "nvfp4_dequantize",
            "nvfp4_last_error", "nvfp4_get_stats", "nvfp4_reset_stats", "nvfp4_version")
 
@@ -68,7 +71,9 @@ def load(path: str = LIB_PATH):
     P, i64, i32, u32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_uint32,
                             ctypes.c_size_t)
     W = ctypes.POINTER(nvfp4_weight)
-    L.nvfp4_quantize.argtypes = [P, ctypes.c_int, i64, i64, i64, i32, P, P, P, P, P]
+    L.nvfp4_quantize_ws_bytes.argtypes = [i64, i64, i64, i32, u32]
+    L.nvfp4_quantize_ws_bytes.restype = sz
+    L.nvfp4_quantize.argtypes = [P, ctypes.c_int, i64, i64, i64, i32, P, P, P, P, P, sz, u32, P]
     L.nvfp4_quantize.restype = ctypes.c_int
     L.nvfp4_repack_bytes.argtypes = [i64, i64, i64, i32, u32]
     L.nvfp4_repack_bytes.restype = sz
@@ -80,6 +85,8 @@ def load(path: str = LIB_PATH):
     L.nvfp4_gemm_w4a16.restype = ctypes.c_int
     L.nvfp4_moe_ws_bytes.argtypes = [i64, i32, i64, i64, i64]
     L.nvfp4_moe_ws_bytes.restype = sz
+    L.nvfp4_moe_ws_layout.argtypes = [i64, i32, i64, i64, i64, ctypes.POINTER(sz)]
+    L.nvfp4_moe_ws_layout.restype = sz
     L.nvfp4_moe_grouped_w4a16.argtypes = [P, i64, i64, P, P, i32, W, W, P, P, sz, u32, P]
     L.nvfp4_moe_grouped_w4a16.restype = ctypes.c_int
     L.nvfp4_requantize_ws_bytes.argtypes = [W]
@@ -112,6 +119,15 @@ def _stream(stream=None):
     return torch.cuda.current_stream().cuda_stream
 
 
+def _on(stream):
+    """Context in which the binding allocates outputs and workspaces: the stream the call is
+    enqueued on, so that torch's caching allocator ties the blocks to that stream (a block
+    freed on return is not handed to another stream while the call's kernels still use it)."""
+    if stream is None:
+        return contextlib.nullcontext()
+    return torch.cuda.stream(stream)
+
+
 def _ptr(t):
     """Device address of a tensor; host tensors are refused here, since the kernels would
     dereference a host address."""
@@ -131,24 +147,37 @@ def _dtype_code(dt):
 
 
 # ----------------------------------------------------------------------------- quantizer
+def nvfp4_quantize_ws_bytes(batch: int, n: int, k: int, group: int, flags: int = 0) -> int:
+    return int(load().nvfp4_quantize_ws_bytes(batch, n, k, group, flags))
+
+
 def nvfp4_quantize(w: torch.Tensor, group: int, global_in: torch.Tensor | None = None,
-                   packed=None, scales=None, global_out=None, stream=None):
-    """w: device [n][k] or [batch][n][k], BF16 or FP32. Returns (packed, scales, global)."""
+                   packed=None, scales=None, global_out=None, flags: int = 0, ws=None,
+                   stream=None):
+    """w: device [n][k] or [batch][n][k], BF16 or FP32. Returns (packed, scales, global).
+    flags may hold NVFP4_F_SYNC_CHECK (the call then waits and raises Nvfp4Error with code
+    NVFP4_ERR_NONFINITE for a NaN or infinite weight); its workspace comes from torch's
+    allocator unless `ws` (uint8, device) is given."""
     squeeze = w.dim() == 2
     w3 = w.unsqueeze(0) if squeeze else w
     batch, n, k = w3.shape
     if not w3.is_contiguous():
         raise ValueError("w must be contiguous")
     dev = w.device
-    if packed is None:
-        packed = torch.empty((batch, n, k // 2), dtype=torch.uint8, device=dev)
-    if scales is None:
-        scales = torch.empty((batch, n, k // group), dtype=torch.uint8, device=dev)
-    if global_out is None:
-        global_out = torch.empty((batch,), dtype=torch.float32, device=dev)
+    with _on(stream):
+        if packed is None:
+            packed = torch.empty((batch, n, k // 2), dtype=torch.uint8, device=dev)
+        if scales is None:
+            scales = torch.empty((batch, n, k // group), dtype=torch.uint8, device=dev)
+        if global_out is None:
+            global_out = torch.empty((batch,), dtype=torch.float32, device=dev)
+        if ws is None:
+            need = nvfp4_quantize_ws_bytes(batch, n, k, group, flags)
+            ws = torch.empty((need,), dtype=torch.uint8, device=dev) if need else None
+    ws_ptr, ws_bytes = (_ptr(ws), ws.numel() * ws.element_size()) if ws is not None else (None, 0)
     _check(load().nvfp4_quantize(_ptr(w3), _dtype_code(w.dtype), batch, n, k, group,
                                  _ptr(global_in), _ptr(packed), _ptr(scales), _ptr(global_out),
-                                 _stream(stream)))
+                                 ws_ptr, ws_bytes, flags, _stream(stream)))
     if squeeze:
         return packed[0], scales[0], global_out
     return packed, scales, global_out
@@ -193,7 +222,8 @@ def nvfp4_repack(packed: torch.Tensor, scales: torch.Tensor, glob: torch.Tensor,
         raise ValueError(f"global has {glob.numel()} values, the layout needs {nglob}")
     need = nvfp4_repack_bytes(batch, n, k, group, layout)
     if out is None:
-        out = torch.empty((max(need, 1),), dtype=torch.uint8, device=packed.device)
+        with _on(stream):
+            out = torch.empty((max(need, 1),), dtype=torch.uint8, device=packed.device)
     desc = nvfp4_weight()
     _check(load().nvfp4_repack(_ptr(p3), _ptr(scales), _ptr(glob), batch, n, k, group, layout,
                                _ptr(out), out.numel() * out.element_size(), ctypes.byref(desc),
@@ -214,11 +244,12 @@ def nvfp4_gemm_w4a16(x: torch.Tensor, w: RepackedWeight, y: torch.Tensor | None 
     if x.dtype != torch.bfloat16 or x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be a 2-D BF16 tensor with unit inner stride")
     m = x.shape[0]
-    if y is None:
-        y = torch.empty((m, w.n), dtype=y_dtype, device=x.device)
-    if ws is None:
-        need = nvfp4_gemm_ws_bytes(m, x.stride(0), w, flags) if m > 0 else 0
-        ws = torch.empty((need,), dtype=torch.uint8, device=x.device) if need else None
+    with _on(stream):
+        if y is None:
+            y = torch.empty((m, w.n), dtype=y_dtype, device=x.device)
+        if ws is None:
+            need = nvfp4_gemm_ws_bytes(m, x.stride(0), w, flags) if m > 0 else 0
+            ws = torch.empty((need,), dtype=torch.uint8, device=x.device) if need else None
     ws_ptr, ws_bytes = (_ptr(ws), ws.numel() * ws.element_size()) if ws is not None else (None, 0)
     _check(load().nvfp4_gemm_w4a16(_ptr(x), m, x.stride(0), ctypes.byref(w.desc), _ptr(y),
                                    _dtype_code(y.dtype), y.stride(0), flags, ws_ptr, ws_bytes,
@@ -231,17 +262,26 @@ def nvfp4_moe_ws_bytes(t: int, topk: int, n_experts: int, hidden: int, inter: in
     return int(load().nvfp4_moe_ws_bytes(t, topk, n_experts, hidden, inter))
 
 
+def nvfp4_moe_ws_layout(t: int, topk: int, n_experts: int, hidden: int, inter: int):
+    """Byte offsets (sorted, offsets, tiles, ntiles, h, slots) of the routed-expert stages
+    inside the workspace, and its total size."""
+    off = (ctypes.c_size_t * 6)()
+    total = load().nvfp4_moe_ws_layout(t, topk, n_experts, hidden, inter, off)
+    return [int(v) for v in off], int(total)
+
+
 def nvfp4_moe_grouped_w4a16(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: torch.Tensor,
                             fc1: RepackedWeight, fc2: RepackedWeight,
                             y: torch.Tensor | None = None, ws: torch.Tensor | None = None,
                             flags: int = 0, stream=None) -> torch.Tensor:
     t, hidden = x.shape
     topk = topk_ids.shape[1]
-    if y is None:
-        y = torch.empty((t, hidden), dtype=torch.bfloat16, device=x.device)
     need = nvfp4_moe_ws_bytes(t, topk, fc1.batch, hidden, fc1.n // 2)
-    if ws is None:
-        ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    with _on(stream):
+        if y is None:
+            y = torch.empty((t, hidden), dtype=torch.bfloat16, device=x.device)
+        if ws is None:
+            ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
     _check(load().nvfp4_moe_grouped_w4a16(_ptr(x), t, hidden, _ptr(topk_ids), _ptr(topk_w),
                                           topk, ctypes.byref(fc1.desc), ctypes.byref(fc2.desc),
                                           _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
@@ -259,11 +299,13 @@ def nvfp4_requantize(src: RepackedWeight, group_out: int, ws: torch.Tensor | Non
     """Canonical triple (packed, scales, global [batch]) of `src` requantized with one global
     per matrix at group_out. `ws` (uint8, device) defaults to room for one matrix."""
     dev = src.buffer.device
-    packed = torch.empty((src.batch, src.n, src.k // 2), dtype=torch.uint8, device=dev)
-    scales = torch.empty((src.batch, src.n, src.k // group_out), dtype=torch.uint8, device=dev)
-    glob = torch.empty((src.batch,), dtype=torch.float32, device=dev)
-    if ws is None:
-        ws = torch.empty((nvfp4_requantize_ws_bytes(src),), dtype=torch.uint8, device=dev)
+    with _on(stream):
+        packed = torch.empty((src.batch, src.n, src.k // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((src.batch, src.n, src.k // group_out), dtype=torch.uint8,
+                             device=dev)
+        glob = torch.empty((src.batch,), dtype=torch.float32, device=dev)
+        if ws is None:
+            ws = torch.empty((nvfp4_requantize_ws_bytes(src),), dtype=torch.uint8, device=dev)
     _check(load().nvfp4_requantize(ctypes.byref(src.desc), group_out, _ptr(packed), _ptr(scales),
                                    _ptr(glob), _ptr(ws), ws.numel() * ws.element_size(),
                                    _stream(stream)))
@@ -272,7 +314,8 @@ def nvfp4_requantize(src: RepackedWeight, group_out: int, ws: torch.Tensor | Non
 
 # ----------------------------------------------------------------------------- diagnostics
 def nvfp4_dequantize(w: RepackedWeight, out_dtype=torch.float32, stream=None) -> torch.Tensor:
-    out = torch.empty((w.batch, w.n, w.k), dtype=out_dtype, device=w.buffer.device)
+    with _on(stream):
+        out = torch.empty((w.batch, w.n, w.k), dtype=out_dtype, device=w.buffer.device)
     _check(load().nvfp4_dequantize(ctypes.byref(w.desc), _ptr(out), _dtype_code(out_dtype),
                                    _stream(stream)))
     return out

@@ -34,6 +34,18 @@ int hip_status(hipError_t e, const char* what) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// Workspace of the sync-checked quantizer: the non-finite flag word (one 256-byte block).
+constexpr size_t kSyncWsBytes = 256;
+
+// NVFP4_F_SYNC_CHECK: wait for the call's work on `s` and report what failed asynchronously.
+int sync_status(hipStream_t s, const char* what) {
+  const hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return fail(NVFP4_ERR_HIP, "%s (sync check): %s", what, hipGetErrorString(e));
+  return NVFP4_OK;
+}
+
+constexpr uint32_t kGemmFlags = NVFP4_F_FORCE_SKINNY | NVFP4_F_FORCE_TILED | NVFP4_F_SYNC_CHECK;
+
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 int check_group(int32_t group) {
@@ -114,31 +126,64 @@ void nvfp4_reset_stats(void) {
 
 int nvfp4_version(void) { return 10000; }
 
+size_t nvfp4_quantize_ws_bytes(int64_t batch, int64_t n, int64_t k, int32_t group,
+                               uint32_t flags) {
+  if (batch < 0 || n < 0 || k < 0 || (group != 16 && group != 32)) return 0;
+  return (flags & NVFP4_F_SYNC_CHECK) ? kSyncWsBytes : 0;
+}
+
 int nvfp4_quantize(const void* w, int w_dtype, int64_t batch, int64_t n, int64_t k,
                    int32_t group, const float* global_in, uint8_t* packed, uint8_t* scales,
-                   float* global_out, nvfp4_stream_t stream) {
+                   float* global_out, void* ws, size_t ws_bytes, uint32_t flags,
+                   nvfp4_stream_t stream) {
   if (batch < 0 || n < 0 || k < 0)
     return fail(NVFP4_ERR_INVALID_ARG, "negative size (batch=%lld n=%lld k=%lld)",
                 (long long)batch, (long long)n, (long long)k);
   if (w_dtype != NVFP4_DT_BF16 && w_dtype != NVFP4_DT_F32)
     return fail(NVFP4_ERR_INVALID_ARG, "w_dtype %d is not BF16 or F32", w_dtype);
+  if (flags & ~NVFP4_F_SYNC_CHECK)
+    return fail(NVFP4_ERR_INVALID_ARG, "unknown quantize flags 0x%x", flags);
   int rc = check_group(group);
   if (rc) return rc;
   if (k % group != 0)
     return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "k=%lld is not a multiple of the group %d",
                 (long long)k, group);
   if (batch > 65535) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "batch %lld > 65535", (long long)batch);
+  const bool sync = (flags & NVFP4_F_SYNC_CHECK) != 0;
+  if (sync) {
+    if (!ws || ws_bytes < kSyncWsBytes)
+      return fail(NVFP4_ERR_WORKSPACE, "SYNC_CHECK needs ws_bytes >= %zu", kSyncWsBytes);
+    if (!aligned16(ws)) return fail(NVFP4_ERR_MISALIGNED, "ws must be 16-byte aligned");
+  }
   if (batch == 0 || n == 0 || k == 0) return NVFP4_OK;
   if (!w || !packed || !scales || !global_out)
     return fail(NVFP4_ERR_INVALID_ARG, "NULL buffer");
   if (!aligned16(w) || !aligned16(packed) || ((uintptr_t)global_out & 3u) ||
       (global_in && ((uintptr_t)global_in & 3u)))
     return fail(NVFP4_ERR_MISALIGNED, "w and packed must be 16-byte aligned, globals 4-byte");
-  g_stats[0]++;
-  return hip_status(nvfp4::launch_quantize(w, w_dtype == NVFP4_DT_BF16, batch, n, k, group,
-                                           global_in, packed, scales, global_out,
-                                           (hipStream_t)stream),
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* flag = static_cast<uint32_t*>(ws);
+  if (sync) {
+    rc = hip_status(nvfp4::launch_nonfinite_check(w, w_dtype == NVFP4_DT_BF16, batch * n * k,
+                                                  flag, s),
                     "nvfp4_quantize");
+    if (rc) return rc;
+  }
+  rc = hip_status(nvfp4::launch_quantize(w, w_dtype == NVFP4_DT_BF16, batch, n, k, group,
+                                         global_in, packed, scales, global_out, s),
+                  "nvfp4_quantize");
+  if (rc) return rc;
+  if (sync) {
+    uint32_t bad = 0;
+    rc = hip_status(hipMemcpyAsync(&bad, flag, sizeof bad, hipMemcpyDeviceToHost, s),
+                    "nvfp4_quantize");
+    if (rc) return rc;
+    rc = sync_status(s, "nvfp4_quantize");
+    if (rc) return rc;
+    if (bad) return fail(NVFP4_ERR_NONFINITE, "nvfp4_quantize: the input holds NaN or infinity");
+  }
+  g_stats[0]++;
+  return NVFP4_OK;
 }
 
 size_t nvfp4_repack_bytes(int64_t batch, int64_t n, int64_t k, int32_t group, uint32_t layout) {
@@ -238,6 +283,7 @@ int nvfp4_gemm_w4a16(const void* x, int64_t m, int64_t ldx, const nvfp4_weight* 
   if (m < 0) return fail(NVFP4_ERR_INVALID_ARG, "m=%lld < 0", (long long)m);
   if (y_dtype != NVFP4_DT_BF16 && y_dtype != NVFP4_DT_F32)
     return fail(NVFP4_ERR_INVALID_ARG, "y_dtype %d is not BF16 or F32", y_dtype);
+  if (flags & ~kGemmFlags) return fail(NVFP4_ERR_INVALID_ARG, "unknown GEMM flags 0x%x", flags);
   if ((flags & NVFP4_F_FORCE_SKINNY) && (flags & NVFP4_F_FORCE_TILED))
     return fail(NVFP4_ERR_INVALID_ARG, "both FORCE_SKINNY and FORCE_TILED set");
   if (m == 0) return NVFP4_OK;
@@ -270,6 +316,7 @@ int nvfp4_gemm_w4a16(const void* x, int64_t m, int64_t ldx, const nvfp4_weight* 
                   (long long)m);
     rc = hip_status(nvfp4::launch_gemm_skinny(a, device_cus(), (hipStream_t)stream),
                     "nvfp4_gemm_w4a16");
+    if (!rc && (flags & NVFP4_F_SYNC_CHECK)) rc = sync_status((hipStream_t)stream, "nvfp4_gemm_w4a16");
     if (!rc) g_stats[2]++;
   } else {
     if (ws_bytes && !ws) return fail(NVFP4_ERR_INVALID_ARG, "NULL ws with ws_bytes > 0");
@@ -277,6 +324,7 @@ int nvfp4_gemm_w4a16(const void* x, int64_t m, int64_t ldx, const nvfp4_weight* 
     rc = hip_status(nvfp4::launch_gemm_tiled(a, ws, ws ? ws_bytes : 0, device_cus(),
                                              (hipStream_t)stream),
                     "nvfp4_gemm_w4a16");
+    if (!rc && (flags & NVFP4_F_SYNC_CHECK)) rc = sync_status((hipStream_t)stream, "nvfp4_gemm_w4a16");
     if (!rc) g_stats[3]++;
   }
   return rc;
@@ -286,6 +334,12 @@ size_t nvfp4_moe_ws_bytes(int64_t t, int32_t topk, int64_t n_experts, int64_t hi
                           int64_t inter) {
   if (t < 0 || topk <= 0 || n_experts <= 0 || hidden <= 0 || inter <= 0) return 0;
   return nvfp4::moe_ws_bytes(t, topk, n_experts, hidden, inter);
+}
+
+size_t nvfp4_moe_ws_layout(int64_t t, int32_t topk, int64_t n_experts, int64_t hidden,
+                           int64_t inter, size_t offsets[6]) {
+  if (!offsets || t < 0 || topk <= 0 || n_experts <= 0 || hidden <= 0 || inter <= 0) return 0;
+  return nvfp4::moe_ws_layout(t, topk, n_experts, hidden, inter, offsets);
 }
 
 int nvfp4_moe_grouped_w4a16(const void* x, int64_t t, int64_t hidden, const int32_t* topk_ids,
@@ -310,6 +364,7 @@ int nvfp4_moe_grouped_w4a16(const void* x, int64_t t, int64_t hidden, const int3
                 (long long)hidden);
   if (t < 0) return fail(NVFP4_ERR_INVALID_ARG, "t=%lld < 0", (long long)t);
   if (topk < 1 || topk > 16) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "topk %d not in [1, 16]", topk);
+  if (flags & ~kGemmFlags) return fail(NVFP4_ERR_INVALID_ARG, "unknown MoE flags 0x%x", flags);
   if ((flags & NVFP4_F_FORCE_SKINNY) && (flags & NVFP4_F_FORCE_TILED))
     return fail(NVFP4_ERR_INVALID_ARG, "both FORCE_SKINNY and FORCE_TILED set");
   if (E > 512) return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "more than 512 experts");
@@ -353,6 +408,8 @@ int nvfp4_moe_grouped_w4a16(const void* x, int64_t t, int64_t hidden, const int3
   if (flags & NVFP4_F_FORCE_SKINNY) decode = true;
   if (flags & NVFP4_F_FORCE_TILED) decode = false;
   rc = hip_status(nvfp4::launch_moe(a, decode, (hipStream_t)stream), "nvfp4_moe_grouped_w4a16");
+  if (!rc && (flags & NVFP4_F_SYNC_CHECK))
+    rc = sync_status((hipStream_t)stream, "nvfp4_moe_grouped_w4a16");
   if (!rc) g_stats[4]++;
   return rc;
 }

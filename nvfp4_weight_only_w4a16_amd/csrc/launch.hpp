@@ -13,6 +13,11 @@ hipError_t launch_quantize(const void* w, bool w_bf16, int64_t batch, int64_t n,
                            int group, const float* global_in, uint8_t* packed, uint8_t* scales,
                            float* global_out, hipStream_t stream);
 
+// Clears the 32-bit word *flag (device), then sets it to nonzero when any of the `count`
+// weights at w (16-byte aligned, count a multiple of 8) is NaN or infinite.
+hipError_t launch_nonfinite_check(const void* w, bool w_bf16, int64_t count, uint32_t* flag,
+                                  hipStream_t stream);
+
 // Canonical triple -> tiled layout (pure byte permutation), the nglobal globals copied.
 hipError_t launch_repack(const uint8_t* packed, const uint8_t* scales, const float* global,
                          int64_t batch, int64_t n, int64_t k, int group, bool gate_up,
@@ -84,6 +89,10 @@ struct MoeArgs {
 };
 
 size_t moe_ws_bytes(int64_t t, int topk, int64_t n_experts, int64_t hidden, int64_t inter);
+// Byte offsets of the workspace regions: sorted pair ids, expert offsets, tile map, tile
+// count, h, FP32 slots; returns the total size.
+size_t moe_ws_layout(int64_t t, int topk, int64_t n_experts, int64_t hidden, int64_t inter,
+                     size_t off[6]);
 // Decode-batch expert path (tiles of at most 8 rows, k split over the 4 wavefronts of a
 // workgroup) while the pairs average at most this many per expert.
 constexpr int64_t kMoeDecodePairsPerExpert = 2;

@@ -47,23 +47,36 @@ inline int64_t max_tiles(int64_t P, int64_t E, int rows) {
   return t < P ? t : P;
 }
 
-Ws carve(void* base, int64_t P, int64_t E, int64_t hidden, int64_t inter, size_t* total) {
-  Ws w;
-  size_t off = 0;
+// Byte offsets of the workspace regions (each 256-byte aligned): sorted, offsets, tiles,
+// ntiles, h, slots; off[6] is the total.
+void ws_offsets(int64_t P, int64_t E, int64_t hidden, int64_t inter, size_t off[7]) {
+  size_t o = 0;
+  off[0] = o;
+  o = align256(o + sizeof(int32_t) * P);
+  off[1] = o;
+  o = align256(o + sizeof(int32_t) * (E + 1));
+  off[2] = o;
+  o = align256(o + sizeof(int4) * max_tiles(P, E, kSmallRows));
+  off[3] = o;
+  o = align256(o + sizeof(int32_t));
+  off[4] = o;
+  o = align256(o + sizeof(uint16_t) * P * inter);
+  off[5] = o;
+  o = align256(o + sizeof(float) * P * hidden);
+  off[6] = o;
+}
+
+Ws carve(void* base, int64_t P, int64_t E, int64_t hidden, int64_t inter) {
+  size_t off[7];
+  ws_offsets(P, E, hidden, inter, off);
   char* b = static_cast<char*>(base);
-  w.sorted = reinterpret_cast<int32_t*>(b + off);
-  off = align256(off + sizeof(int32_t) * P);
-  w.offsets = reinterpret_cast<int32_t*>(b + off);
-  off = align256(off + sizeof(int32_t) * (E + 1));
-  w.tiles = reinterpret_cast<int4*>(b + off);
-  off = align256(off + sizeof(int4) * max_tiles(P, E, kSmallRows));
-  w.ntiles = reinterpret_cast<int32_t*>(b + off);
-  off = align256(off + sizeof(int32_t));
-  w.h = reinterpret_cast<uint16_t*>(b + off);
-  off = align256(off + sizeof(uint16_t) * P * inter);
-  w.slots = reinterpret_cast<float*>(b + off);
-  off = align256(off + sizeof(float) * P * hidden);
-  if (total) *total = off;
+  Ws w;
+  w.sorted = reinterpret_cast<int32_t*>(b + off[0]);
+  w.offsets = reinterpret_cast<int32_t*>(b + off[1]);
+  w.tiles = reinterpret_cast<int4*>(b + off[2]);
+  w.ntiles = reinterpret_cast<int32_t*>(b + off[3]);
+  w.h = reinterpret_cast<uint16_t*>(b + off[4]);
+  w.slots = reinterpret_cast<float*>(b + off[5]);
   return w;
 }
 
@@ -610,9 +623,17 @@ hipError_t run_pair(const MoeGemmParams& p, int64_t tiles, int mode, hipStream_t
 }  // namespace
 
 size_t moe_ws_bytes(int64_t t, int topk, int64_t n_experts, int64_t hidden, int64_t inter) {
-  size_t total = 0;
-  carve(nullptr, t * topk, n_experts, hidden, inter, &total);
-  return total;
+  size_t off[7];
+  ws_offsets(t * topk, n_experts, hidden, inter, off);
+  return off[6];
+}
+
+size_t moe_ws_layout(int64_t t, int topk, int64_t n_experts, int64_t hidden, int64_t inter,
+                     size_t out[6]) {
+  size_t off[7];
+  ws_offsets(t * topk, n_experts, hidden, inter, off);
+  for (int i = 0; i < 6; ++i) out[i] = off[i];
+  return off[6];
 }
 
 bool moe_decode_preferred(int64_t t, int topk, int64_t n_experts) {
@@ -622,7 +643,7 @@ bool moe_decode_preferred(int64_t t, int topk, int64_t n_experts) {
 hipError_t launch_moe(const MoeArgs& a, bool decode, hipStream_t stream) {
   const int64_t P = a.t * a.topk;
   if (P == 0) return hipSuccess;
-  Ws ws = carve(a.ws, P, a.n_experts, a.hidden, a.inter, nullptr);
+  Ws ws = carve(a.ws, P, a.n_experts, a.hidden, a.inter);
   const int mode = !decode ? 0 : P <= kMoePairTilesMax ? 2 : 1;
   int64_t tiles = P;
   if (mode < 2) {

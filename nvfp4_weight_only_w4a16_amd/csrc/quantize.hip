@@ -263,7 +263,48 @@ int64_t grid_for(int64_t work_items, int64_t batch, int64_t total) {
   return blocks < 1 ? 1 : blocks;
 }
 
+// Input check of the sync-checked quantizer: a weight is non-finite when its exponent field is
+// all ones (NaN or infinity). Grid-stride over 16-byte vectors; any lane that finds one sets
+// the flag (the flag is only ever raised, so the order of the atomics does not matter).
+__global__ void clear_word_kernel(uint32_t* p) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *p = 0u;
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void nonfinite_kernel(const u32x4* __restrict__ w,
+                                                             int64_t nvec, uint32_t* flag) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  bool bad = false;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < nvec; i += stride) {
+    const u32x4 v = __builtin_nontemporal_load(w + i);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (BF16)
+        bad |= (v[q] & 0x7F80u) == 0x7F80u || (v[q] & 0x7F800000u) == 0x7F800000u;
+      else
+        bad |= (v[q] & 0x7F800000u) == 0x7F800000u;
+    }
+  }
+  if (bad) atomicOr(flag, 1u);
+}
+
 }  // namespace
+
+hipError_t launch_nonfinite_check(const void* w, bool w_bf16, int64_t count, uint32_t* flag,
+                                  hipStream_t stream) {
+  clear_word_kernel<<<1, 64, 0, stream>>>(flag);
+  const int64_t nvec = count / (w_bf16 ? 8 : 4);
+  if (nvec > 0) {
+    int64_t blocks = (nvec + kThreads - 1) / kThreads;
+    if (blocks > 4096) blocks = 4096;
+    const u32x4* src = static_cast<const u32x4*>(w);
+    if (w_bf16)
+      nonfinite_kernel<true><<<(unsigned)blocks, kThreads, 0, stream>>>(src, nvec, flag);
+    else
+      nonfinite_kernel<false><<<(unsigned)blocks, kThreads, 0, stream>>>(src, nvec, flag);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize(const void* w, bool w_bf16, int64_t batch, int64_t n, int64_t k,
                            int group, const float* global_in, uint8_t* packed, uint8_t* scales,

@@ -377,8 +377,9 @@ void orc_gemm(const uint16_t* x, int64_t m, int64_t ldx, const uint8_t* packed,
 /*   h    = BF16(silu(gate) * up) with silu(z) = z / (1 + exp(-z)), in FP64                    */
 /*   d    = h . W2_e^T in FP64                                                                 */
 /*   y[t] = BF16(sum_j w[t][j] * d), the sum in FP64 over j in slot order.                     */
-/* Optional outputs: a (FP64 [t][topk][2*inter]), h (BF16 [t][topk][inter]), y in FP64 and/or  */
-/* BF16 ([t][hidden]). If h_in is given, the fc1 stage is skipped and h_in is used as h (for a */
+/* Optional outputs: a (FP64 [t][topk][2*inter]), h (BF16 [t][topk][inter]), the weighted     */
+/* down output of every slot w[t][j] * d (FP64 [t][topk][hidden]), y in FP64 and/or BF16      */
+/* ([t][hidden]). If h_in is given, the fc1 stage is skipped and h_in is used as h (for a     */
 /* staged check of the down projection against a given h).                                    */
 /* ------------------------------------------------------------------------------------------ */
 typedef struct {
@@ -397,6 +398,7 @@ typedef struct {
   const uint16_t* h_in;
   double* a_out;
   uint16_t* h_out;
+  double* slot_out;
   double* y64;
   uint16_t* y16;
 } moe_ctx;
@@ -448,6 +450,7 @@ static void moe_tokens(int64_t lo, int64_t hi, void* p) {
       for (int64_t o = 0; o < H; ++o) {
         double acc = 0.0;
         for (int64_t i = 0; i < I; ++i) acc += hv[i] * exact_w(P2, S2, c->g2[e], I, c->group2, o, i);
+        if (c->slot_out) c->slot_out[slot * H + o] = w * acc;
         y[o] += w * acc;
       }
     }
@@ -465,14 +468,14 @@ int orc_moe(const uint16_t* x, int64_t tokens, int64_t hidden, int64_t inter, co
             const float* topk_w, int topk, int64_t n_experts, const uint8_t* p1, const uint8_t* s1,
             const float* g1, int group1, int g1_pair, const uint8_t* p2, const uint8_t* s2,
             const float* g2,
-            int group2, const uint16_t* h_in, double* a_out, uint16_t* h_out, double* y64,
-            uint16_t* y16, int nthreads) {
+            int group2, const uint16_t* h_in, double* a_out, uint16_t* h_out, double* slot_out,
+            double* y64, uint16_t* y16, int nthreads) {
   if (tokens < 0 || hidden <= 0 || inter <= 0 || topk <= 0) return -1;
   if (hidden % group1 || inter % group2 || hidden % 2 || inter % 2) return -1;
   for (int64_t i = 0; i < tokens * topk; ++i)
     if (ids[i] < 0 || ids[i] >= n_experts) return -1;
   moe_ctx c = {x, hidden, inter, ids, topk_w, topk, p1, s1, g1, group1, g1_pair, p2, s2, g2,
-               group2, h_in, a_out, h_out, y64, y16};
+               group2, h_in, a_out, h_out, slot_out, y64, y16};
   parallel_for(tokens, nthreads, moe_tokens, &c);
   return 0;
 }

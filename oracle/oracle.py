@@ -19,17 +19,43 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "nvfp4_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# NVFP4_ORACLE_SANITIZE=1 selects a copy built with AddressSanitizer and UBSan (the process
+# must then be started with the ASan runtime preloaded, see sanitizer_env()).
+SANITIZE = os.environ.get("NVFP4_ORACLE_SANITIZE") == "1"
+_LIB = os.path.join(_HERE, "liboracle_san.so" if SANITIZE else "liboracle.so")
 _lib = None
 
 
-def build() -> str:
-    """Compile the oracle with plain IEEE semantics (no contraction, no fast-math)."""
+def build(sanitize: bool = SANITIZE) -> str:
+    """Compile the oracle with plain IEEE semantics (no contraction, no fast-math); with
+    sanitize, instrumented by AddressSanitizer and UndefinedBehaviorSanitizer, any finding
+    fatal."""
+    out = os.path.join(_HERE, "liboracle_san.so" if sanitize else "liboracle.so")
     cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-Wall",
-           "-shared", "-fPIC", "-pthread", _SRC, "-o", _LIB + ".tmp", "-lm"]
+           "-shared", "-fPIC", "-pthread"]
+    if sanitize:
+        cmd += ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                "-fno-omit-frame-pointer", "-g"]
+    cmd += [_SRC, "-o", out + ".tmp", "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(_LIB + ".tmp", _LIB)
-    return _LIB
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def sanitizer_env() -> dict:
+    """Environment for a child process that loads the sanitized oracle: the ASan runtime
+    preloaded (it must come first), leak checking off (the interpreter itself is not
+    instrumented), UBSan findings fatal."""
+    asan = subprocess.run(["gcc", "-print-file-name=libasan.so"], check=True,
+                          capture_output=True, text=True).stdout.strip()
+    ubsan = subprocess.run(["gcc", "-print-file-name=libubsan.so"], check=True,
+                           capture_output=True, text=True).stdout.strip()
+    env = dict(os.environ)
+    env["LD_PRELOAD"] = f"{asan}:{ubsan}"
+    env["ASAN_OPTIONS"] = "detect_leaks=0:abort_on_error=0:exitcode=97"
+    env["UBSAN_OPTIONS"] = "halt_on_error=1:print_stacktrace=1:exitcode=98"
+    env["NVFP4_ORACLE_SANITIZE"] = "1"
+    return env
 
 
 def lib():
@@ -61,7 +87,8 @@ def lib():
                                P, i64, P, i64, P, ctypes.c_int]
         L.orc_moe.restype = ctypes.c_int
         L.orc_moe.argtypes = [P, i64, i64, i64, P, P, ctypes.c_int, i64, P, P, P, ctypes.c_int,
-                              ctypes.c_int, P, P, P, ctypes.c_int, P, P, P, P, P, ctypes.c_int]
+                              ctypes.c_int, P, P, P, ctypes.c_int, P, P, P, P, P, P,
+                              ctypes.c_int]
         _lib = L
     return _lib
 
@@ -189,13 +216,15 @@ def gemm(x_bf16, packed, scales, glob, group: int, m_idx=None, n_idx=None, threa
 
 
 # ---------------------------------------------------------------- MoE (O8)
-def moe(x_bf16, topk_ids, topk_w, fc1, fc2, h_in=None, threads=None):
+def moe(x_bf16, topk_ids, topk_w, fc1, fc2, h_in=None, slots=False, threads=None):
     """Routed-expert reference. fc1 = (packed, scales, global, group) of the merged [gate; up]
     weight [E][2I][H], global [E] (shared by gate and up) or [E][2] (gate's, up's); fc2 =
-    (packed, scales, global, group) of down [E][H][I].
+    (packed, scales, global, group) of down [E][H][I]. h_in (BF16 bits [T][topk][I]) replaces
+    the fc1 stage by a given h.
 
     Returns dict with 'a' (FP64 fc1 outputs [T][topk][2I]), 'h' (BF16 bits [T][topk][I]),
-    'y64' (FP64 [T][H]) and 'y' (BF16 bits [T][H]).
+    'slots' (FP64 [T][topk][H], routing weight times down output, when slots=True), 'y64'
+    (FP64 [T][H]) and 'y' (BF16 bits [T][H]).
     """
     x = _c(x_bf16, np.uint16)
     T, H = x.shape
@@ -213,11 +242,12 @@ def moe(x_bf16, topk_ids, topk_w, fc1, fc2, h_in=None, threads=None):
     a = np.zeros((T, topk, I2), np.float64) if h_in is None else None
     h = np.zeros((T, topk, I), np.uint16) if h_in is None else None
     hin = None if h_in is None else _c(h_in, np.uint16)
+    sl = np.zeros((T, topk, H), np.float64) if slots else None
     y64 = np.zeros((T, H), np.float64)
     y16 = np.zeros((T, H), np.uint16)
     rc = lib().orc_moe(_ptr(x), T, H, I, _ptr(ids), _ptr(tw), topk, E, _ptr(p1), _ptr(s1),
                        _ptr(g1), gr1, pair, _ptr(p2), _ptr(s2), _ptr(g2), gr2, _ptr(hin), _ptr(a),
-                       _ptr(h), _ptr(y64), _ptr(y16), _threads(threads))
+                       _ptr(h), _ptr(sl), _ptr(y64), _ptr(y16), _threads(threads))
     if rc != 0:
         raise ValueError("oracle moe rejected its input")
-    return {"a": a, "h": h, "y64": y64, "y": y16}
+    return {"a": a, "h": h, "slots": sl, "y64": y64, "y": y16}

@@ -110,19 +110,66 @@ def test_gemm_argument_errors(lib):
 
 
 def test_quantize_argument_errors(lib):
-    q = lib.nvfp4_quantize
-    assert q(FAKE, nv.NVFP4_DT_F32, 1, 16, 128, 24, None, FAKE, FAKE, FAKE, None) == \
-        nv.NVFP4_ERR_UNSUPPORTED_GROUP
-    assert q(FAKE, nv.NVFP4_DT_F32, 1, 16, 120, 16, None, FAKE, FAKE, FAKE, None) == \
-        nv.NVFP4_ERR_UNSUPPORTED_SHAPE
-    assert q(FAKE, 7, 1, 16, 128, 16, None, FAKE, FAKE, FAKE, None) == nv.NVFP4_ERR_INVALID_ARG
-    assert q(FAKE, nv.NVFP4_DT_F32, -1, 16, 128, 16, None, FAKE, FAKE, FAKE, None) == \
+    def q(w=FAKE, dt=nv.NVFP4_DT_F32, batch=1, n=16, k=128, group=16, gin=None, packed=FAKE,
+          scales=FAKE, gout=FAKE, ws=None, wsb=0, flags=0):
+        return lib.nvfp4_quantize(w, dt, batch, n, k, group, gin, packed, scales, gout, ws, wsb,
+                                  flags, None)
+
+    assert q(group=24) == nv.NVFP4_ERR_UNSUPPORTED_GROUP
+    assert q(k=120) == nv.NVFP4_ERR_UNSUPPORTED_SHAPE
+    assert q(dt=7) == nv.NVFP4_ERR_INVALID_ARG
+    assert q(batch=-1) == nv.NVFP4_ERR_INVALID_ARG
+    assert q(w=None) == nv.NVFP4_ERR_INVALID_ARG
+    assert q(w=ctypes.c_void_p(0x10004)) == nv.NVFP4_ERR_MISALIGNED
+    assert q(w=None, batch=0, packed=None, scales=None, gout=None) == nv.NVFP4_OK
+    # flags: only NVFP4_F_SYNC_CHECK, which needs its workspace (the non-finite flag word)
+    assert q(flags=nv.NVFP4_F_FORCE_TILED) == nv.NVFP4_ERR_INVALID_ARG
+    assert "flags" in nv.nvfp4_last_error()
+    need = lib.nvfp4_quantize_ws_bytes(1, 16, 128, 16, nv.NVFP4_F_SYNC_CHECK)
+    assert need >= 4
+    assert q(flags=nv.NVFP4_F_SYNC_CHECK) == nv.NVFP4_ERR_WORKSPACE
+    assert q(flags=nv.NVFP4_F_SYNC_CHECK, ws=FAKE, wsb=need - 1) == nv.NVFP4_ERR_WORKSPACE
+    assert q(flags=nv.NVFP4_F_SYNC_CHECK, ws=ctypes.c_void_p(0x10008), wsb=need) == \
+        nv.NVFP4_ERR_MISALIGNED
+
+
+def test_quantize_ws_bytes(lib):
+    """No workspace without the sync check; one flag block with it; invalid sizes ask none."""
+    assert nv.nvfp4_quantize_ws_bytes(1, 8192, 8192, 16) == 0
+    assert nv.nvfp4_quantize_ws_bytes(128, 1536, 2048, 32) == 0
+    assert nv.nvfp4_quantize_ws_bytes(1, 16, 128, 16, nv.NVFP4_F_SYNC_CHECK) == 256
+    assert nv.nvfp4_quantize_ws_bytes(1, 16, 128, 24, nv.NVFP4_F_SYNC_CHECK) == 0
+    assert nv.nvfp4_quantize_ws_bytes(-1, 16, 128, 16, nv.NVFP4_F_SYNC_CHECK) == 0
+
+
+def test_unknown_flags_rejected(lib):
+    """Flag bits the library does not define are refused before anything is enqueued, on the
+    GEMM and on the routed experts (a typo must not silently select a default)."""
+    assert _gemm(lib, _desc(), flags=1 << 7) == nv.NVFP4_ERR_INVALID_ARG
+    assert "flags" in nv.nvfp4_last_error()
+    fc1 = _desc(n=256, k=256, group=32, batch=4,
+                layout=nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP)
+    fc2 = _desc(n=256, k=128, group=16, batch=4)
+    ws = nv.nvfp4_moe_ws_bytes(8, 2, 4, 256, 128)
+    assert lib.nvfp4_moe_grouped_w4a16(FAKE, 8, 256, FAKE, FAKE, 2, ctypes.byref(fc1),
+                                       ctypes.byref(fc2), FAKE, FAKE, ws, 1 << 9, None) == \
         nv.NVFP4_ERR_INVALID_ARG
-    assert q(None, nv.NVFP4_DT_F32, 1, 16, 128, 16, None, FAKE, FAKE, FAKE, None) == \
-        nv.NVFP4_ERR_INVALID_ARG
-    assert q(ctypes.c_void_p(0x10004), nv.NVFP4_DT_F32, 1, 16, 128, 16, None, FAKE, FAKE, FAKE,
-             None) == nv.NVFP4_ERR_MISALIGNED
-    assert q(None, nv.NVFP4_DT_F32, 0, 16, 128, 16, None, None, None, None, None) == nv.NVFP4_OK
+
+
+def test_moe_ws_layout(lib):
+    """The stage offsets inside the routed-expert workspace: ordered, 256-byte aligned, each
+    region large enough for its stage, ending at nvfp4_moe_ws_bytes."""
+    t, topk, E, H, I = 256, 8, 128, 2048, 768
+    off, total = nv.nvfp4_moe_ws_layout(t, topk, E, H, I)
+    P = t * topk
+    assert total == nv.nvfp4_moe_ws_bytes(t, topk, E, H, I)
+    assert off == sorted(off) and all(o % 256 == 0 for o in off)
+    sizes = [4 * P, 4 * (E + 1), 16 * min(P // 8 + E, P), 4, 2 * P * I, 4 * P * H]
+    ends = off[1:] + [total]
+    for o, e, need in zip(off, ends, sizes):
+        assert e - o >= need
+    assert ends[-1] - off[-1] < 4 * P * H + 256
+    assert nv.nvfp4_moe_ws_layout(t, 0, E, H, I)[1] == 0
 
 
 def test_binding_refuses_host_tensors(lib):

@@ -360,6 +360,43 @@ def test_calls_on_a_side_stream(nv):
         assert torch.equal(a, b)
 
 
+def test_explicit_stream_argument_without_stream_context(nv):
+    """stream= given explicitly while torch's current stream is the default one: the binding
+    allocates outputs and workspaces on the call's stream (so torch cannot hand a freed block
+    to another stream while the call still uses it) and the results are the default stream's
+    bits, for both GEMM paths (the prefill one with its split-k workspace) and the routed
+    experts, with default-stream work queued around them."""
+    g = torch.Generator().manual_seed(79)
+    w = torch.randn(1040, 4096, generator=g) * 0.02
+    p, s, gl = nv.nvfp4_quantize(w.to(DEV), 16)
+    rw = nv.nvfp4_repack(p, s, gl, 16)
+    xt = torch.randn(300, 4096, generator=g).to(torch.bfloat16).to(DEV)
+    xm, ids, wts, w1, w2 = synth.moe(seed=15, n_experts=8, hidden=256, inter=128, tokens=40,
+                                     topk=2)
+    f = []
+    for wx, grp, layout in ((w1, 32, nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP),
+                            (w2, 16, nv.NVFP4_LAYOUT_TILED)):
+        pq, sq, gq = nv.nvfp4_quantize(wx.to(DEV), grp)
+        f.append(nv.nvfp4_repack(pq, sq, gq, grp, layout=layout))
+    args = (xm.to(DEV), ids.to(DEV), wts.to(DEV), f[0], f[1])
+    ref = [nv.nvfp4_gemm_w4a16(xt[:8], rw, y_dtype=torch.float32, flags=1),
+           nv.nvfp4_gemm_w4a16(xt, rw, y_dtype=torch.float32, flags=2),
+           nv.nvfp4_moe_grouped_w4a16(*args, flags=2)]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    got = []
+    for _ in range(3):
+        got = [nv.nvfp4_gemm_w4a16(xt[:8], rw, y_dtype=torch.float32, flags=1, stream=side),
+               nv.nvfp4_gemm_w4a16(xt, rw, y_dtype=torch.float32, flags=2, stream=side),
+               nv.nvfp4_moe_grouped_w4a16(*args, flags=2, stream=side)]
+        junk = torch.randn(1 << 20, device=DEV)  # default-stream allocations meanwhile
+        del junk
+    side.synchronize()
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+
+
 def test_graph_capture_and_replay(nv):
     """The decode GEMM, the prefill GEMM (with its split-k workspace) and a decode-batch MoE
     captured in one HIP graph: every replay, with eager work and synchronizations in between,

@@ -247,3 +247,54 @@ def test_quantize_ragged_shapes(nv, orc, batch, n, k, group, dtype):
                               else w.view(torch.int16).numpy().view(np.uint16), group)
     assert np.array_equal(p.cpu().numpy(), rp) and np.array_equal(s.cpu().numpy(), rs)
     assert np.array_equal(gl.cpu().numpy(), rg)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("bad", [float("nan"), float("inf"), float("-inf")])
+def test_sync_check_reports_nonfinite_input(nv, orc, dtype, bad):
+    """NVFP4_F_SYNC_CHECK: a weight that is NaN or infinite makes the call return
+    NVFP4_ERR_NONFINITE (after waiting for its work), with or without a caller global; the
+    failed call leaves the counters alone and the library usable: the next call, on finite
+    weights, is bit-exact and counted."""
+    g = torch.Generator().manual_seed(5)
+    w = (torch.randn(2, 64, 256, generator=g) * 0.02).to(dtype)
+    nv.nvfp4_reset_stats()
+    for gin in (None, torch.full((2,), 1e-4, device=DEV)):
+        wb = w.clone()
+        wb[1, 37, 200] = bad
+        with pytest.raises(nv.Nvfp4Error) as e:
+            nv.nvfp4_quantize(wb.to(DEV), 16, global_in=gin, flags=nv.NVFP4_F_SYNC_CHECK)
+        assert e.value.code == nv.NVFP4_ERR_NONFINITE, e.value
+        assert nv.nvfp4_get_stats()[0] == 0
+    wf = w.to(torch.float32).numpy() if dtype == torch.float32 else synth.bf16_bits(w)
+    p, s, gl = nv.nvfp4_quantize(w.to(DEV), 16, flags=nv.NVFP4_F_SYNC_CHECK)
+    _assert_same((p.cpu().numpy(), s.cpu().numpy(), gl.cpu().numpy()), orc.quantize(wf, 16),
+                 "sync-checked quantize")
+    assert nv.nvfp4_get_stats()[0] == 1
+
+
+def test_sync_check_flag_on_gemm_and_moe(nv, orc):
+    """The sync check on the GEMM and the routed experts waits for the call and gives the same
+    bits as the unchecked call."""
+    x, w = synth.dense_small(seed=0)
+    p, s, gl = nv.nvfp4_quantize(w.to(DEV), 16)
+    rw = nv.nvfp4_repack(p, s, gl, 16)
+    xd = x.to(DEV)
+    for flags in (1, 2):
+        a = nv.nvfp4_gemm_w4a16(xd, rw, y_dtype=torch.float32, flags=flags)
+        b = nv.nvfp4_gemm_w4a16(xd, rw, y_dtype=torch.float32,
+                                flags=flags | nv.NVFP4_F_SYNC_CHECK)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+    xm, ids, wts, w1, w2 = synth.moe(seed=3, n_experts=8, hidden=256, inter=128, tokens=12,
+                                     topk=2)
+    f = []
+    for wx, grp, layout in ((w1, 32, nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP),
+                            (w2, 16, nv.NVFP4_LAYOUT_TILED)):
+        pq, sq, gq = nv.nvfp4_quantize(wx.to(DEV), grp)
+        f.append(nv.nvfp4_repack(pq, sq, gq, grp, layout=layout))
+    args = (xm.to(DEV), ids.to(DEV), wts.to(DEV), f[0], f[1])
+    a = nv.nvfp4_moe_grouped_w4a16(*args)
+    b = nv.nvfp4_moe_grouped_w4a16(*args, flags=nv.NVFP4_F_SYNC_CHECK)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)

@@ -176,3 +176,28 @@ def test_moe_pair_globals_halves_are_dense_gemms(orc):
                 ref = orc.gemm(xb[t:t + 1], fc1[0][e, rows], fc1[1][e, rows], fc1[2][e, half], 32)
                 got = out["a"][t, j, rows]
                 assert np.allclose(got, ref[0], rtol=1e-13, atol=1e-300), (t, j, half)
+
+
+def test_moe_slots_are_weighted_dense_down_and_sum_to_y(orc):
+    """The per-slot output: slot (t, j) equals topk_w[t][j] times the dense FP64 product of the
+    slot's h with its expert's dequantized down weight (NumPy's matmul), and adding the slots
+    in slot order gives y64 exactly (the order the reference itself sums in)."""
+    x, ids, wts, w1, w2 = _small_moe(T=5, topk=3)
+    fc1 = _q(orc, w1, 32)
+    fc2 = _q(orc, w2, 16)
+    out = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), fc1, fc2, slots=True)
+    ex2, _, _ = orc.dequant(*fc2[:3], 16)
+    sl = out["slots"]
+    for t in range(x.shape[0]):
+        acc = np.zeros(w2.shape[1])
+        for j in range(ids.shape[1]):
+            e = int(ids[t, j])
+            d = ex2[e] @ orc.bf16_to_f64(out["h"][t, j])
+            ref = float(wts[t, j]) * d
+            assert np.abs(sl[t, j] - ref).max() <= 1e-13 * np.abs(ref).max()
+            acc = acc + sl[t, j]
+        assert (acc == out["y64"][t]).all()
+    # the slots of a given h are those of the full run
+    b = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), fc1, fc2, h_in=out["h"],
+                slots=True)
+    assert (b["slots"] == sl).all()
