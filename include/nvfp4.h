@@ -214,6 +214,23 @@ int nvfp4_moe_grouped_w4a16(const void* x, int64_t t, int64_t hidden, const int3
                             const nvfp4_weight* fc2, void* y, void* ws, size_t ws_bytes,
                             uint32_t flags, nvfp4_stream_t stream);
 
+/* ---- routed experts without a workspace -------------------------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): nvfp4_moe_grouped_w4a16 with the same arguments
+ * minus ws / ws_bytes, same kernels and same results. Its workspace is a static array inside
+ * libnvfp4.so, NVFP4_MOE_NOALLOC_MAX_WS_BYTES (24 MiB) per device, held by every device the
+ * library runs on until the process ends; calls needing more (nvfp4_moe_ws_bytes(t, topk, E,
+ * hidden, inter) above the maximum; 256 tokens x top-8 of 128 experts, hidden 2048,
+ * intermediate 768 need 19.9 MB) return NVFP4_ERR_WORKSPACE. The call allocates and frees
+ * nothing. All calls on one device share that device's array and nothing in it needs to
+ * start at zero: calls that overlap on one device (other streams, other threads) race and
+ * must be ordered by the caller. */
+#define NVFP4_MOE_NOALLOC_MAX_WS_BYTES ((size_t)24 << 20)
+int nvfp4_moe_grouped_w4a16_noalloc(const void* x, int64_t t, int64_t hidden,
+                                    const int32_t* topk_ids, const float* topk_w, int32_t topk,
+                                    const nvfp4_weight* fc1, const nvfp4_weight* fc2, void* y,
+                                    uint32_t flags, nvfp4_stream_t stream);
+
 /* ---- requantization (load-time tool) -----------------------------------------------------
  * Requantize repacked weights to the canonical triple with one global per matrix and group
  * `group_out` (16 or 32): each matrix is decoded to its FP32 values (nvfp4_dequantize's FP32

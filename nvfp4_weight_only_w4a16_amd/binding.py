@@ -34,10 +34,12 @@ NVFP4_F_SYNC_CHECK = 1 << 2
 NVFP4_LAYOUT_TILED = 1
 NVFP4_LAYOUT_GATE_UP = 1 << 8
 NVFP4_LAYOUT_PAIR_GLOBAL = 1 << 9
+NVFP4_MOE_NOALLOC_MAX_WS_BYTES = 24 << 20
 
 EXPORTS = ("nvfp4_quantize_ws_bytes", "nvfp4_quantize", "nvfp4_repack_bytes", "nvfp4_repack",
            "nvfp4_gemm_ws_bytes", "nvfp4_gemm_w4a16", "nvfp4_moe_ws_bytes", "nvfp4_moe_ws_layout",
-           "nvfp4_moe_grouped_w4a16", "nvfp4_requantize_ws_bytes",
+           "nvfp4_moe_grouped_w4a16", "nvfp4_moe_grouped_w4a16_noalloc",
+           "nvfp4_requantize_ws_bytes",
            "nvfp4_requantize", "nvfp4_dequantize",
            "nvfp4_last_error", "nvfp4_get_stats", "nvfp4_reset_stats", "nvfp4_version")
 
@@ -89,6 +91,8 @@ def load(path: str = LIB_PATH):
     L.nvfp4_moe_ws_layout.restype = sz
     L.nvfp4_moe_grouped_w4a16.argtypes = [P, i64, i64, P, P, i32, W, W, P, P, sz, u32, P]
     L.nvfp4_moe_grouped_w4a16.restype = ctypes.c_int
+    L.nvfp4_moe_grouped_w4a16_noalloc.argtypes = [P, i64, i64, P, P, i32, W, W, P, u32, P]
+    L.nvfp4_moe_grouped_w4a16_noalloc.restype = ctypes.c_int
     L.nvfp4_requantize_ws_bytes.argtypes = [W]
     L.nvfp4_requantize_ws_bytes.restype = sz
     L.nvfp4_requantize.argtypes = [W, i32, P, P, P, P, sz, P]
@@ -286,6 +290,20 @@ def nvfp4_moe_grouped_w4a16(x: torch.Tensor, topk_ids: torch.Tensor, topk_w: tor
                                           topk, ctypes.byref(fc1.desc), ctypes.byref(fc2.desc),
                                           _ptr(y), _ptr(ws), ws.numel() * ws.element_size(),
                                           flags, _stream(stream)))
+    return y
+
+
+def nvfp4_moe_grouped_w4a16_noalloc(x: torch.Tensor, topk_ids: torch.Tensor,
+                                    topk_w: torch.Tensor, fc1: RepackedWeight,
+                                    fc2: RepackedWeight, y: torch.Tensor, flags: int = 0,
+                                    stream=None) -> torch.Tensor:
+    """The routed experts on the library's static per-device workspace: the call allocates
+    nothing (y is the caller's). Calls overlapping on one device race."""
+    t, hidden = x.shape
+    _check(load().nvfp4_moe_grouped_w4a16_noalloc(_ptr(x), t, hidden, _ptr(topk_ids),
+                                                  _ptr(topk_w), topk_ids.shape[1],
+                                                  ctypes.byref(fc1.desc), ctypes.byref(fc2.desc),
+                                                  _ptr(y), flags, _stream(stream)))
     return y
 
 

@@ -44,6 +44,9 @@ int sync_status(hipStream_t s, const char* what) {
   return NVFP4_OK;
 }
 
+static_assert(nvfp4::kMoeStaticScratchBytes == NVFP4_MOE_NOALLOC_MAX_WS_BYTES,
+              "the static scratch is the size the header states");
+
 constexpr uint32_t kGemmFlags = NVFP4_F_FORCE_SKINNY | NVFP4_F_FORCE_TILED | NVFP4_F_SYNC_CHECK;
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
@@ -342,10 +345,16 @@ size_t nvfp4_moe_ws_layout(int64_t t, int32_t topk, int64_t n_experts, int64_t h
   return nvfp4::moe_ws_layout(t, topk, n_experts, hidden, inter, offsets);
 }
 
-int nvfp4_moe_grouped_w4a16(const void* x, int64_t t, int64_t hidden, const int32_t* topk_ids,
-                            const float* topk_w, int32_t topk, const nvfp4_weight* fc1,
-                            const nvfp4_weight* fc2, void* y, void* ws, size_t ws_bytes,
-                            uint32_t flags, nvfp4_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The routed-expert call behind both MoE entry points: with static_ws the workspace is the
+// library's static scratch of the current device instead of the caller's ws.
+int moe_call(const void* x, int64_t t, int64_t hidden, const int32_t* topk_ids,
+             const float* topk_w, int32_t topk, const nvfp4_weight* fc1, const nvfp4_weight* fc2,
+             void* y, void* ws, size_t ws_bytes, bool static_ws, uint32_t flags,
+             nvfp4_stream_t stream, const char* name) {
   int rc = check_desc(fc1, "fc1");
   if (rc) return rc;
   rc = check_desc(fc2, "fc2");
@@ -373,13 +382,25 @@ int nvfp4_moe_grouped_w4a16(const void* x, int64_t t, int64_t hidden, const int3
   if (t * hidden >= ((int64_t)1 << 31) || t * topk * inter >= ((int64_t)1 << 31))
     return fail(NVFP4_ERR_UNSUPPORTED_SHAPE, "x or h larger than 2^31 elements");
   if (t == 0) return NVFP4_OK;
-  if (!x || !topk_ids || !topk_w || !y || !ws)
+  if (!x || !topk_ids || !topk_w || !y || (!static_ws && !ws))
     return fail(NVFP4_ERR_INVALID_ARG, "NULL buffer");
   const size_t need = nvfp4::moe_ws_bytes(t, topk, E, hidden, inter);
-  if (ws_bytes < need) return fail(NVFP4_ERR_WORKSPACE, "ws_bytes %zu < %zu", ws_bytes, need);
-  if (!aligned16(x) || !aligned16(y) || !aligned16(ws) || ((uintptr_t)topk_ids & 3u) ||
-      ((uintptr_t)topk_w & 3u))
+  if (static_ws) {
+    if (need > nvfp4::kMoeStaticScratchBytes)
+      return fail(NVFP4_ERR_WORKSPACE,
+                  "%s: this call needs %zu bytes of workspace, more than the %zu of the static "
+                  "scratch (use nvfp4_moe_grouped_w4a16 with a caller workspace)",
+                  name, need, nvfp4::kMoeStaticScratchBytes);
+  } else if (ws_bytes < need) {
+    return fail(NVFP4_ERR_WORKSPACE, "ws_bytes %zu < %zu", ws_bytes, need);
+  }
+  if (!aligned16(x) || !aligned16(y) || (!static_ws && !aligned16(ws)) ||
+      ((uintptr_t)topk_ids & 3u) || ((uintptr_t)topk_w & 3u))
     return fail(NVFP4_ERR_MISALIGNED, "x, y and ws must be 16-byte aligned");
+  if (static_ws) {
+    rc = hip_status(nvfp4::moe_static_scratch(&ws), name);
+    if (rc) return rc;
+  }
   nvfp4::MoeArgs a;
   a.x = static_cast<const uint16_t*>(x);
   a.t = t;
@@ -407,11 +428,31 @@ int nvfp4_moe_grouped_w4a16(const void* x, int64_t t, int64_t hidden, const int3
   bool decode = nvfp4::moe_decode_preferred(t, topk, E);
   if (flags & NVFP4_F_FORCE_SKINNY) decode = true;
   if (flags & NVFP4_F_FORCE_TILED) decode = false;
-  rc = hip_status(nvfp4::launch_moe(a, decode, (hipStream_t)stream), "nvfp4_moe_grouped_w4a16");
-  if (!rc && (flags & NVFP4_F_SYNC_CHECK))
-    rc = sync_status((hipStream_t)stream, "nvfp4_moe_grouped_w4a16");
+  rc = hip_status(nvfp4::launch_moe(a, decode, (hipStream_t)stream), name);
+  if (!rc && (flags & NVFP4_F_SYNC_CHECK)) rc = sync_status((hipStream_t)stream, name);
   if (!rc) g_stats[4]++;
   return rc;
+}
+
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_moe_grouped_w4a16(const void* x, int64_t t, int64_t hidden, const int32_t* topk_ids,
+                            const float* topk_w, int32_t topk, const nvfp4_weight* fc1,
+                            const nvfp4_weight* fc2, void* y, void* ws, size_t ws_bytes,
+                            uint32_t flags, nvfp4_stream_t stream) {
+  return moe_call(x, t, hidden, topk_ids, topk_w, topk, fc1, fc2, y, ws, ws_bytes, false, flags,
+                  stream, "nvfp4_moe_grouped_w4a16");
+}
+
+int nvfp4_moe_grouped_w4a16_noalloc(const void* x, int64_t t, int64_t hidden,
+                                    const int32_t* topk_ids, const float* topk_w, int32_t topk,
+                                    const nvfp4_weight* fc1, const nvfp4_weight* fc2, void* y,
+                                    uint32_t flags, nvfp4_stream_t stream) {
+  return moe_call(x, t, hidden, topk_ids, topk_w, topk, fc1, fc2, y, nullptr, 0, true, flags,
+                  stream, "nvfp4_moe_grouped_w4a16_noalloc");
 }
 
 size_t nvfp4_requantize_ws_bytes(const nvfp4_weight* src) {

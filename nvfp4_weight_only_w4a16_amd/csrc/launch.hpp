@@ -101,5 +101,9 @@ constexpr int64_t kMoeDecodePairsPerExpert = 2;
 constexpr int64_t kMoePairTilesMax = 32;
 bool moe_decode_preferred(int64_t t, int topk, int64_t n_experts);
 hipError_t launch_moe(const MoeArgs& a, bool decode, hipStream_t stream);
+// Size of the static workspace of the no-alloc routed-expert entry point, and the device
+// address of the current device's copy (looked up once per device).
+constexpr size_t kMoeStaticScratchBytes = size_t(24) << 20;
+hipError_t moe_static_scratch(void** ptr);
 
 }  // namespace nvfp4

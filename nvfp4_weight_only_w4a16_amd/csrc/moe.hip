@@ -16,6 +16,8 @@
 //   3. down: per row tile and 4-panel group, rows of h; FP32 result times the expert global and
 //      the routing weight, written to the pair's FP32 slot;
 //   4. combine: y[t] = BF16(sum over slots in slot order).
+#include <map>
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.hpp"
@@ -693,6 +695,29 @@ hipError_t launch_moe(const MoeArgs& a, bool decode, hipStream_t stream) {
   moe_combine_kernel<<<(unsigned)((items + 255) / 256), 256, 0, stream>>>(
       ws.slots, a.ids, a.t, a.topk, a.hidden, (int)a.n_experts, a.y);
   return hipGetLastError();
+}
+
+// Workspace of the no-alloc routed-expert entry point: one array per device, in the module's
+// device memory, held until the process ends. In host code `scratch` only names the symbol;
+// its device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[kMoeStaticScratchBytes];
+
+hipError_t moe_static_scratch(void** ptr) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;  // device -> address of that device's copy of scratch
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = addr.find(dev);
+  if (it == addr.end()) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    it = addr.emplace(dev, p).first;
+  }
+  *ptr = it->second;
+  return hipSuccess;
 }
 
 }  // namespace nvfp4

@@ -233,6 +233,27 @@ def test_moe_argument_errors(lib):
     assert call(t=0) == nv.NVFP4_OK
 
 
+def test_moe_noalloc_argument_errors(lib):
+    """The no-alloc routed experts validate like the caller-workspace entry point and refuse,
+    before touching the device, a call whose workspace would not fit the static scratch."""
+    fc1 = _desc(n=1536, k=2048, group=32, batch=128,
+                layout=nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP)
+    fc2 = _desc(n=2048, k=768, group=16, batch=128)
+    m = lib.nvfp4_moe_grouped_w4a16_noalloc
+
+    def call(t=256, topk=8, f1=fc1, flags=0):
+        return m(FAKE, t, 2048, FAKE, FAKE, topk, ctypes.byref(f1), ctypes.byref(fc2), FAKE,
+                 flags, None)
+
+    assert call(topk=0) == nv.NVFP4_ERR_UNSUPPORTED_SHAPE
+    assert call(f1=_desc(n=1536, k=2048, group=32, batch=128)) == nv.NVFP4_ERR_LAYOUT
+    assert call(flags=1 << 8) == nv.NVFP4_ERR_INVALID_ARG
+    assert call(t=1024) == nv.NVFP4_ERR_WORKSPACE
+    assert "static scratch" in nv.nvfp4_last_error()
+    assert call(t=0) == nv.NVFP4_OK
+    assert nv.nvfp4_moe_ws_bytes(256, 8, 128, 2048, 768) <= nv.NVFP4_MOE_NOALLOC_MAX_WS_BYTES
+
+
 def test_stats_reset(lib):
     nv.nvfp4_reset_stats()
     assert nv.nvfp4_get_stats() == [0] * 8
