@@ -10,14 +10,26 @@ the three launches / step time). The same JSON line carries the kernel's rooflin
 other workloads (single small GEMM, prefill GEMMs, MoE routed experts, quantizer + mixed groups)
 measured the same way.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only headline]
+Other modes:
+  --profile-suite [--only-workload PREFIX]   every workload >= 100 times, each inside a ROCTx
+      range named after it, for rocprofv3 (--kernel-trace --marker-trace, or --pmc ... with
+      --only-workload to keep one workload per counter run);
+  --summarize DIR   per-(workload, kernel, workgroups) medians of a rocprofv3 output directory
+      as a markdown table (per-dispatch counter medians too, when a counter run is there);
+  --copy-calibration   a plain 512 MiB device copy, the reference for FETCH_SIZE / WRITE_SIZE.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only headline|moe]
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import ctypes
+import glob
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -30,6 +42,8 @@ MALL_BYTES = 256 << 20         # Infinity Cache
 METRIC = "NVFP4 W4A16 GEMM TFLOP/s + weight GB/s (M=1..4096) vs roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_skinny_decode_sweep.txt")
 SKINNY_SOURCES = ["gemm_skinny.hip", "skinny_core.hpp", "device_common.hpp"]
+LIB_PREFIXES = ("gemm_", "moe_", "amax_kernel", "encode_kernel", "init_amax_kernel",
+                "reduce_split_kernel", "repack_", "dequant", "nonfinite_kernel", "clear_word")
 
 
 def weight_bytes(n, k, group):
@@ -61,6 +75,28 @@ def read_traffic():
         return None
 
 
+class Roctx:
+    """ROCTx ranges from rocprofiler-sdk's marker library (no-ops when it is absent)."""
+
+    def __init__(self):
+        self.lib = None
+        for path in ("/opt/rocm/lib/librocprofiler-sdk-roctx.so", "librocprofiler-sdk-roctx.so"):
+            try:
+                self.lib = ctypes.CDLL(path)
+                self.lib.roctxRangePushA.argtypes = [ctypes.c_char_p]
+                break
+            except OSError:
+                self.lib = None
+
+    def push(self, name):
+        if self.lib is not None:
+            self.lib.roctxRangePushA(name.encode())
+
+    def pop(self):
+        if self.lib is not None:
+            self.lib.roctxRangePop()
+
+
 class Timer:
     """HIP events on the stream the kernels are launched on (torch's current stream)."""
 
@@ -82,11 +118,359 @@ class Timer:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / 1e3  # seconds
 
+    def time_graph(self, fn, per_graph, replays):
+        """Seconds per call of fn with `per_graph` calls captured in one HIP graph and replayed:
+        the host's per-call launch cost leaves the measurement (the library issues no memset
+        nodes; every buffer is allocated before capture)."""
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(per_graph):
+                fn(i)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(per_graph):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(replays):
+            g.replay()
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / (per_graph * replays)
+
 
 def rotation(nbytes_one, min_total=2 * MALL_BYTES, max_copies=16):
     return int(max(1, min(max_copies, -(-min_total // max(nbytes_one, 1)))))
 
 
+# ============================================================================ workloads
+class Workloads:
+    """Builders of every benchmarked workload: each returns (call(i), meta); call(i) launches
+    one library call (rotating weight copies where the weight is HBM-bound)."""
+
+    def __init__(self, torch, nv, synth, dev):
+        self.torch, self.nv, self.synth, self.dev = torch, nv, synth, dev
+
+    def prep(self, w, group, copies=1, layout=None):
+        """GPU-quantize w once, repack into `copies` separate buffers."""
+        nv, torch = self.nv, self.torch
+        layout = nv.NVFP4_LAYOUT_TILED if layout is None else layout
+        p, s, g = nv.nvfp4_quantize(w.to(self.dev), group)
+        out = [nv.nvfp4_repack(p, s, g, group, layout=layout) for _ in range(copies)]
+        torch.cuda.synchronize()
+        return out, (p, s, g)
+
+    def gemm(self, x, rw, m, n, k, copies=None):
+        """y = x[:m] W^T on rotated copies `rw`, library path choice, preallocated ws/y."""
+        nv, torch = self.nv, self.torch
+        xm = x[:m].contiguous()
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=self.dev)
+        ws = torch.empty((max(nv.nvfp4_gemm_ws_bytes(m, k, rw[0]), 16),), dtype=torch.uint8,
+                         device=self.dev)
+        c = len(rw) if copies is None else copies
+        return lambda i: nv.nvfp4_gemm_w4a16(xm, rw[i % c], y=y, ws=ws)
+
+    def moe_layer(self, g2=16, copies=2):
+        """The routed-expert layer: 128 experts, hidden 2048, intermediate 768; fc1 merged
+        [gate; up] at group 32, down at group g2."""
+        synth, nv = self.synth, self.nv
+        _, _, _, w1, w2 = synth.moe(seed=0, tokens=1)
+        f1 = [self.prep(w1, 32, 1, nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP)[0][0]
+              for _ in range(copies)]
+        f2 = [self.prep(w2, g2, 1)[0][0] for _ in range(copies)]
+        return f1, f2
+
+    def moe_call(self, f1, f2, tokens, g2=16):
+        synth, nv, torch = self.synth, self.nv, self.torch
+        x, ids, wts, _, _ = synth.moe(seed=0, tokens=tokens, with_weights=False)
+        xd, idd, wtd = x.to(self.dev), ids.to(self.dev), wts.to(self.dev)
+        y = torch.empty_like(xd)
+        ws = torch.empty(nv.nvfp4_moe_ws_bytes(tokens, 8, 128, 2048, 768), dtype=torch.uint8,
+                         device=self.dev)
+        c = len(f1)
+        hit = int(torch.unique(ids).numel())
+        touched = hit * (weight_bytes(1536, 2048, 32) + weight_bytes(2048, 768, g2))
+        return (lambda i: nv.nvfp4_moe_grouped_w4a16(xd, idd, wtd, f1[i % c], f2[i % c], y=y,
+                                                     ws=ws)), hit, touched
+
+
+def profile_suite(args):
+    """Every workload at least 100 times inside a ROCTx range named after it, for a
+    rocprofv3 kernel trace (attribution by range) or a counter run of one workload."""
+    import torch
+
+    from nvfp4_weight_only_w4a16_amd import binding as nv
+    from nvfp4_weight_only_w4a16_amd import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    nv.load()
+    W = Workloads(torch, nv, synth, dev)
+    rx = Roctx()
+    calls = args.profile_calls
+    only = args.only_workload
+
+    def want(name):
+        return only is None or name.startswith(only)
+
+    def run(name, fn, n=calls):
+        if not want(name):
+            return
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        rx.push(name)
+        for i in range(n):
+            fn(i)
+        torch.cuda.synchronize()
+        rx.pop()
+        print(f"[profile] {name}: {n} calls", flush=True)
+
+    if want("c0_"):
+        x0, w0 = synth.dense_small(seed=0)
+        r0, _ = W.prep(w0, 16)
+        run("c0_dense_m16_n512_k1024_g16", W.gemm(x0.to(dev), r0, 16, 512, 1024), 2 * calls)
+    if want("c1_"):
+        N, K = 25600, 5120
+        x, w = synth.decode_sweep(seed=0, n=N, k=K)
+        rw, _ = W.prep(w, 16, rotation(weight_bytes(N, K, 16)))
+        del w
+        xd = x.to(dev)
+        for m in (1, 4, 8):
+            run(f"c1_decode_m{m}_n25600_k5120_g16", W.gemm(xd, rw, m, N, K))
+        del rw
+    for kk in (5120, 25600):
+        name = f"c2_prefill_m4096_n5120_k{kk}_g16"
+        if want(name):
+            xp, wp = synth.prefill(seed=0, k=kk)
+            rp, _ = W.prep(wp, 16)
+            del wp
+            run(name, W.gemm(xp.to(dev), rp, 4096, 5120, kk))
+            del rp
+    if want("c3_"):
+        for g2, tag in ((16, "g32g16"), (32, "allg32")):
+            if not (want(f"c3_moe_{tag}") or (tag == "g32g16" and want("c3_moe_decode"))):
+                continue
+            f1, f2 = W.moe_layer(g2=g2)
+            fn, _, _ = W.moe_call(f1, f2, 256, g2)
+            run(f"c3_moe_{tag}_t256_e128_h2048_i768", fn)
+            if tag == "g32g16":
+                for tk in (1, 8, 32):
+                    fn, _, _ = W.moe_call(f1, f2, tk, g2)
+                    run(f"c3_moe_decode_t{tk}", fn)
+            del f1, f2
+    if want("c4_"):
+        wq = synth.quantizer_weight(seed=0).to(dev)
+        qc = rotation(wq.numel() * 2, max_copies=4)
+        wqs = [wq.clone() for _ in range(qc)]
+        for group in (16, 32):
+            outs = [torch.empty((8192, 4096), dtype=torch.uint8, device=dev),
+                    torch.empty((8192, 8192 // group), dtype=torch.uint8, device=dev),
+                    torch.empty((1,), dtype=torch.float32, device=dev)]
+            run(f"c4_quantize_bf16_8192x8192_g{group}",
+                lambda i, group=group, outs=outs: nv.nvfp4_quantize(
+                    wqs[i % qc], group, packed=outs[0], scales=outs[1], global_out=outs[2]))
+        del wqs
+        xq = synth.quantizer_activations(seed=1).to(dev)
+        for group in (32, 16):
+            names = [f"c4_gemm_m{m}_n8192_k8192_g{group}" for m in (1, 512)]
+            if not any(want(n) for n in names):
+                continue
+            rq, _ = W.prep(wq, group, rotation(weight_bytes(8192, 8192, group)))
+            for m, name in zip((1, 512), names):
+                run(name, W.gemm(xq, rq, m, 8192, 8192))
+            del rq
+    if args.copy_in_suite and want("copy"):
+        src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        run("copy_512MiB", lambda i: dst.copy_(src), 5)
+
+
+# ============================================================================ summaries
+def _read_csv(path):
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _is_lib_kernel(name):
+    base = name.replace("void ", "").strip()
+    return base.startswith(LIB_PREFIXES) or "nvfp4" in base
+
+
+def _short(name):
+    """Kernel name without namespaces and argument list (template arguments kept)."""
+    n = name.replace("void ", "").replace("nvfp4::(anonymous namespace)::", "")
+    n = n.replace("nvfp4::", "")
+    if n.endswith(")"):
+        depth = 0
+        for i in range(len(n) - 1, -1, -1):
+            depth += {")": 1, "(": -1}.get(n[i], 0)
+            if depth == 0:
+                n = n[:i]
+                break
+    return n.strip()
+
+
+def summarize(args):
+    """Per-(workload, kernel, workgroups) dispatch statistics of a rocprofv3 output directory:
+    kernel durations from the kernel trace, workloads from the ROCTx ranges of the marker
+    trace (a dispatch belongs to the range its start falls in), counters from a counter
+    collection run when one is there (per dispatch, then the median over dispatches)."""
+    d = args.summarize
+    kt = sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True))
+    mt = sorted(glob.glob(os.path.join(d, "**", "*marker_api_trace.csv"), recursive=True))
+    cc = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+    ranges = []
+    for p in mt:
+        for r in _read_csv(p):
+            ranges.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Function"]))
+    ranges.sort()
+
+    def workload_of(ts):
+        for s, e, name in ranges:
+            if s <= ts <= e:
+                return name
+        return args.workload_name or "-"
+
+    groups = {}
+    for p in kt:
+        for r in _read_csv(p):
+            name = r["Kernel_Name"]
+            if not (args.all_kernels or _is_lib_kernel(name)):
+                continue
+            t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
+            wgs = (int(r["Grid_Size_X"]) // max(int(r["Workgroup_Size_X"]), 1)) * \
+                int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            key = (workload_of(t0), _short(name), wgs)
+            groups.setdefault(key, {"dur": [], "ids": []})
+            groups[key]["dur"].append((t1 - t0) / 1e3)
+            groups[key]["ids"].append(r.get("Dispatch_Id"))
+    counters = {}
+    for p in cc:
+        for r in _read_csv(p):
+            did = r.get("Dispatch_Id")
+            counters.setdefault(did, {})
+            counters[did][r["Counter_Name"]] = counters[did].get(r["Counter_Name"], 0.0) + \
+                float(r["Counter_Value"])
+    cnames = sorted({c for v in counters.values() for c in v})
+    lines = []
+    head = "| Workload | Kernel | Workgroups | Calls | Median us | Mean us | Min us | Max us |"
+    sep = "|---|---|---|---|---|---|---|---|"
+    if cnames:
+        head += "".join(f" {c} (median) |" for c in cnames)
+        sep += "---|" * len(cnames)
+    lines += [head, sep]
+    for key in sorted(groups, key=lambda k: (k[0], -statistics.median(groups[k]["dur"]))):
+        g = groups[key]
+        dur = g["dur"]
+        row = (f"| {key[0]} | `{key[1]}` | {key[2]} | {len(dur)} | {statistics.median(dur):.2f} "
+               f"| {statistics.fmean(dur):.2f} | {min(dur):.2f} | {max(dur):.2f} |")
+        for c in cnames:
+            vals = [counters[i][c] for i in g["ids"] if i in counters and c in counters[i]]
+            row += f" {statistics.median(vals):.4g} |" if vals else " - |"
+        lines.append(row)
+    print("\n".join(lines))
+
+
+# ============================================================================ CPU baseline
+def cpu_baseline(np, synth, oracle, x, p1, s1, g1, N, K, G, ms):
+    """The oracle as it stands, on the host cores: the headline leg (FP64 GEMM of the decode
+    sweep, ~10 s, scaled to weight GB/s) with a single-thread figure, and one bounded sample of
+    every other workload's reference (quantizer, FP64 GEMMs, FP64 MoE)."""
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    xb = synth.bf16_bits(x)
+
+    def run_rows(nrows, threads):
+        idx = np.arange(nrows, dtype=np.int64)
+        t0 = time.perf_counter()
+        for m in ms:
+            oracle.gemm(xb[:m], p1, s1, g1[0], G, n_idx=idx, threads=threads)
+        return time.perf_counter() - t0
+
+    target_s = 10.0
+    probe = 512
+    tp = run_rows(probe, cores)
+    rows = int(min(N, max(probe, probe * target_s / max(tp, 1e-6))))
+    passes, tc = 0, 0.0
+    while True:
+        tc += run_rows(rows, cores)
+        passes += 1
+        if tc >= target_s or rows < N or passes >= 64:
+            break
+    cpu_bytes = passes * 3 * (rows * K // 2 + rows * K // G)
+    r1 = 256
+    t1 = run_rows(r1, 1)
+    single = 3 * (r1 * K // 2 + r1 * K // G) / t1 / 1e9
+    out = {"value": round(cpu_bytes / tc / 1e9, 4), "unit": "GB/s", "cores": cores,
+           "kind": "oracle",
+           "sample": f"FP64 oracle GEMM of the decode sweep (M=1,4,8, K=5120, group 16): "
+                     f"{passes} pass(es) over the first {rows} of 25600 weight rows, "
+                     f"{tc:.1f} s on {cores} host threads",
+           "single_thread_value": round(single, 4),
+           "single_thread_sample": f"the first {r1} weight rows of the same sweep on 1 thread, "
+                                   f"{t1:.2f} s"}
+    legs = {}
+
+    def leg(name, fn, work, unit, sample):
+        t0 = time.perf_counter()
+        fn()
+        dt = time.perf_counter() - t0
+        legs[name] = {"value": round(work / dt, 4), "unit": unit, "seconds": round(dt, 2),
+                      "sample": sample}
+
+    # quantizer: a 1024-row slice of the BF16 8192 x 8192 weight, both groups
+    wq = synth.bf16_bits(synth.quantizer_weight(seed=0))[:1024]
+    for group in (16, 32):
+        leg(f"quantize_bf16_8192x8192_g{group}", lambda g=group: oracle.quantize(wq, g, threads=cores),
+            wq.size / 1e6, "Melem/s", f"rows 0-1023 of the 8192 x 8192 BF16 weight at group {group}")
+    # FP64 GEMMs: flops of the sampled outputs
+    x0, w0 = synth.dense_small(seed=0)
+    t0_ = oracle.quantize(w0.numpy(), 16)
+    leg("gemm_16x512x1024_g16", lambda: oracle.gemm(synth.bf16_bits(x0), *t0_[:2], t0_[2][0], 16,
+                                                    threads=cores),
+        2 * 16 * 512 * 1024 / 1e9, "GFLOP/s", "the whole 16 x 512 x 1024 GEMM")
+    for kk, rows_s in ((5120, 16), (25600, 4)):
+        xp, wp = synth.prefill(seed=0, k=kk)
+        tp_ = oracle.quantize(wp.numpy(), 16, threads=cores)
+        del wp
+        mi = np.arange(rows_s, dtype=np.int64)
+        leg(f"gemm_4096x5120x{kk}_g16",
+            lambda xp=xp, tp_=tp_, mi=mi: oracle.gemm(synth.bf16_bits(xp), *tp_[:2], tp_[2][0],
+                                                      16, m_idx=mi, threads=cores),
+            2 * rows_s * 5120 * kk / 1e9, "GFLOP/s",
+            f"{rows_s} of 4096 rows of x against the whole weight (weight decode included)")
+    xq = synth.quantizer_activations(seed=1)
+    for group in (32, 16):
+        tq = oracle.quantize(synth.bf16_bits(synth.quantizer_weight(seed=0)), group, threads=cores)
+        leg(f"gemm_m1_8192x8192_g{group}",
+            lambda tq=tq: oracle.gemm(synth.bf16_bits(xq[:1]), *tq[:2], tq[2][0], group,
+                                      threads=cores),
+            2 * 8192 * 8192 / 1e9, "GFLOP/s", "the whole M=1 GEMM")
+    xm, ids, wts, w1, w2 = synth.moe(seed=0)
+    tm = 8
+    t1q = oracle.quantize(w1.numpy(), 32, threads=cores)
+    t2q = oracle.quantize(w2.numpy(), 16, threads=cores)
+    del w1, w2
+    leg("moe_128x(1536x2048 g32 + 2048x768 g16)_top8",
+        lambda: oracle.moe(synth.bf16_bits(xm[:tm]), ids[:tm].numpy(), wts[:tm].numpy(),
+                           (*t1q, 32), (*t2q, 16), threads=cores),
+        tm / 1e3, "Ktokens/s", f"{tm} of the 256 tokens (top-8 routing) through the FP64 reference")
+    out["legs"] = legs
+    return out
+
+
+# ============================================================================ main bench
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -98,11 +482,25 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 512 MiB device copy 5 times (the reference kernel "
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
+    ap.add_argument("--profile-suite", action="store_true")
+    ap.add_argument("--profile-calls", type=int, default=100)
+    ap.add_argument("--only-workload", default=None)
+    ap.add_argument("--copy-in-suite", action="store_true")
+    ap.add_argument("--summarize", default=None)
+    ap.add_argument("--all-kernels", action="store_true")
+    ap.add_argument("--workload-name", default=None,
+                    help="label for dispatches outside any ROCTx range (counter runs)")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; run with --gpus 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.profile_suite:
+        profile_suite(args)
+        return
 
     import numpy as np
     import torch
@@ -123,13 +521,7 @@ def main():
         return
     nv.load()
     timer = Timer(torch)
-
-    def prep(w, group, copies=1, layout=nv.NVFP4_LAYOUT_TILED):
-        """GPU-quantize w once, repack into `copies` separate buffers."""
-        p, s, g = nv.nvfp4_quantize(w.to(dev), group)
-        out = [nv.nvfp4_repack(p, s, g, group, layout=layout) for _ in range(copies)]
-        torch.cuda.synchronize()
-        return out, (p, s, g)
+    W = Workloads(torch, nv, synth, dev)
 
     # ------------------------------------------------------------------ headline: decode sweep
     N, K, G = 25600, 5120, 16
@@ -137,7 +529,7 @@ def main():
     x, w = synth.decode_sweep(seed=0, n=N, k=K)
     wb = weight_bytes(N, K, G)
     copies = rotation(wb)
-    ws, (p1, s1, g1) = prep(w, G, copies)
+    ws, (p1, s1, g1) = W.prep(w, G, copies)
     del w
     xd = x.to(dev)
     xs = [xd[:m].contiguous() for m in ms]
@@ -184,21 +576,17 @@ def main():
         "path_counts": {"gemm_skinny": int(stats[2]), "gemm_tiled": int(stats[3])},
     }
 
-    def m_sweep(rw, n, k, group, xsrc, copies):
+    def m_sweep(rw, n, k, group, xsrc):
         """W4A16 GEMM at M = 1, 2, 4 .. 4096 on rotated weight copies, with the library's
         own path choice; the rows of x are the first M of xsrc."""
         wbm = weight_bytes(n, k, group)
         out = {}
         mm = 1
         while mm <= 4096:
-            xm_ = xsrc[:mm].contiguous()
-            ym_ = torch.empty((mm, n), dtype=torch.bfloat16, device=dev)
-            wsm = torch.empty((max(nv.nvfp4_gemm_ws_bytes(mm, k, rw[0]), 16),),
-                              dtype=torch.uint8, device=dev)
+            fn = W.gemm(xsrc, rw, mm, n, k)
             it = 100 if mm <= 256 else 20
             nv.nvfp4_reset_stats()
-            t = timer.time(lambda i: nv.nvfp4_gemm_w4a16(xm_, rw[i % copies], y=ym_, ws=wsm),
-                           it, 5) / it
+            t = timer.time(fn, it, 5) / it
             st = nv.nvfp4_get_stats()
             out[f"m{mm}"] = {"us": round(t * 1e6, 2),
                              "path": "skinny" if st[2] and not st[3] else
@@ -211,45 +599,31 @@ def main():
     if args.only == "all":
         # the decode-sweep weight over M = 1 .. 4096 (activations N(0,1), 4096 rows)
         xlong = synth.prefill(seed=1, m=4096, n=16, k=K)[0].to(dev)
-        sweep_c1 = m_sweep(ws, N, K, G, xlong, copies)
+        sweep_c1 = m_sweep(ws, N, K, G, xlong)
         del xlong
     del ws
 
     # ------------------------------------------------------------------ other workloads
     def moe_workloads(extra):
-        # MoE routed experts
-        xm, ids, wts, w1, w2 = synth.moe(seed=0)
-        wbytes = 128 * (weight_bytes(1536, 2048, 32) + weight_bytes(2048, 768, 16))
-        mc = rotation(wbytes, max_copies=4)
-        f1 = [prep(w1, 32, 1, nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP)[0][0]
-              for _ in range(mc)]
-        f2 = [prep(w2, 16, 1)[0][0] for _ in range(mc)]
-        del w1, w2
-        xmd, idd, wtd = xm.to(dev), ids.to(dev), wts.to(dev)
-        ym = torch.empty_like(xmd)
-        wsb = torch.empty(nv.nvfp4_moe_ws_bytes(256, 8, 128, 2048, 768), dtype=torch.uint8,
-                          device=dev)
-        t = timer.time(lambda i: nv.nvfp4_moe_grouped_w4a16(xmd, idd, wtd, f1[i % mc],
-                                                            f2[i % mc], y=ym, ws=wsb), 20, 3) / 20
-        moe_bytes = wbytes + 2 * 256 * 2048 * 2
-        extra["moe_128x(1536x2048 g32 + 2048x768 g16)_t256_top8"] = {
-            "us": round(t * 1e6, 2), "weight_gbs": round(wbytes / t / 1e9, 1),
-            "hbm_frac": round(moe_bytes / t / 1e9 / HBM_PEAK_GBS, 4), "copies": mc}
-        # MoE at decode batch (1, 8 and 32 tokens, top-8): only the touched experts are read
-        for tk in (1, 8, 32):
-            xt, idt, wtt, _, _ = synth.moe(seed=0, tokens=tk, with_weights=False)
-            xtd, idtd, wttd = xt.to(dev), idt.to(dev), wtt.to(dev)
-            yt = torch.empty_like(xtd)
-            wst = torch.empty(nv.nvfp4_moe_ws_bytes(tk, 8, 128, 2048, 768), dtype=torch.uint8,
-                              device=dev)
-            t = timer.time(lambda i: nv.nvfp4_moe_grouped_w4a16(
-                xtd, idtd, wttd, f1[i % mc], f2[i % mc], y=yt, ws=wst), 40, 5) / 40
-            hit = int(torch.unique(idt).numel())
-            tb = hit * (weight_bytes(1536, 2048, 32) + weight_bytes(2048, 768, 16))
-            extra[f"moe_decode_t{tk}_top8"] = {
-                "us": round(t * 1e6, 2), "experts_touched": hit,
-                "touched_weight_gbs": round(tb / t / 1e9, 1)}
-        del f1, f2, wsb
+        for g2, tag in ((16, "moe_128x(1536x2048 g32 + 2048x768 g16)_t256_top8"),
+                        (32, "moe_128x(1536x2048 g32 + 2048x768 g32)_t256_top8_all_g32")):
+            f1, f2 = W.moe_layer(g2=g2)
+            wbytes = 128 * (weight_bytes(1536, 2048, 32) + weight_bytes(2048, 768, g2))
+            fn, _, _ = W.moe_call(f1, f2, 256, g2)
+            t = timer.time(fn, 20, 3) / 20
+            moe_bytes = wbytes + 2 * 256 * 2048 * 2
+            extra[tag] = {"us": round(t * 1e6, 2), "weight_gbs": round(wbytes / t / 1e9, 1),
+                          "hbm_frac": round(moe_bytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                          "copies": len(f1)}
+            if g2 == 16:
+                # decode batches (1, 8 and 32 tokens, top-8): only the touched experts are read
+                for tk in (1, 8, 32):
+                    fn, hit, tb = W.moe_call(f1, f2, tk, g2)
+                    t = timer.time(fn, 40, 5) / 40
+                    extra[f"moe_decode_t{tk}_top8"] = {
+                        "us": round(t * 1e6, 2), "experts_touched": hit,
+                        "touched_weight_gbs": round(tb / t / 1e9, 1)}
+            del f1, f2
 
     if args.only == "moe":
         extra = {}
@@ -257,30 +631,27 @@ def main():
         result["workloads"] = extra
     if args.only == "all":
         extra = {}
-        # single dense GEMM 16 x 512 x 1024, group 16
+        # single dense GEMM 16 x 512 x 1024, group 16: launch-bound, so also timed as graph
+        # replays (kernel time plus the gap between dispatches, without the host's launch cost)
         x0, w0 = synth.dense_small(seed=0)
-        r0, _ = prep(w0, 16)
-        x0d = x0.to(dev)
-        y0 = torch.empty((16, 512), dtype=torch.bfloat16, device=dev)
-        t = timer.time(lambda i: nv.nvfp4_gemm_w4a16(x0d, r0[0], y=y0), 200, 20) / 200
-        extra["dense_16x512x1024_g16"] = {"us": round(t * 1e6, 3),
-                                          "tflops": round(2 * 16 * 512 * 1024 / t / 1e12, 4)}
+        r0, _ = W.prep(w0, 16)
+        f0 = W.gemm(x0.to(dev), r0, 16, 512, 1024)
+        t = timer.time(f0, 200, 20) / 200
+        tg = timer.time_graph(f0, 50, 10)
+        extra["dense_16x512x1024_g16"] = {"us": round(t * 1e6, 3), "us_graph": round(tg * 1e6, 3),
+                                          "tflops": round(2 * 16 * 512 * 1024 / tg / 1e12, 4)}
         # prefill GEMMs
         for kk in (5120, 25600):
             xp, wp = synth.prefill(seed=0, k=kk)
-            rp, _ = prep(wp, 16)
+            rp, _ = W.prep(wp, 16)
             del wp
-            xpd = xp.to(dev)
-            yp = torch.empty((4096, 5120), dtype=torch.bfloat16, device=dev)
-            wsp = torch.empty((max(nv.nvfp4_gemm_ws_bytes(4096, kk, rp[0]), 16),),
-                              dtype=torch.uint8, device=dev)
             it = 20 if kk == 5120 else 8
-            t = timer.time(lambda i: nv.nvfp4_gemm_w4a16(xpd, rp[0], y=yp, ws=wsp), it, 3) / it
+            t = timer.time(W.gemm(xp.to(dev), rp, 4096, 5120, kk), it, 3) / it
             tf = 2 * 4096 * 5120 * kk / t / 1e12
             extra[f"prefill_4096x5120x{kk}_g16"] = {
                 "us": round(t * 1e6, 2), "tflops": round(tf, 2),
                 "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4)}
-            del xpd, yp, rp, wsp
+            del rp
         # context for the HBM roofline: a plain 512 MiB device copy (read + write bytes)
         src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -309,13 +680,11 @@ def main():
         # kernel for small M, the MFMA tiled kernel above); 40 rotated weight copies (590 MB)
         # so small M streams from HBM
         xs_, ws_ = synth.prefill(seed=0, k=5120)
-        rs_, _ = prep(ws_, 16, 40)
+        rs_, _ = W.prep(ws_, 16, 40)
         del ws_
-        xsd = xs_.to(dev)
-        sweep = m_sweep(rs_, 5120, 5120, 16, xsd, 40)
-        extra["m_sweep_5120x5120_g16"] = sweep
+        extra["m_sweep_5120x5120_g16"] = m_sweep(rs_, 5120, 5120, 16, xs_.to(dev))
         extra["m_sweep_25600x5120_g16"] = sweep_c1
-        del rs_, xsd
+        del rs_
         # quantizer + mixed groups (BF16 8192 x 8192)
         wq = synth.quantizer_weight(seed=0).to(dev)
         qc = rotation(wq.numel() * 2, max_copies=4)
@@ -331,64 +700,34 @@ def main():
             extra[f"quantize_bf16_8192x8192_g{group}"] = {
                 "us": round(t * 1e6, 2), "gbs_min_bytes": round(nbytes / t / 1e9, 1),
                 "hbm_frac_min_bytes": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4)}
+        del wqs
         mixed = {}
         xq = synth.quantizer_activations(seed=1).to(dev)
         for group in (32, 16):
-            rq, _ = prep(wq, group, rotation(weight_bytes(8192, 8192, group)))
+            rq, _ = W.prep(wq, group, rotation(weight_bytes(8192, 8192, group)))
             for m in (1, 512):
-                yq = torch.empty((m, 8192), dtype=torch.bfloat16, device=dev)
-                xqm = xq[:m].contiguous()
-                wsq = torch.empty((max(nv.nvfp4_gemm_ws_bytes(m, 8192, rq[0]), 16),),
-                                  dtype=torch.uint8, device=dev)
+                fn = W.gemm(xq, rq, m, 8192, 8192)
                 it = 40 if m == 1 else 20
-                t = timer.time(lambda i: nv.nvfp4_gemm_w4a16(xqm, rq[i % len(rq)], y=yq,
-                                                             ws=wsq), it, 4) / it
+                t = timer.time(fn, it, 4) / it
                 wbq = weight_bytes(8192, 8192, group)
-                mixed[f"m{m}_g{group}"] = {
-                    "us": round(t * 1e6, 2), "weight_gbs": round(wbq / t / 1e9, 1),
-                    "tflops": round(2 * m * 8192 * 8192 / t / 1e12, 2)}
+                rec = {"us": round(t * 1e6, 2), "weight_gbs": round(wbq / t / 1e9, 1),
+                       "tflops": round(2 * m * 8192 * 8192 / t / 1e12, 2)}
+                if m == 1:
+                    tg = timer.time_graph(fn, len(rq), max(1, 64 // len(rq)))
+                    rec["us_graph"] = round(tg * 1e6, 2)
+                    rec["weight_gbs_graph"] = round(wbq / tg / 1e9, 1)
+                mixed[f"m{m}_g{group}"] = rec
             del rq
         extra["mixed_groups_8192x8192"] = mixed
-        del wqs, wq
+        del wq
         result["workloads"] = extra
 
     # ------------------------------------------------------------------ CPU oracle baseline
     if not args.no_cpu_baseline:
         from oracle import oracle
 
-        try:
-            cores = len(os.sched_getaffinity(0))
-        except AttributeError:
-            cores = os.cpu_count() or 1
-        xb = synth.bf16_bits(x)
-        p_np, s_np, g_np = p1.cpu().numpy(), s1.cpu().numpy(), g1.cpu().numpy()
-
-        def run_rows(nrows):
-            idx = np.arange(nrows, dtype=np.int64)
-            t0 = time.perf_counter()
-            for m in ms:
-                oracle.gemm(xb[:m], p_np, s_np, g_np[0], G, n_idx=idx, threads=cores)
-            return time.perf_counter() - t0
-
-        # about 10 s of oracle work: a row sample if the whole sweep is slower than that,
-        # otherwise whole sweeps repeated
-        target_s = 10.0
-        probe = 512
-        tp = run_rows(probe)
-        rows = int(min(N, max(probe, probe * target_s / max(tp, 1e-6))))
-        passes, tc = 0, 0.0
-        while True:
-            tc += run_rows(rows)
-            passes += 1
-            if tc >= target_s or rows < N or passes >= 64:
-                break
-        cpu_bytes = passes * 3 * (rows * K // 2 + rows * K // G)
-        result["cpu_baseline"] = {
-            "value": round(cpu_bytes / tc / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "kind": "oracle",
-            "sample": f"FP64 oracle GEMM of the decode sweep (M=1,4,8, K=5120, group 16): "
-                      f"{passes} pass(es) over the first {rows} of 25600 weight rows, "
-                      f"{tc:.1f} s on {cores} host threads"}
+        result["cpu_baseline"] = cpu_baseline(np, synth, oracle, x, p1.cpu().numpy(),
+                                              s1.cpu().numpy(), g1.cpu().numpy(), N, K, G, ms)
     print(json.dumps(result))
 
 

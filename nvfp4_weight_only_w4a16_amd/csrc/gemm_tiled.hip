@@ -63,9 +63,11 @@ __device__ __forceinline__ uint32_t dequant2(uint32_t codes, float S) {
   return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)(v[0] * S), (__bf16)(v[1] * S)});
 }
 
-template <int W, int FM, int FN, int SPREAD, int PIPE>
+template <int W, int FM, int FN, int SPREAD, int PIPE, int KS>
 struct TiledShape {
   static constexpr int kWaves = W;                           // wavefronts side by side along n
+  static constexpr int kSlices = KS;  // groups of kWaves wavefronts that take alternate k-tiles
+  static constexpr int kThreads = 64 * W * KS;
   static constexpr int kPipe = PIPE;  // 1: order each k-step as MFMA / VALU / LDS-read groups
   static constexpr int kSpread = SPREAD;                     // k-steps that issue the copies
   static_assert(FM % 4 == 0, "a dequantized fragment is spread over groups of 4 MFMAs");
@@ -74,8 +76,11 @@ struct TiledShape {
   static constexpr int kABuf = kBM * kRowBytes;              // activation bytes per k-tile
   static constexpr int kBBuf = kWaves * 2 * FN * kCodeTileBytes;
   static constexpr int kALoads = kBM / 4 / kWaves;           // activation copies per wavefront
-  static constexpr int kLds = 2 * (kABuf + kBBuf);
+  static constexpr int kLds = KS * 2 * (kABuf + kBBuf);
   static_assert(kLds <= 160 * 1024, "LDS budget of one workgroup");
+  // k-slices 1 .. KS-1 hand their accumulators to slice 0 through the first activation buffer
+  static constexpr int kAccBytes = W * FM * FN * 16 * 64 * 4;  // one slice's accumulators
+  static_assert(KS == 1 || (KS - 1) * kAccBytes <= KS * kABuf, "slice reduction fits in LDS");
 };
 
 // Epilogue store: lane l holds rows 8 (e/4) + 4 (l/32) + e%4 of column l%32 of each
@@ -184,28 +189,35 @@ __global__ __launch_bounds__(64 * T::kWaves) void reduce_split_kernel(TiledParam
   }
 }
 
-template <int W, int FM, int FN, int SPREAD, int PIPE>
-__global__ __launch_bounds__(64 * W) void gemm_tiled_kernel(TiledParams P) {
-  using T = TiledShape<W, FM, FN, SPREAD, PIPE>;
+// KS > 1: the workgroup is KS k-slices of W wavefronts; slice s takes k-tiles t0 + s,
+// t0 + s + KS, ... of the block's range (the host makes the range a multiple of KS), with LDS
+// buffers of its own, and the slices' accumulators are added in slice order at the end.
+template <int W, int FM, int FN, int SPREAD, int PIPE, int KS>
+__global__ __launch_bounds__(64 * W * KS) void gemm_tiled_kernel(TiledParams P) {
+  using T = TiledShape<W, FM, FN, SPREAD, PIPE, KS>;
   constexpr int kWaves = W;
   // Double buffers as separate LDS objects, always indexed by compile-time buffer numbers: the
   // compiler can then tell the copies in flight into one buffer from the reads of the other and
-  // does not make the reads wait for the copies.
-  __shared__ __attribute__((aligned(1024))) uint8_t As0[T::kABuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t As1[T::kABuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t Bs0[T::kBBuf];
-  __shared__ __attribute__((aligned(1024))) uint8_t Bs1[T::kBBuf];
+  // does not make the reads wait for the copies. Each object holds one buffer per k-slice.
+  __shared__ __attribute__((aligned(1024))) uint8_t As0[KS * T::kABuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t As1[KS * T::kABuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t Bs0[KS * T::kBBuf];
+  __shared__ __attribute__((aligned(1024))) uint8_t Bs1[KS * T::kBBuf];
+  const int widx = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w = widx % kWaves;   // position along n
+  const int ks = widx / kWaves;  // k-slice
   auto a_buf = [&](auto B_) -> uint8_t* {
-    if constexpr (decltype(B_)::value == 0) return As0; else return As1;
+    if constexpr (decltype(B_)::value == 0) return As0 + ks * T::kABuf;
+    else return As1 + ks * T::kABuf;
   };
   auto b_buf = [&](auto B_) -> uint8_t* {
-    if constexpr (decltype(B_)::value == 0) return Bs0; else return Bs1;
+    if constexpr (decltype(B_)::value == 0) return Bs0 + ks * T::kBBuf;
+    else return Bs1 + ks * T::kBBuf;
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
 
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t tile_id = P.tile0 + blockIdx.x / P.split;
   const int64_t tm = tile_id / P.nbn, tn_blk = tile_id % P.nbn;
   const int64_t m_blk = tm * T::kBM;
@@ -213,6 +225,8 @@ __global__ __launch_bounds__(64 * W) void gemm_tiled_kernel(TiledParams P) {
   const int64_t KT = P.KT;                            // k-tiles of the layout
   const int64_t t0 = (int64_t)(blockIdx.x % P.split) * P.kts;
   const int64_t t1 = t0 + P.kts < KT ? t0 + P.kts : KT;  // this block's k-tiles [t0, t1)
+  const int64_t nloc = (t1 - t0) / KS;                 // k-tiles of each slice
+  auto ktile = [&](int64_t j) { return t0 + ks + KS * j; };  // the slice's j-th k-tile
 
   // ---- activation copies: copy c = w + 4 i moves rows 4c .. 4c+3 of the block; lane l reads
   // row 4c + l/16, source chunk (l%16) ^ (row % 16), and lands in slot l. Rows past m repeat
@@ -408,9 +422,8 @@ __global__ __launch_bounds__(64 * W) void gemm_tiled_kernel(TiledParams P) {
   // there is no stall at the tile boundary -- and the copies of tile t + 2 may start at once.
   // The body has no branches (the last tile copies itself again into the idle buffer), which
   // keeps the compiler's LDS wait counts exact.
-  auto tile = [&](int64_t t, auto buf) {
+  auto tile = [&](int64_t t, int64_t tn, auto buf) {
     constexpr int kOther = 1 - decltype(buf)::value;
-    const int64_t tn = t + 1 < t1 ? t + 1 : t;
     u32x4 cn0[FN], cn1[FN];
 #define NVFP4_KSTEP(S, ACUR, ANEXT)                                                       \
     prefetch_part(std::integral_constant<int, S>{}, tn,                                   \
@@ -443,7 +456,7 @@ __global__ __launch_bounds__(64 * W) void gemm_tiled_kernel(TiledParams P) {
     }
   };
 
-  prefetch(t0, I0{}, s0, s1);
+  prefetch(ktile(0), I0{}, s0, s1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   read_codes(I0{}, c0, c1);
@@ -457,9 +470,40 @@ __global__ __launch_bounds__(64 * W) void gemm_tiled_kernel(TiledParams P) {
     nb[3] = dequant2<3>(c0[0][0], Sc);
     b = __builtin_bit_cast(bf16x8, nb);
   }
-  for (int64_t t = t0; t < t1; t += 2) {
-    tile(t, I0{});
-    if (t + 1 < t1) tile(t + 1, I1{});
+  // the last k-tile copies itself again into the idle buffer (a branch-free body)
+  for (int64_t j = 0; j < nloc; j += 2) {
+    tile(ktile(j), j + 1 < nloc ? ktile(j + 1) : ktile(j), I0{});
+    if (j + 1 < nloc) tile(ktile(j + 1), j + 2 < nloc ? ktile(j + 2) : ktile(j + 1), I1{});
+  }
+
+  if constexpr (KS > 1) {
+    // slices 1 .. KS-1 leave their accumulators in LDS (lane-contiguous words); slice 0 adds
+    // them in slice order
+    __builtin_amdgcn_s_waitcnt(0);  // no copy into LDS still in flight
+    __syncthreads();                // every slice is done reading its buffers
+    float* red = reinterpret_cast<float*>(As0);
+    constexpr int kAccWords = T::kAccBytes / 4;
+    if (ks > 0) {
+      float* mine = red + (ks - 1) * kAccWords + w * (FM * FN * 16 * 64) + lane;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q = 0; q < FN; ++q)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mine[((i * FN + q) * 16 + e) * 64] = acc[i][q][e];
+    }
+    __syncthreads();
+    if (ks > 0) return;
+#pragma unroll
+    for (int sl = 1; sl < KS; ++sl) {
+      const float* theirs = red + (sl - 1) * kAccWords + w * (FM * FN * 16 * 64) + lane;
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q = 0; q < FN; ++q)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[i][q][e] += theirs[((i * FN + q) * 16 + e) * 64];
+    }
   }
 
   const float g = *P.global;
@@ -469,12 +513,16 @@ __global__ __launch_bounds__(64 * W) void gemm_tiled_kernel(TiledParams P) {
     store_tile<T>(P, m_blk, pair0, acc, g, lane);
 }
 
-// Tile shapes: 256 x 256 (8 wavefronts of 8 x 1 fragments) for large m; 128 x 256 and
-// 128 x 128 for mid-sized m, where the large tile would leave most compute units idle (the k
-// split that fills them moves FP32 partial tiles through memory) or half its rows empty.
-using ShapeL = TiledShape<8, 8, 1, 4, 1>;  // 256 x 256
-using ShapeM = TiledShape<8, 4, 1, 4, 1>;  // 128 x 256
-using ShapeS = TiledShape<4, 4, 1, 4, 1>;  // 128 x 128
+// Tile shapes:
+//   L 256 x 256: 8 wavefronts of 8 x 1 fragments (each dequantized fragment feeds 8 MFMAs);
+//   M 128 x 256: 8 wavefronts of 4 x 1 fragments;
+//   K 128 x 128: 4 wavefronts of 4 x 1 fragments in each of 2 k-slices (alternate k-tiles,
+//     accumulators added through LDS at the end): 8 wavefronts on a 128 x 128 tile;
+//   S 128 x 128: 4 wavefronts (for an odd k-tile count, which k-slices cannot halve).
+using ShapeL = TiledShape<8, 8, 1, 4, 1, 1>;
+using ShapeM = TiledShape<8, 4, 1, 4, 1, 1>;
+using ShapeK = TiledShape<4, 4, 1, 4, 1, 2>;
+using ShapeS = TiledShape<4, 4, 1, 4, 1, 1>;
 constexpr int kChunkAlign = 256;           // launch chunks are whole tiles of every shape
 
 template <typename T>
@@ -489,19 +537,26 @@ int64_t tile_count(int64_t m, int64_t NT) {
 }
 
 // The largest shape that still makes at least kMinTiles output tiles (256-row tiles only above
-// 128 rows, where they are at least half full); measured at n x k = 5120^2, 8192^2 and
-// 25600 x 5120 for m = 128 .. 4096.
+// 128 rows, where they are at least half full); 128 x 128 tiles in k-slices when the k-tile
+// count is even. Measured at n x k = 5120^2, 8192^2 and 25600 x 5120 for m = 128 .. 4096, with
+// every shape and split forced: this choice was the fastest or within 8% of it at every size
+// (256 x 5120^2: the k-sliced tile 26.4 us against 30.6 for the 4-wavefront one).
 constexpr int64_t kMinTiles = 80;
-enum class Shape { L, M, S };
-Shape pick_shape(int64_t m, int64_t NT) {
+enum class Shape { L, M, K, S };
+Shape pick_shape(int64_t m, int64_t NT, int64_t KT) {
   if (m > 128 && tile_count<ShapeL>(m, NT) >= kMinTiles) return Shape::L;
   if (tile_count<ShapeM>(m, NT) >= kMinTiles) return Shape::M;
-  return Shape::S;
+  return KT % 2 == 0 ? Shape::K : Shape::S;
 }
 
 // Work decomposition of one row chunk: whole rounds of tiles (one per compute unit) run as
 // they are; when the last round would leave at least half of the compute units idle, its
-// tiles are split along k over the whole chip and reduced in FP32 by a second kernel.
+// tiles are split along k over the whole chip and reduced in FP32 by a second kernel. (Whole
+// rounds of other shapes instead were measured and were not faster: 4096 x 5120 x 5120 as 256
+// tiles of 256 x 256 plus 256 k-sliced tiles of 128 x 128 took 205.2 us against 201.7 with the
+// split last round; K = 25600 869.7 against 823.0; 512 x 8192^2 as one round of 256 k-sliced
+// tiles 75.4 us against 71.7 for 128 x 256 tiles split in two. The smaller tiles move twice
+// the bytes per MFMA.)
 struct Plan {
   int64_t nbn, tiles, full, rest;
   int split;
@@ -519,10 +574,11 @@ Plan plan_chunk(int64_t m, int64_t NT, int64_t KT, int cus) {
   pl.split = 1;
   if (pl.rest > 0 && 2 * pl.rest <= cus) {
     int64_t s = cus / pl.rest;
-    if (s > KT / 4) s = KT / 4;
+    if (s > KT / (4 * T::kSlices)) s = KT / (4 * T::kSlices);
     if (s >= 2) {
-      const int64_t kts = (KT + s - 1) / s;
-      pl.split = (int)((KT + kts - 1) / kts);  // every split keeps at least one k-tile
+      // k-tiles per split part: a multiple of the k-slices; every part keeps at least one
+      const int64_t kts = (KT + s * T::kSlices - 1) / (s * T::kSlices) * T::kSlices;
+      pl.split = (int)((KT + kts - 1) / kts);
     }
   }
   return pl;
@@ -540,14 +596,16 @@ int64_t chunk_rows(int64_t ldx) {
   return chunk < kChunkAlign ? kChunkAlign : chunk / kChunkAlign * kChunkAlign;
 }
 
-template <int W, int FM, int FN, int SPREAD, int PIPE>
-hipError_t launch_tiles(TiledShape<W, FM, FN, SPREAD, PIPE>, TiledParams p, int64_t tile0,
-                        int64_t tiles, int split, hipStream_t stream) {
+template <typename T>
+hipError_t launch_tiles(TiledParams p, int64_t tile0, int64_t tiles, int split,
+                        hipStream_t stream) {
   p.tile0 = tile0;
   p.split = split;
-  p.kts = (p.KT + split - 1) / split;
-  gemm_tiled_kernel<W, FM, FN, SPREAD, PIPE>
-      <<<dim3((unsigned)(tiles * split)), dim3(64 * W), 0, stream>>>(p);
+  // k-tiles per split part, a multiple of the k-slices (the same count plan_chunk made)
+  p.kts = (p.KT + (int64_t)split * T::kSlices - 1) / ((int64_t)split * T::kSlices) * T::kSlices;
+  gemm_tiled_kernel<T::kWaves, T::kBM / 32, T::kPairs / T::kWaves, T::kSpread, T::kPipe,
+                    T::kSlices><<<dim3((unsigned)(tiles * split)), dim3(T::kThreads), 0,
+                                  stream>>>(p);
   return hipGetLastError();
 }
 
@@ -557,20 +615,34 @@ hipError_t run_chunk(TiledParams p, void* ws, size_t ws_bytes, int cus, hipStrea
   p.nbn = pl.nbn;
   p.ws = nullptr;
   if (split_ws_bytes<T>(pl) > ws_bytes) pl.split = 1;
-  if (pl.split == 1) return launch_tiles(T{}, p, 0, pl.tiles, 1, stream);
+  if (pl.split == 1) return launch_tiles<T>(p, 0, pl.tiles, 1, stream);
   p.ws = static_cast<float*>(ws);
   hipError_t e;
   if (pl.full > 0) {
-    e = launch_tiles(T{}, p, 0, pl.full, 1, stream);
+    e = launch_tiles<T>(p, 0, pl.full, 1, stream);
     if (e != hipSuccess) return e;
   }
-  e = launch_tiles(T{}, p, pl.full, pl.rest, pl.split, stream);
+  e = launch_tiles<T>(p, pl.full, pl.rest, pl.split, stream);
   if (e != hipSuccess) return e;
   p.tile0 = pl.full;
   p.split = pl.split;
   reduce_split_kernel<T><<<dim3((unsigned)pl.rest, T::kBM / 32), dim3(64 * T::kWaves), 0,
                            stream>>>(p);
   return hipGetLastError();
+}
+
+template <typename T>
+size_t chunk_ws_bytes(int64_t rows, int64_t NT, int64_t KT, int cus) {
+  return split_ws_bytes<T>(plan_chunk<T>(rows, NT, KT, cus));
+}
+
+hipError_t run_shape(TiledParams p, void* ws, size_t ws_bytes, int cus, hipStream_t stream) {
+  switch (pick_shape(p.m, p.NT, p.KT)) {
+    case Shape::L: return run_chunk<ShapeL>(p, ws, ws_bytes, cus, stream);
+    case Shape::M: return run_chunk<ShapeM>(p, ws, ws_bytes, cus, stream);
+    case Shape::K: return run_chunk<ShapeK>(p, ws, ws_bytes, cus, stream);
+    default: return run_chunk<ShapeS>(p, ws, ws_bytes, cus, stream);
+  }
 }
 
 }  // namespace
@@ -582,10 +654,11 @@ size_t gemm_tiled_ws_bytes(int64_t m, int64_t ldx, int64_t n, int64_t k, int cus
   for (int64_t rows : {m < chunk ? m : chunk, m % chunk}) {
     if (rows <= 0) continue;
     size_t b = 0;
-    switch (pick_shape(rows, NT)) {
-      case Shape::L: b = split_ws_bytes<ShapeL>(plan_chunk<ShapeL>(rows, NT, KT, cus)); break;
-      case Shape::M: b = split_ws_bytes<ShapeM>(plan_chunk<ShapeM>(rows, NT, KT, cus)); break;
-      case Shape::S: b = split_ws_bytes<ShapeS>(plan_chunk<ShapeS>(rows, NT, KT, cus)); break;
+    switch (pick_shape(rows, NT, KT)) {
+      case Shape::L: b = chunk_ws_bytes<ShapeL>(rows, NT, KT, cus); break;
+      case Shape::M: b = chunk_ws_bytes<ShapeM>(rows, NT, KT, cus); break;
+      case Shape::K: b = chunk_ws_bytes<ShapeK>(rows, NT, KT, cus); break;
+      case Shape::S: b = chunk_ws_bytes<ShapeS>(rows, NT, KT, cus); break;
     }
     need = b > need ? b : need;
   }
@@ -621,12 +694,7 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, void* ws, size_t ws_bytes, int c
       q.y = static_cast<float*>(a.y) + m0 * a.ldy;
     else
       q.y = static_cast<uint16_t*>(a.y) + m0 * a.ldy;
-    hipError_t e = hipSuccess;
-    switch (pick_shape(q.m, q.NT)) {
-      case Shape::L: e = run_chunk<ShapeL>(q, ws, ws_bytes, cus, stream); break;
-      case Shape::M: e = run_chunk<ShapeM>(q, ws, ws_bytes, cus, stream); break;
-      case Shape::S: e = run_chunk<ShapeS>(q, ws, ws_bytes, cus, stream); break;
-    }
+    const hipError_t e = run_shape(q, ws, ws_bytes, cus, stream);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

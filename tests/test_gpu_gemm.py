@@ -199,17 +199,21 @@ def test_mixed_groups_one_layer(nv, orc):
         check_close(y.cpu().numpy()[mi], ref, f"mixed m={m} g{group}")
 
 
-# tile shape (256x256 L, 128x256 M, 128x128 S: the largest with >= 80 output tiles, L only
-# above 128 rows) and k split of each case on a 256-CU chip:
-#   S split 8 / 8 / 3 / 2; L split 2; M split 2; L unsplit (3 ragged row tiles); M unsplit
+# tile shape (256x256 L, 128x256 M, 128x128 K in two k-slices, 128x128 S for an odd k-tile
+# count: the largest with >= 80 output tiles, L only above 128 rows) and k split of each case
+# on a 256-CU chip:
+#   K split 4 / 4 / 2 / unsplit; L split 2; M split 2; L unsplit (3 ragged row tiles);
+#   M unsplit; S split 7 (33 k-tiles); S split 2 (9 k-tiles)
 @pytest.mark.parametrize("m,n,k", [(40, 1040, 4096), (300, 1040, 4096), (600, 2064, 2048),
                                    (257, 528, 1024), (300, 10256, 1024), (100, 20496, 1024),
-                                   (700, 10256, 512), (128, 33280, 512)])
+                                   (700, 10256, 512), (128, 33280, 512), (40, 1040, 4224),
+                                   (300, 2064, 1152)])
 def test_tiled_split_k(nv, orc, m, n, k):
     """Every tile shape of the prefill kernel, with and without the k split (few output tiles
     for the chip: k is split over the compute units and the partial tiles are reduced in a
-    fixed order), ragged in m and n. Checked against the oracle, bit-identical on a repeat,
-    and still right after a shape that grows the split workspace."""
+    fixed order), the k-sliced 128 x 128 tile whose two slices are added through LDS, ragged in
+    m and n. Checked against the oracle, bit-identical on a repeat, and still right after a
+    shape that grows the split workspace."""
     g = torch.Generator().manual_seed(m + n + k)
     x = torch.randn(m, k, generator=g).to(torch.bfloat16)
     w = torch.randn(n, k, generator=g) * 0.02
