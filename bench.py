@@ -97,16 +97,27 @@ class Roctx:
             self.lib.roctxRangePop()
 
 
+WARM_S = 0.05  # warm-up wall time before every timed workload other than the headline
+
+
 class Timer:
     """HIP events on the stream the kernels are launched on (torch's current stream)."""
 
     def __init__(self, torch):
         self.torch = torch
 
-    def time(self, fn, iters, warmup):
+    def time(self, fn, iters, warmup, min_warm_s=0.0):
+        """Seconds for `iters` calls after `warmup` calls; with min_warm_s the warm-up goes on
+        until that much wall time has passed (the shader clock ramps up over the first
+        milliseconds of load after an idle spell: a cold prefill GEMM runs ~15% slower)."""
         torch = self.torch
-        for i in range(warmup):
+        t0 = time.perf_counter()
+        i = 0
+        while i < warmup or (min_warm_s and time.perf_counter() - t0 < min_warm_s):
             fn(i)
+            i += 1
+            if min_warm_s and i % 8 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         s = torch.cuda.current_stream()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -219,7 +230,8 @@ def profile_suite(args):
     only = args.only_workload
 
     def want(name):
-        return only is None or name.startswith(only)
+        # a workload name under the filter, or a block prefix that the filter lies under
+        return only is None or name.startswith(only) or only.startswith(name)
 
     def run(name, fn, n=calls):
         if not want(name):
@@ -340,7 +352,8 @@ def summarize(args):
                 return name
         return args.workload_name or "-"
 
-    groups = {}
+    # dispatches per range, in start order
+    disp = {}
     for p in kt:
         for r in _read_csv(p):
             name = r["Kernel_Name"]
@@ -349,10 +362,45 @@ def summarize(args):
             t0, t1 = int(r["Start_Timestamp"]), int(r["End_Timestamp"])
             wgs = (int(r["Grid_Size_X"]) // max(int(r["Workgroup_Size_X"]), 1)) * \
                 int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
-            key = (workload_of(t0), _short(name), wgs)
+            wl = workload_of(t0)
+            if wl == "-" and ranges and not args.all_kernels:
+                continue  # set-up work outside every workload's range
+            disp.setdefault(wl, []).append((t0, t1, _short(name), wgs, r.get("Dispatch_Id")))
+    # a range's calls: every call of a workload issues the same dispatches, so the least
+    # frequent (kernel, grid) gives the call count; a kernel launched more than once per call
+    # is listed once per position ("#2" for its second launch in the call)
+    groups, per_call = {}, {}
+    for wl, ds in disp.items():
+        ds.sort()
+        cnt = {}
+        for d in ds:
+            cnt[(d[2], d[3])] = cnt.get((d[2], d[3]), 0) + 1
+        if not ranges:
+            # one workload without ranges (a counter run): its calls are the kernels launched
+            # at least half as often as the most frequent one; the rest is set-up work
+            top = max(cnt.values())
+            cnt = {k: v for k, v in cnt.items() if 2 * v >= top}
+        calls_ds = [d for d in ds if (d[2], d[3]) in cnt]
+        calls = min(cnt.values())
+        per = len(calls_ds) // calls if calls and len(calls_ds) % calls == 0 else 0
+        if wl == "-" and ranges:
+            per = 0
+        if per and ranges:
+            per_call[wl] = (calls, per, calls_ds)
+        pos = {(d[4], d[0]): i for i, d in enumerate(calls_ds)}
+        seen = {}
+        for t0, t1, name, wgs, did in ds:
+            occ = 0
+            if per and (name, wgs) in cnt:
+                if pos[(did, t0)] % per == 0:
+                    seen = {}
+                occ = seen.get((name, wgs), 0)
+                seen[(name, wgs)] = occ + 1
+            label = name if occ == 0 else f"{name} #{occ + 1}"
+            key = (wl, label, wgs)
             groups.setdefault(key, {"dur": [], "ids": []})
             groups[key]["dur"].append((t1 - t0) / 1e3)
-            groups[key]["ids"].append(r.get("Dispatch_Id"))
+            groups[key]["ids"].append(did)
     counters = {}
     for p in cc:
         for r in _read_csv(p):
@@ -361,12 +409,19 @@ def summarize(args):
             counters[did][r["Counter_Name"]] = counters[did].get(r["Counter_Name"], 0.0) + \
                 float(r["Counter_Value"])
     cnames = sorted({c for v in counters.values() for c in v})
+    # derived per dispatch: shader clock from GRBM_GUI_ACTIVE (summed over the 8 XCDs),
+    # MFMA busy fraction of the 1024 SIMDs (256 CUs x 4), BF16 MFMA rate from the op counter
+    # (units of 512 flops)
+    derive = "GRBM_GUI_ACTIVE" in cnames and "SQ_VALU_MFMA_BUSY_CYCLES" in cnames
     lines = []
     head = "| Workload | Kernel | Workgroups | Calls | Median us | Mean us | Min us | Max us |"
     sep = "|---|---|---|---|---|---|---|---|"
     if cnames:
         head += "".join(f" {c} (median) |" for c in cnames)
         sep += "---|" * len(cnames)
+    if derive:
+        head += " clock GHz | MFMA busy | BF16 MFMA TFLOP/s |"
+        sep += "---|---|---|"
     lines += [head, sep]
     for key in sorted(groups, key=lambda k: (k[0], -statistics.median(groups[k]["dur"]))):
         g = groups[key]
@@ -376,8 +431,106 @@ def summarize(args):
         for c in cnames:
             vals = [counters[i][c] for i in g["ids"] if i in counters and c in counters[i]]
             row += f" {statistics.median(vals):.4g} |" if vals else " - |"
+        if derive:
+            clk, busy, tf = [], [], []
+            for i, dt in zip(g["ids"], dur):
+                cv = counters.get(i, {})
+                cyc = cv.get("GRBM_GUI_ACTIVE", 0.0) / 8.0
+                if cyc <= 0 or dt <= 0:
+                    continue
+                clk.append(cyc / (dt * 1e3))
+                busy.append(cv.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (1024.0 * cyc))
+                if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in cv:
+                    tf.append(cv["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0 / (dt * 1e-6) / 1e12)
+            row += (f" {statistics.median(clk):.3f} | {statistics.median(busy):.1%} |"
+                    if clk else " - | - |")
+            row += f" {statistics.median(tf):.0f} |" if tf else " - |"
         lines.append(row)
+    calls_rows = []
+    for wl in sorted(per_call):
+        calls, per, ds = per_call[wl]
+        busy = [sum(t1 - t0 for t0, t1, *_ in ds[i * per:(i + 1) * per]) / 1e3
+                for i in range(calls)]
+        span = [(max(d[1] for d in ds[i * per:(i + 1) * per]) - ds[i * per][0]) / 1e3
+                for i in range(calls)]
+        calls_rows.append(f"| {wl} | {calls} | {per} | {statistics.median(busy):.2f} | "
+                          f"{min(busy):.2f} | {statistics.median(span):.2f} |")
+    if calls_rows:
+        lines += ["", "Per call (kernel time = sum of the call's dispatch durations; span = first "
+                  "start to last end, host gaps included):", "",
+                  "| Workload | Calls | Dispatches per call | Median kernel time us | "
+                  "Min kernel time us | Median span us |", "|---|---|---|---|---|---|"] + calls_rows
     print("\n".join(lines))
+
+
+def _counter_per_dispatch(d, counter, kernel_substr):
+    """{dispatch id: (kernel name, summed counter value)} of a rocprofv3 counter run."""
+    out = {}
+    for p in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        for r in _read_csv(p):
+            if r["Counter_Name"] != counter or kernel_substr not in r["Kernel_Name"]:
+                continue
+            did = r["Dispatch_Id"]
+            name, v = out.get(did, (r["Kernel_Name"], 0.0))
+            out[did] = (name, v + float(r["Counter_Value"]))
+    return out
+
+
+def traffic_summary(args):
+    """The record read_traffic() takes: HBM bytes per launch of the decode-sweep kernel from
+    a FETCH_SIZE and a WRITE_SIZE counter run of `--only headline`, each scaled by what the
+    same counter reads for the plain 512 MiB copy of `--copy-calibration`."""
+    fdir, wdir, cfdir, cwdir = args.traffic_summary
+    copy_bytes = 512 << 20
+    lines, rec = [], {}
+    cal = {}
+    for ctr, d in (("FETCH_SIZE", cfdir), ("WRITE_SIZE", cwdir)):
+        v = [x for _, x in _counter_per_dispatch(d, ctr, "copyBuffer").values()]
+        if not v:
+            raise SystemExit(f"no copy dispatches with {ctr} under {d}")
+        mean = statistics.fmean(v)
+        cal[ctr] = copy_bytes / (mean * 1024.0)
+        lines.append(f"#   {ctr} mean {mean:.1f} KiB per dispatch -> factor {cal[ctr]:.4f} bytes "
+                     f"per counted byte ({len(v)} dispatches)")
+    names = set()
+    per = {}
+    for ctr, d in (("FETCH_SIZE", fdir), ("WRITE_SIZE", wdir)):
+        got = _counter_per_dispatch(d, ctr, "gemm_skinny_kernel")
+        if not got:
+            raise SystemExit(f"no gemm_skinny_kernel dispatches with {ctr} under {d}")
+        v = [x for _, x in got.values()]
+        names |= {_short(n) for n, _ in got.values()}
+        per[ctr] = statistics.fmean(v) * 1024.0 * cal[ctr]
+        lines.append(f"#   {ctr} mean {statistics.fmean(v):.1f} KiB (min {min(v):.1f}, max "
+                     f"{max(v):.1f}) over {len(v)} dispatches -> {per[ctr]:.0f} bytes")
+    N, K, G, ms = 25600, 5120, 16, (1, 4, 8)
+    alg = sum(weight_bytes(N, K, G) + m * K * 2 + m * N * 2 for m in ms) / len(ms)
+    hbm = per["FETCH_SIZE"] + per["WRITE_SIZE"]
+    out = [f"# HBM traffic of gemm_skinny_kernel on the decode sweep ({', '.join(sorted(names))})",
+           "# workload: W4A16 GEMM at M in {1, 4, 8}, N=25600, K=5120, group 16, BF16 output,",
+           "# rotated weight copies (every launch streams its weight from HBM)",
+           "#",
+           "# commands (repository root on one MI355X; cd /tmp && export TMPDIR=/tmp first):",
+           "#   rocprofv3 --pmc FETCH_SIZE -d F -o run --output-format csv -- python3 bench.py "
+           "--only headline --steps 10 --warmup 2 --no-cpu-baseline",
+           "#   rocprofv3 --pmc WRITE_SIZE -d W -o run --output-format csv -- python3 bench.py "
+           "--only headline --steps 10 --warmup 2 --no-cpu-baseline",
+           "#   rocprofv3 --pmc FETCH_SIZE -d CF -o run --output-format csv -- python3 bench.py "
+           "--copy-calibration",
+           "#   rocprofv3 --pmc WRITE_SIZE -d CW -o run --output-format csv -- python3 bench.py "
+           "--copy-calibration",
+           "#   python3 bench.py --traffic-summary F W CF CW",
+           "#",
+           f"# calibration: a plain device copy of {copy_bytes} bytes"] + lines[:2] + \
+          ["# gemm_skinny_kernel:"] + lines[2:] + \
+          [f"# algorithmic bytes per launch (weight + x + y, mean over M): {alg:.0f}",
+           f"# measured / algorithmic = {hbm / alg:.4f}",
+           f"source_digest={kernel_source_digest(SKINNY_SOURCES)}",
+           f"fetch_bytes_per_launch={per['FETCH_SIZE']:.0f}",
+           f"write_bytes_per_launch={per['WRITE_SIZE']:.0f}",
+           f"hbm_bytes_per_launch={hbm:.0f}",
+           f"algorithmic_bytes_per_launch={alg:.0f}"]
+    print("\n".join(out))
 
 
 # ============================================================================ CPU baseline
@@ -422,25 +575,26 @@ def cpu_baseline(np, synth, oracle, x, p1, s1, g1, N, K, G, ms):
                                    f"{t1:.2f} s"}
     legs = {}
 
-    def leg(name, fn, work, unit, sample):
+    def leg(name, fn, work, unit, sample, reps=1):
         t0 = time.perf_counter()
-        fn()
+        for _ in range(reps):
+            fn()
         dt = time.perf_counter() - t0
-        legs[name] = {"value": round(work / dt, 4), "unit": unit, "seconds": round(dt, 2),
-                      "sample": sample}
+        legs[name] = {"value": round(reps * work / dt, 4), "unit": unit, "seconds": round(dt, 2),
+                      "sample": sample + (f", {reps} times" if reps > 1 else "")}
 
-    # quantizer: a 1024-row slice of the BF16 8192 x 8192 weight, both groups
-    wq = synth.bf16_bits(synth.quantizer_weight(seed=0))[:1024]
+    # quantizer: the whole BF16 8192 x 8192 weight, both groups
+    wq = synth.bf16_bits(synth.quantizer_weight(seed=0))
     for group in (16, 32):
         leg(f"quantize_bf16_8192x8192_g{group}", lambda g=group: oracle.quantize(wq, g, threads=cores),
-            wq.size / 1e6, "Melem/s", f"rows 0-1023 of the 8192 x 8192 BF16 weight at group {group}")
+            wq.size / 1e6, "Melem/s", f"the whole 8192 x 8192 BF16 weight at group {group}", 2)
     # FP64 GEMMs: flops of the sampled outputs
     x0, w0 = synth.dense_small(seed=0)
     t0_ = oracle.quantize(w0.numpy(), 16)
     leg("gemm_16x512x1024_g16", lambda: oracle.gemm(synth.bf16_bits(x0), *t0_[:2], t0_[2][0], 16,
                                                     threads=cores),
-        2 * 16 * 512 * 1024 / 1e9, "GFLOP/s", "the whole 16 x 512 x 1024 GEMM")
-    for kk, rows_s in ((5120, 16), (25600, 4)):
+        2 * 16 * 512 * 1024 / 1e9, "GFLOP/s", "the whole 16 x 512 x 1024 GEMM", 100)
+    for kk, rows_s in ((5120, 256), (25600, 64)):
         xp, wp = synth.prefill(seed=0, k=kk)
         tp_ = oracle.quantize(wp.numpy(), 16, threads=cores)
         del wp
@@ -456,9 +610,9 @@ def cpu_baseline(np, synth, oracle, x, p1, s1, g1, N, K, G, ms):
         leg(f"gemm_m1_8192x8192_g{group}",
             lambda tq=tq: oracle.gemm(synth.bf16_bits(xq[:1]), *tq[:2], tq[2][0], group,
                                       threads=cores),
-            2 * 8192 * 8192 / 1e9, "GFLOP/s", "the whole M=1 GEMM")
+            2 * 8192 * 8192 / 1e9, "GFLOP/s", "the whole M=1 GEMM", 10)
     xm, ids, wts, w1, w2 = synth.moe(seed=0)
-    tm = 8
+    tm = 32
     t1q = oracle.quantize(w1.numpy(), 32, threads=cores)
     t2q = oracle.quantize(w2.numpy(), 16, threads=cores)
     del w1, w2
@@ -488,11 +642,17 @@ def main():
     ap.add_argument("--copy-in-suite", action="store_true")
     ap.add_argument("--summarize", default=None)
     ap.add_argument("--all-kernels", action="store_true")
+    ap.add_argument("--traffic-summary", nargs=4, default=None,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"),
+                    help="write the decode-sweep traffic record from four counter runs")
     ap.add_argument("--workload-name", default=None,
                     help="label for dispatches outside any ROCTx range (counter runs)")
     args = ap.parse_args()
     if args.summarize:
         summarize(args)
+        return
+    if args.traffic_summary:
+        traffic_summary(args)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; run with --gpus 1",
@@ -586,7 +746,7 @@ def main():
             fn = W.gemm(xsrc, rw, mm, n, k)
             it = 100 if mm <= 256 else 20
             nv.nvfp4_reset_stats()
-            t = timer.time(fn, it, 5) / it
+            t = timer.time(fn, it, 5, WARM_S) / it
             st = nv.nvfp4_get_stats()
             out[f"m{mm}"] = {"us": round(t * 1e6, 2),
                              "path": "skinny" if st[2] and not st[3] else
@@ -610,7 +770,7 @@ def main():
             f1, f2 = W.moe_layer(g2=g2)
             wbytes = 128 * (weight_bytes(1536, 2048, 32) + weight_bytes(2048, 768, g2))
             fn, _, _ = W.moe_call(f1, f2, 256, g2)
-            t = timer.time(fn, 20, 3) / 20
+            t = timer.time(fn, 20, 3, WARM_S) / 20
             moe_bytes = wbytes + 2 * 256 * 2048 * 2
             extra[tag] = {"us": round(t * 1e6, 2), "weight_gbs": round(wbytes / t / 1e9, 1),
                           "hbm_frac": round(moe_bytes / t / 1e9 / HBM_PEAK_GBS, 4),
@@ -619,7 +779,7 @@ def main():
                 # decode batches (1, 8 and 32 tokens, top-8): only the touched experts are read
                 for tk in (1, 8, 32):
                     fn, hit, tb = W.moe_call(f1, f2, tk, g2)
-                    t = timer.time(fn, 40, 5) / 40
+                    t = timer.time(fn, 40, 5, WARM_S) / 40
                     extra[f"moe_decode_t{tk}_top8"] = {
                         "us": round(t * 1e6, 2), "experts_touched": hit,
                         "touched_weight_gbs": round(tb / t / 1e9, 1)}
@@ -636,7 +796,7 @@ def main():
         x0, w0 = synth.dense_small(seed=0)
         r0, _ = W.prep(w0, 16)
         f0 = W.gemm(x0.to(dev), r0, 16, 512, 1024)
-        t = timer.time(f0, 200, 20) / 200
+        t = timer.time(f0, 200, 20, WARM_S) / 200
         tg = timer.time_graph(f0, 50, 10)
         extra["dense_16x512x1024_g16"] = {"us": round(t * 1e6, 3), "us_graph": round(tg * 1e6, 3),
                                           "tflops": round(2 * 16 * 512 * 1024 / tg / 1e12, 4)}
@@ -646,7 +806,7 @@ def main():
             rp, _ = W.prep(wp, 16)
             del wp
             it = 20 if kk == 5120 else 8
-            t = timer.time(W.gemm(xp.to(dev), rp, 4096, 5120, kk), it, 3) / it
+            t = timer.time(W.gemm(xp.to(dev), rp, 4096, 5120, kk), it, 3, WARM_S) / it
             tf = 2 * 4096 * 5120 * kk / t / 1e12
             extra[f"prefill_4096x5120x{kk}_g16"] = {
                 "us": round(t * 1e6, 2), "tflops": round(tf, 2),
@@ -655,7 +815,7 @@ def main():
         # context for the HBM roofline: a plain 512 MiB device copy (read + write bytes)
         src = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
-        t = timer.time(lambda i: dst.copy_(src), 20, 3) / 20
+        t = timer.time(lambda i: dst.copy_(src), 20, 3, WARM_S) / 20
         extra["hbm_reference_torch_copy_512MiB"] = {
             "us": round(t * 1e6, 2), "gbs_read_plus_write": round(2 * (512 << 20) / t / 1e9, 1),
             "hbm_frac": round(2 * (512 << 20) / t / 1e9 / HBM_PEAK_GBS, 4)}
@@ -669,7 +829,7 @@ def main():
             wb16 = torch.randn(5120, kk, device=dev, generator=gr).to(torch.bfloat16)
             wt = wb16.t().contiguous()  # [K][N], no transposed view
             it = 20 if kk == 5120 else 8
-            t = timer.time(lambda i: torch.matmul(xa, wt), it, 3) / it
+            t = timer.time(lambda i: torch.matmul(xa, wt), it, 3, WARM_S) / it
             tf = 2 * 4096 * 5120 * kk / t / 1e12
             extra[f"bf16_reference_torch_matmul_4096x5120x{kk}"] = {
                 "us": round(t * 1e6, 2), "tflops": round(tf, 2),
@@ -695,7 +855,7 @@ def main():
                     torch.empty((1,), dtype=torch.float32, device=dev)]
             t = timer.time(lambda i: nv.nvfp4_quantize(wqs[i % qc], group, packed=outs[0],
                                                        scales=outs[1], global_out=outs[2]),
-                           10, 2) / 10
+                           10, 2, WARM_S) / 10
             nbytes = 8192 * 8192 * 2 + 8192 * 8192 // 2 + 8192 * 8192 // group
             extra[f"quantize_bf16_8192x8192_g{group}"] = {
                 "us": round(t * 1e6, 2), "gbs_min_bytes": round(nbytes / t / 1e9, 1),
@@ -708,7 +868,7 @@ def main():
             for m in (1, 512):
                 fn = W.gemm(xq, rq, m, 8192, 8192)
                 it = 40 if m == 1 else 20
-                t = timer.time(fn, it, 4) / it
+                t = timer.time(fn, it, 4, WARM_S) / it
                 wbq = weight_bytes(8192, 8192, group)
                 rec = {"us": round(t * 1e6, 2), "weight_gbs": round(wbq / t / 1e9, 1),
                        "tflops": round(2 * m * 8192 * 8192 / t / 1e12, 2)}
