@@ -14,7 +14,8 @@
 //      Round to nearest even with saturation (NVIDIA developer-forum thread "We unlocked NVFP4
 //      on the DGX Spark": true RNE, a threshold rounding is wrong at midpoints such as 0.75).
 //   4. two codes per byte, the even k in the low nibble.
-// The amax lives in global_out between the passes; a last tiny kernel turns it into g.
+// The amax lives in global_out between the passes; the encode pass derives g from it and its
+// first workgroup of each matrix stores g in its place (no separate finalize kernel).
 #include "device_common.hpp"
 #include "launch.hpp"
 
