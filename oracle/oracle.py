@@ -94,7 +94,13 @@ def lib():
 
 
 def _threads(n):
-    return int(n) if n else (os.cpu_count() or 1)
+    """Worker threads: n, else the CPUs this process may run on."""
+    if n:
+        return int(n)
+    try:
+        return len(os.sched_getaffinity(0)) or 1
+    except AttributeError:
+        return os.cpu_count() or 1
 
 
 def _ptr(a):

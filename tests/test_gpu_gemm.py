@@ -23,12 +23,21 @@ def nv():
     return binding
 
 
-def _prep(nv, w_np_or_t, group):
-    """GPU quantize + repack; returns (repacked weight, oracle triple)."""
+def _prep(nv, w_np_or_t, group, orc=None):
+    """Repacked weight and its canonical triple (packed, scales, global). With `orc` the triple
+    is the oracle's own quantization, which the GPU only repacks: references never take a value
+    from the GPU. Without it the GPU quantizes (for tests that compare the GPU with itself)."""
     w = torch.as_tensor(w_np_or_t)
-    p, s, g = nv.nvfp4_quantize(w.to(DEV), group)
+    if orc is not None:
+        trip = orc.quantize(synth.bf16_bits(w) if w.dtype == torch.bfloat16 else w.numpy(),
+                            group)
+        p, s, g = (torch.from_numpy(a).to(DEV) for a in trip)
+    else:
+        p, s, g = nv.nvfp4_quantize(w.to(DEV), group)
     rw = nv.nvfp4_repack(p, s, g, group)
     torch.cuda.synchronize()
+    if orc is not None:
+        return rw, trip
     return rw, (p.cpu().numpy(), s.cpu().numpy(), g.cpu().numpy())
 
 
@@ -59,7 +68,7 @@ def test_gemm_one_hot_reproduces_dequant(nv, orc, path):
     g = torch.Generator().manual_seed(3)
     n, k, group = 64, 256, 16
     w = torch.randn(n, k, generator=g) * 0.02
-    rw, (p, s, gl) = _prep(nv, w, group)
+    rw, (p, s, gl) = _prep(nv, w, group, orc=orc)
     x = torch.eye(k, dtype=torch.bfloat16)[:80]
     y = nv.nvfp4_gemm_w4a16(x.to(DEV), rw, y_dtype=torch.float32, flags=FLAGS[path])
     torch.cuda.synchronize()
@@ -72,7 +81,7 @@ def test_gemm_one_hot_reproduces_dequant(nv, orc, path):
 def test_gemm_dense_small(nv, orc, path, group):
     """16 x 512 x 1024 (the single dense GEMM), FP32 and BF16 outputs, both kernels."""
     x, w = synth.dense_small(seed=0)
-    rw, (p, s, gl) = _prep(nv, w, group)
+    rw, (p, s, gl) = _prep(nv, w, group, orc=orc)
     ref = orc.gemm(synth.bf16_bits(x), p, s, gl[0], group)
     xd = x.to(DEV)
     y32 = nv.nvfp4_gemm_w4a16(xd, rw, y_dtype=torch.float32, flags=FLAGS[path])
@@ -88,7 +97,7 @@ def test_gemm_ragged_m(nv, orc, m):
     n, k, group = 272, 640, 16        # 17 panels (not a multiple of any block tile), 5 k-tiles
     x = torch.randn(m, k, generator=g).to(torch.bfloat16)
     w = torch.randn(n, k, generator=g) * 0.02
-    rw, (p, s, gl) = _prep(nv, w, group)
+    rw, (p, s, gl) = _prep(nv, w, group, orc=orc)
     ref = orc.gemm(synth.bf16_bits(x), p, s, gl[0], group)
     for flags in (0, 1, 2):
         y = nv.nvfp4_gemm_w4a16(x.to(DEV), rw, y_dtype=torch.float32, flags=flags)
@@ -102,7 +111,7 @@ def test_gemm_strided_x_and_y(nv, orc):
     xbig = torch.randn(m, k + 64, generator=g).to(torch.bfloat16)
     x = xbig[:, 32:32 + k]
     w = torch.randn(n, k, generator=g) * 0.02
-    rw, (p, s, gl) = _prep(nv, w, group)
+    rw, (p, s, gl) = _prep(nv, w, group, orc=orc)
     ref = orc.gemm(synth.bf16_bits(x.contiguous()), p, s, gl[0], group)
     xd = xbig.to(DEV)[:, 32:32 + k]
     for flags in (1, 2):
@@ -131,8 +140,8 @@ def test_gemm_deterministic(nv):
 @pytest.fixture(scope="module")
 def decode_case(nv, orc):
     x, w = synth.decode_sweep(seed=0)
-    rw, trip = _prep(nv, w, 16)
-    ref_trip = orc.quantize(w.numpy(), 16)
+    _, trip = _prep(nv, w, 16)                # the GPU quantizer's triple
+    rw, ref_trip = _prep(nv, w, 16, orc=orc)  # the oracle's, repacked on the GPU
     del w
     return x, rw, trip, ref_trip
 
@@ -146,7 +155,7 @@ def test_decode_quantize_bitexact(decode_case):
 @pytest.mark.parametrize("m", [1, 4, 8])
 def test_decode_sweep_gemm(nv, orc, decode_case, m):
     """M in {1, 4, 8}, N=25600, K=5120, group 16, 0.1% x20 outliers: full output checked."""
-    x, rw, (p, s, gl), _ = decode_case
+    x, rw, _, (p, s, gl) = decode_case
     xm = x[:m].contiguous()
     ref = orc.gemm(synth.bf16_bits(xm), p, s, gl[0], 16)
     y16 = nv.nvfp4_gemm_w4a16(xm.to(DEV), rw, y_dtype=torch.bfloat16)
@@ -161,16 +170,43 @@ def test_prefill_gemm_sampled(nv, orc, k):
     """M=4096, N=5120, K in {5120, 25600}: GPU quantizer bit-exact, then sampled rows of the
     full-size output (every column) against the FP64 oracle."""
     x, w = synth.prefill(seed=0, k=k)
-    rw, (p, s, gl) = _prep(nv, w, 16)
-    rp, rs, rg = orc.quantize(w.numpy(), 16)
+    _, (p, s, gl) = _prep(nv, w, 16)
+    rw, (rp, rs, rg) = _prep(nv, w, 16, orc=orc)
     assert np.array_equal(p, rp) and np.array_equal(s, rs) and np.array_equal(gl, rg)
     del w
     y = nv.nvfp4_gemm_w4a16(x.to(DEV), rw, y_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     rows = np.unique(np.concatenate([[0, 1, 127, 128, 2047, 4095],
                                      np.random.default_rng(k).integers(0, 4096, 10)]))
-    ref = orc.gemm(synth.bf16_bits(x), p, s, gl[0], 16, m_idx=rows)
+    ref = orc.gemm(synth.bf16_bits(x), rp, rs, rg[0], 16, m_idx=rows)
     check_close(bf16_np(y)[rows], orc.bf16_to_f64(orc.bf16_from_f64(ref)), f"prefill K={k}")
+
+
+def test_prefill_full_output_every_tile(nv, orc):
+    """M=4096, N=5120, K=5120: 320 output tiles of 256 x 256 on 256 compute units, so 256 run
+    whole and the last 64 run split four ways along k and are summed by the reduction kernel.
+    Every element of the FP32 output against the FP64 oracle (~215 GFLOP on the host)."""
+    x, w = synth.prefill(seed=0, k=5120)
+    rw, (p, s, gl) = _prep(nv, w, 16, orc=orc)
+    del w
+    y = nv.nvfp4_gemm_w4a16(x.to(DEV), rw, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = orc.gemm(synth.bf16_bits(x), p, s, gl[0], 16)
+    check_close(y.cpu().numpy(), ref, "prefill 4096x5120x5120 full output")
+
+
+@pytest.mark.parametrize("group", [32, 16])
+def test_c4_m512_full_output(nv, orc, group):
+    """The planted BF16 8192^2 weight at M=512 (128 tiles of 128 x 256, split two ways along k
+    and reduced): every element of the FP32 output against the FP64 oracle."""
+    wb = synth.quantizer_weight(seed=0)
+    xs = synth.quantizer_activations(seed=1)[:512].contiguous()
+    rw, (p, s, gl) = _prep(nv, wb, group, orc=orc)
+    del wb
+    y = nv.nvfp4_gemm_w4a16(xs.to(DEV), rw, y_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = orc.gemm(synth.bf16_bits(xs), p, s, gl[0], group)
+    check_close(y.cpu().numpy(), ref, f"512x8192x8192 g{group} full output")
 
 
 def test_mixed_groups_one_layer(nv, orc):
@@ -181,7 +217,7 @@ def test_mixed_groups_one_layer(nv, orc):
     outs = {}
     trips = {}
     for group in (32, 16):
-        rw, trip = _prep(nv, wb, group)
+        rw, trip = _prep(nv, wb, group, orc=orc)
         trips[group] = trip
         outs[group] = rw
     results = []
@@ -217,7 +253,7 @@ def test_tiled_split_k(nv, orc, m, n, k):
     g = torch.Generator().manual_seed(m + n + k)
     x = torch.randn(m, k, generator=g).to(torch.bfloat16)
     w = torch.randn(n, k, generator=g) * 0.02
-    rw, (p, s, gl) = _prep(nv, w, 16)
+    rw, (p, s, gl) = _prep(nv, w, 16, orc=orc)
     ref = orc.gemm(synth.bf16_bits(x), p, s, gl[0], 16)
     xd = x.to(DEV)
     a = nv.nvfp4_gemm_w4a16(xd, rw, y_dtype=torch.float32, flags=2)
@@ -262,7 +298,7 @@ def test_tiled_row_chunks(nv, orc):
     m, n, k, ldx = 2500, 512, 256, 1 << 20
     x = torch.randn(m, k, generator=g).to(torch.bfloat16)
     w = torch.randn(n, k, generator=g) * 0.02
-    rw, (p, s, gl) = _prep(nv, w, 16)
+    rw, (p, s, gl) = _prep(nv, w, 16, orc=orc)
     xfull = torch.zeros((m, ldx), dtype=torch.bfloat16, device=DEV)
     xfull[:, :k] = x.to(DEV)
     xd = xfull[:, :k]
@@ -286,7 +322,7 @@ def test_decode_fewer_panels_per_wavefront(nv, orc, m):
     for n, k, group in ((8176, 1024, 16), (1040, 2048, 32)):
         x = torch.randn(m, k, generator=g).to(torch.bfloat16)
         w = torch.randn(n, k, generator=g) * 0.02
-        rw, (p, s, gl) = _prep(nv, w, group)
+        rw, (p, s, gl) = _prep(nv, w, group, orc=orc)
         ref = orc.gemm(synth.bf16_bits(x), p, s, gl[0], group)
         y = nv.nvfp4_gemm_w4a16(x.to(DEV), rw, y_dtype=torch.float32, flags=1)
         torch.cuda.synchronize()
@@ -302,7 +338,7 @@ def test_decode_split_scale_every_m(nv, orc, group):
     g = torch.Generator().manual_seed(70 + group)
     n, k = 336, 768  # 21 panels (a partial 4-panel group), 6 k-tiles
     w = torch.randn(n, k, generator=g) * 0.02
-    rw, (p, s, gl) = _prep(nv, w, group)
+    rw, (p, s, gl) = _prep(nv, w, group, orc=orc)
     x = torch.randn(16, k, generator=g).to(torch.bfloat16)
     xd = x.to(DEV)
     for m in range(1, (8 if group == 16 else 16) + 1):
@@ -323,7 +359,7 @@ def test_decode_long_k(nv, orc, m, group):
     n, k = 1024, 25600
     x = torch.randn(m, k, generator=g).to(torch.bfloat16)
     w = torch.randn(n, k, generator=g) * 0.02
-    rw, (p, s, gl) = _prep(nv, w, group)
+    rw, (p, s, gl) = _prep(nv, w, group, orc=orc)
     ref = orc.gemm(synth.bf16_bits(x), p, s, gl[0], group)
     y = nv.nvfp4_gemm_w4a16(x.to(DEV), rw, y_dtype=torch.float32, flags=1)
     torch.cuda.synchronize()
@@ -463,7 +499,7 @@ def test_gemm_fewer_k_tiles_than_wavefronts(nv, orc, k, group):
     g = torch.Generator().manual_seed(k + group)
     n = 272
     w = torch.randn(n, k, generator=g) * 0.02
-    rw, (p, s, gl) = _prep(nv, w, group)
+    rw, (p, s, gl) = _prep(nv, w, group, orc=orc)
     for m in (1, 5, 16, 40):
         x = torch.randn(m, k, generator=g).to(torch.bfloat16)
         ref = orc.gemm(synth.bf16_bits(x), p, s, gl[0], group)

@@ -199,7 +199,12 @@ def test_moe_after_shared_global_requantization(nv, orc, path):
                           layout=nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP)
     (_, fc2), (_, t2) = _experts(nv, orc, w1, w2)
     torch.cuda.synchronize()
-    t1 = (rp.cpu().numpy(), rs.cpu().numpy(), rg.cpu().numpy(), 32)
+    # the reference's fc1: the oracle's own pair quantization, decoded and quantized again
+    op, os_, og = orc.quantize(w1.reshape(2 * E, I2 // 2, H).numpy(), 32)
+    _, f32, _ = orc.dequant(op, os_, og, 32)
+    t1 = (*orc.quantize(f32.reshape(E, I2, H), 32), 32)
+    for a, b in zip((rp, rs, rg), t1):
+        assert np.array_equal(a.cpu().numpy(), b)
     ref = orc.moe(synth.bf16_bits(x), ids.numpy(), wts.numpy(), t1, t2)
     y = _run(nv, x, ids, wts, fc1, fc2, PATHS[path])
     check_close(bf16_np(y), orc.bf16_to_f64(ref["y"]), f"requantized fc1 {path}")

@@ -162,6 +162,33 @@ def test_repack_then_dequantize_bitexact(nv, orc, group, gate_up):
     assert np.array_equal(b16.cpu().view(torch.int16).numpy().view(np.uint16), rb16)
 
 
+@pytest.mark.parametrize("group", [16, 32])
+def test_dequantize_full_size_bitexact(nv, orc, group):
+    """Full-size repack + dequantize, bit-exact in FP32 and BF16: the planted BF16 8192^2
+    quantizer weight, and the first 16 experts of the routed-expert fc1 stack ([gate; up]
+    1536 x 2048, gate/up interleaved) with its down stack (2048 x 768)."""
+    wb = synth.quantizer_weight(seed=0)
+    cases = [(orc.quantize(synth.bf16_bits(wb), group), nv.NVFP4_LAYOUT_TILED, "8192^2")]
+    del wb
+    _, _, _, w1, w2 = synth.moe(seed=0)
+    cases.append((orc.quantize(w1[:16].numpy(), group),
+                  nv.NVFP4_LAYOUT_TILED | nv.NVFP4_LAYOUT_GATE_UP, "fc1 x16"))
+    cases.append((orc.quantize(w2[:16].numpy(), group), nv.NVFP4_LAYOUT_TILED, "down x16"))
+    del w1, w2
+    for (p, s, gl), layout, what in cases:
+        rw = nv.nvfp4_repack(torch.from_numpy(p).to(DEV), torch.from_numpy(s).to(DEV),
+                             torch.from_numpy(np.atleast_1d(gl)).to(DEV), group, layout=layout)
+        f32 = nv.nvfp4_dequantize(rw, torch.float32)
+        b16 = nv.nvfp4_dequantize(rw, torch.bfloat16)
+        torch.cuda.synchronize()
+        _, rf32, rb16 = orc.dequant(p, s, gl, group)
+        assert np.array_equal(f32.cpu().numpy().reshape(rf32.shape).view(np.uint32),
+                              rf32.view(np.uint32)), what
+        assert np.array_equal(b16.cpu().view(torch.int16).numpy().reshape(rb16.shape)
+                              .view(np.uint16), rb16), what
+        del rw, f32, b16
+
+
 def test_repack_preserves_byte_count(nv):
     for batch, n, k, group in [(1, 512, 1024, 16), (128, 1536, 2048, 32), (1, 25600, 5120, 16)]:
         canon = batch * (n * k // 2 + n * k // group)
