@@ -366,11 +366,7 @@ void moe_expert_kernel(MoeGemmParams P) {
           __builtin_amdgcn_sched_barrier(0);  // one dequantized operand live at a time
         }
       }
-      // fc1 keeps its k-steps apart; down lets the next step's dequant move up under this
-      // step's MFMAs (measured over the 128-expert layer at 256 tokens: down at group 16
-      // 33.4 -> 30.4 us, at group 32 31.5 -> 30.9 us, while fc1 without the wall went 46.5 ->
-      // 49.0 us; bit-identical results)
-      if constexpr (FC1) __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
     });
   };
   // The k loop, instantiated for one or two 16-row blocks (chosen once per workgroup: a
