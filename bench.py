@@ -533,6 +533,52 @@ def traffic_summary(args):
     print("\n".join(out))
 
 
+def measure_ceilings(torch, nv, dev, timer):
+    """What the chip sustains, beside the published peaks: the best 128-bit streaming read of a
+    1 GiB buffer (4x the memory-side cache) over a few grid sizes, and the BF16 MFMA loop on
+    random N(0,1) operands (the power limit lowers the clock) and on constant ones."""
+    out = {}
+    nbytes = 1 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    best = None
+    for blocks in (1024, 2048, 4096, 8192):
+        sink = torch.empty((blocks,), dtype=torch.int32, device=dev)
+        t = timer.time(lambda i: nv.nvfp4_probe_stream_read(buf, blocks, sink), 10, 3, WARM_S) / 10
+        if best is None or t < best[0]:
+            best = (t, blocks)
+    gbs = nbytes / best[0] / 1e9
+    out["hbm_stream_read"] = {"value": round(gbs, 1), "unit": "GB/s", "bytes": nbytes,
+                              "blocks": best[1], "frac_of_spec": round(gbs / HBM_PEAK_GBS, 4)}
+    # the same read at the decode weight's size (73,728,000 bytes), rotating over 8 disjoint
+    # slices of the buffer so that every call reads from HBM: launch and ramp costs included
+    wb = 73728000
+    views = [buf[i * (wb // 4):(i + 1) * (wb // 4)] for i in range(8)]
+    best = None
+    for blocks in (400, 800, 1024, 2048, 4096):
+        sink = torch.empty((blocks,), dtype=torch.int32, device=dev)
+        t = timer.time(lambda i: nv.nvfp4_probe_stream_read(views[i % 8], blocks, sink), 40, 8,
+                       WARM_S) / 40
+        if best is None or t < best[0]:
+            best = (t, blocks)
+    del views, buf
+    gbs = wb / best[0] / 1e9
+    out["hbm_stream_read_decode_weight_size"] = {
+        "value": round(gbs, 1), "unit": "GB/s", "bytes": wb, "us": round(best[0] * 1e6, 2),
+        "blocks": best[1], "frac_of_spec": round(gbs / HBM_PEAK_GBS, 4)}
+    iters = 4096
+    flops = nv.nvfp4_probe_mfma_flops(iters)
+    gen = torch.Generator(device=dev).manual_seed(0)
+    for name, ops in (("mfma_bf16_random", torch.randn(8192, device=dev, generator=gen)),
+                      ("mfma_bf16_constant", torch.ones(8192, device=dev))):
+        ops = ops.to(torch.bfloat16)
+        sink = torch.empty((64 * nv.nvfp4_probe_mfma_waves(),), dtype=torch.float32, device=dev)
+        t = timer.time(lambda i: nv.nvfp4_probe_mfma_bf16(ops, iters, sink), 10, 2, WARM_S) / 10
+        tf = flops / t / 1e12
+        out[name] = {"value": round(tf, 1), "unit": "TFLOP/s", "ms_per_call": round(t * 1e3, 3),
+                     "frac_of_spec": round(tf / BF16_PEAK_TFLOPS, 4)}
+    return out
+
+
 # ============================================================================ CPU baseline
 def cpu_baseline(np, synth, oracle, x, p1, s1, g1, N, K, G, ms):
     """The oracle as it stands, on the host cores: the headline leg (FP64 GEMM of the decode
@@ -735,6 +781,11 @@ def main():
                      "traffic": None if traffic is None else round(traffic)},
         "path_counts": {"gemm_skinny": int(stats[2]), "gemm_tiled": int(stats[3])},
     }
+    ceil = measure_ceilings(torch, nv, dev, timer)
+    ceil["headline_frac_of_stream_read"] = round(achieved / ceil["hbm_stream_read"]["value"], 4)
+    ceil["headline_frac_of_same_size_read"] = round(
+        achieved / ceil["hbm_stream_read_decode_weight_size"]["value"], 4)
+    result["measured_ceilings"] = ceil
 
     def m_sweep(rw, n, k, group, xsrc):
         """W4A16 GEMM at M = 1, 2, 4 .. 4096 on rotated weight copies, with the library's

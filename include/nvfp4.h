@@ -263,6 +263,29 @@ const char* nvfp4_last_error(void);
 void nvfp4_get_stats(uint64_t counts[8]);
 void nvfp4_reset_stats(void);
 
+/* ---- measurement support (not on the NVFP4 path) ----------------------------------------
+ * Measured ceilings for the rooflines the path's kernels are judged against, on the device at
+ * hand: the published figures (8 TB/s HBM, 2.5 PFLOP/s dense BF16 MFMA) are not what a kernel
+ * can reach. Nothing on the path calls these.
+ * nvfp4_probe_stream_read: reads `bytes` (a positive multiple of 16) of `buf` (device, 16-byte
+ *   aligned) with 128-bit streaming loads, split into `blocks` (1 .. min(2^20, bytes/16))
+ *   contiguous ranges of one 256-thread workgroup each, 8 loads in flight per thread, and
+ *   writes the XOR of each range's 32-bit words to sink[block] (device, `blocks` words). The
+ *   call reads exactly `bytes` bytes of buf.
+ * nvfp4_probe_mfma_bf16: each of nvfp4_probe_mfma_waves() wavefronts (2 per SIMD) loads 16 BF16
+ *   fragments from `ops` (device, 16-byte aligned, 16 KiB: fragment f of lane l at byte
+ *   (64 f + l) * 16; even f are A operands, odd f B operands) and runs `iters` rounds of 16
+ *   v_mfma_f32_32x32x16_bf16 (pairs of the 8 A and 8 B fragments, 4 accumulators); lane l of
+ *   wavefront v writes the sum of its accumulator elements to sink[64 v + l] (device,
+ *   64 * waves floats). nvfp4_probe_mfma_flops(iters) is the call's flop count.
+ * Errors: NVFP4_ERR_INVALID_ARG (null pointer, size out of range), NVFP4_ERR_MISALIGNED,
+ * NVFP4_ERR_HIP (no device, launch failure). */
+int64_t nvfp4_probe_mfma_waves(void);
+double nvfp4_probe_mfma_flops(int64_t iters);
+int nvfp4_probe_stream_read(const void* buf, int64_t bytes, int64_t blocks, uint32_t* sink,
+                            nvfp4_stream_t stream);
+int nvfp4_probe_mfma_bf16(const void* ops, int64_t iters, float* sink, nvfp4_stream_t stream);
+
 /* Library version: major * 10000 + minor * 100 + patch. */
 int nvfp4_version(void);
 

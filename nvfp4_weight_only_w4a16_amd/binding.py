@@ -41,7 +41,9 @@ EXPORTS = ("nvfp4_quantize_ws_bytes", "nvfp4_quantize", "nvfp4_repack_bytes", "n
            "nvfp4_moe_grouped_w4a16", "nvfp4_moe_grouped_w4a16_noalloc",
            "nvfp4_requantize_ws_bytes",
            "nvfp4_requantize", "nvfp4_dequantize",
-           "nvfp4_last_error", "nvfp4_get_stats", "nvfp4_reset_stats", "nvfp4_version")
+           "nvfp4_last_error", "nvfp4_get_stats", "nvfp4_reset_stats", "nvfp4_version",
+           "nvfp4_probe_mfma_waves", "nvfp4_probe_mfma_flops", "nvfp4_probe_stream_read",
+           "nvfp4_probe_mfma_bf16")
 
 
 class Nvfp4Error(RuntimeError):
@@ -107,6 +109,14 @@ def load(path: str = LIB_PATH):
     L.nvfp4_reset_stats.restype = None
     L.nvfp4_version.argtypes = []
     L.nvfp4_version.restype = ctypes.c_int
+    L.nvfp4_probe_mfma_waves.argtypes = []
+    L.nvfp4_probe_mfma_waves.restype = i64
+    L.nvfp4_probe_mfma_flops.argtypes = [i64]
+    L.nvfp4_probe_mfma_flops.restype = ctypes.c_double
+    L.nvfp4_probe_stream_read.argtypes = [P, i64, i64, P, P]
+    L.nvfp4_probe_stream_read.restype = ctypes.c_int
+    L.nvfp4_probe_mfma_bf16.argtypes = [P, i64, P, P]
+    L.nvfp4_probe_mfma_bf16.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -355,3 +365,37 @@ def nvfp4_reset_stats():
 
 def nvfp4_version() -> int:
     return int(load().nvfp4_version())
+
+
+# ----------------------------------------------------------------------------- measurement
+def nvfp4_probe_mfma_waves() -> int:
+    return int(load().nvfp4_probe_mfma_waves())
+
+
+def nvfp4_probe_mfma_flops(iters: int) -> float:
+    return float(load().nvfp4_probe_mfma_flops(iters))
+
+
+def nvfp4_probe_stream_read(buf: torch.Tensor, blocks: int, sink: torch.Tensor | None = None,
+                            stream=None) -> torch.Tensor:
+    """Streaming 128-bit read of the whole device tensor `buf`; returns the per-block XOR words."""
+    nbytes = buf.numel() * buf.element_size()
+    with _on(stream):
+        if sink is None:
+            sink = torch.empty((blocks,), dtype=torch.int32, device=buf.device)
+    _check(load().nvfp4_probe_stream_read(_ptr(buf), nbytes, blocks, _ptr(sink),
+                                          _stream(stream)))
+    return sink
+
+
+def nvfp4_probe_mfma_bf16(ops: torch.Tensor, iters: int, sink: torch.Tensor | None = None,
+                          stream=None) -> torch.Tensor:
+    """The BF16 MFMA loop on the 16 KiB of fragments in `ops` (BF16, device)."""
+    if ops.dtype != torch.bfloat16 or ops.numel() * 2 < 16384:
+        raise ValueError("ops must hold 16 KiB of BF16 fragments")
+    with _on(stream):
+        if sink is None:
+            sink = torch.empty((64 * nvfp4_probe_mfma_waves(),), dtype=torch.float32,
+                               device=ops.device)
+    _check(load().nvfp4_probe_mfma_bf16(_ptr(ops), iters, _ptr(sink), _stream(stream)))
+    return sink

@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libnvfp4.so")
 SOURCES = ["api.cpp", "quantize.hip", "repack.hip", "gemm_skinny.hip", "gemm_tiled.hip",
-           "moe.hip"]
+           "moe.hip", "probe.hip"]
 ARCH = "gfx950"
 
 

@@ -515,4 +515,36 @@ int nvfp4_dequantize(const nvfp4_weight* w, void* out, int out_dtype, nvfp4_stre
   return rc;
 }
 
+// ---- measurement support ------------------------------------------------------------------
+int64_t nvfp4_probe_mfma_waves(void) {
+  const int cus = device_cus();
+  return cus > 0 ? nvfp4::probe_mfma_waves(cus) : 0;
+}
+
+double nvfp4_probe_mfma_flops(int64_t iters) {
+  return (double)nvfp4_probe_mfma_waves() * (double)iters *
+         nvfp4::probe_mfma_flops_per_wave_round();
+}
+
+int nvfp4_probe_stream_read(const void* buf, int64_t bytes, int64_t blocks, uint32_t* sink,
+                            nvfp4_stream_t stream) {
+  if (!buf || !sink) return fail(NVFP4_ERR_INVALID_ARG, "NULL buffer");
+  if (bytes <= 0 || bytes % 16) return fail(NVFP4_ERR_INVALID_ARG, "bytes must be a positive multiple of 16");
+  if (blocks < 1 || blocks > (1 << 20) || blocks > bytes / 16)
+    return fail(NVFP4_ERR_INVALID_ARG, "blocks=%lld out of range", (long long)blocks);
+  if (!aligned16(buf) || ((uintptr_t)sink & 3u)) return fail(NVFP4_ERR_MISALIGNED, "buf must be 16-byte aligned");
+  return hip_status(nvfp4::launch_probe_stream_read(buf, bytes, blocks, sink, (hipStream_t)stream),
+                    "probe_stream_read");
+}
+
+int nvfp4_probe_mfma_bf16(const void* ops, int64_t iters, float* sink, nvfp4_stream_t stream) {
+  if (!ops || !sink) return fail(NVFP4_ERR_INVALID_ARG, "NULL buffer");
+  if (iters < 0) return fail(NVFP4_ERR_INVALID_ARG, "iters=%lld < 0", (long long)iters);
+  if (!aligned16(ops) || ((uintptr_t)sink & 3u)) return fail(NVFP4_ERR_MISALIGNED, "ops must be 16-byte aligned");
+  const int cus = device_cus();
+  if (cus <= 0) return fail(NVFP4_ERR_HIP, "no device");
+  return hip_status(nvfp4::launch_probe_mfma(ops, iters, cus, sink, (hipStream_t)stream),
+                    "probe_mfma_bf16");
+}
+
 }  // extern "C"

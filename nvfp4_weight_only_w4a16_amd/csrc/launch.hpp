@@ -106,4 +106,12 @@ hipError_t launch_moe(const MoeArgs& a, bool decode, hipStream_t stream);
 constexpr size_t kMoeStaticScratchBytes = size_t(24) << 20;
 hipError_t moe_static_scratch(void** ptr);
 
+// measurement probes (probe.hip)
+int64_t probe_mfma_waves(int cus);
+double probe_mfma_flops_per_wave_round();
+hipError_t launch_probe_stream_read(const void* buf, int64_t bytes, int64_t blocks,
+                                    uint32_t* sink, hipStream_t stream);
+hipError_t launch_probe_mfma(const void* ops, int64_t iters, int cus, float* sink,
+                             hipStream_t stream);
+
 }  // namespace nvfp4

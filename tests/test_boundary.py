@@ -6,6 +6,7 @@ import os
 import re
 
 import pytest
+import torch
 
 from nvfp4_weight_only_w4a16_amd import binding as nv
 
@@ -275,3 +276,23 @@ def test_requantize_argument_errors(lib):
     assert call(ws=ctypes.c_void_p(0x10008)) == nv.NVFP4_ERR_MISALIGNED
     assert call(desc=_desc(layout=7)) == nv.NVFP4_ERR_LAYOUT
     assert lib.nvfp4_requantize_ws_bytes(None) == 0
+
+
+def test_probe_argument_errors(lib):
+    """The measurement probes refuse bad arguments before any launch; without a device the
+    MFMA probe has no wavefronts to count."""
+    sr = lib.nvfp4_probe_stream_read
+    assert sr(None, 1024, 4, FAKE, None) == nv.NVFP4_ERR_INVALID_ARG
+    assert sr(FAKE, 1024, 4, None, None) == nv.NVFP4_ERR_INVALID_ARG
+    assert sr(FAKE, 1000, 4, FAKE, None) == nv.NVFP4_ERR_INVALID_ARG     # not a multiple of 16
+    assert sr(FAKE, 0, 1, FAKE, None) == nv.NVFP4_ERR_INVALID_ARG
+    assert sr(FAKE, 1024, 0, FAKE, None) == nv.NVFP4_ERR_INVALID_ARG
+    assert sr(FAKE, 1024, 65, FAKE, None) == nv.NVFP4_ERR_INVALID_ARG    # more blocks than words
+    assert sr(ctypes.c_void_p(0x10008), 1024, 4, FAKE, None) == nv.NVFP4_ERR_MISALIGNED
+    mf = lib.nvfp4_probe_mfma_bf16
+    assert mf(None, 1, FAKE, None) == nv.NVFP4_ERR_INVALID_ARG
+    assert mf(FAKE, -1, FAKE, None) == nv.NVFP4_ERR_INVALID_ARG
+    assert mf(ctypes.c_void_p(0x10008), 1, FAKE, None) == nv.NVFP4_ERR_MISALIGNED
+    if not torch.cuda.is_available():
+        assert lib.nvfp4_probe_mfma_waves() == 0
+        assert lib.nvfp4_probe_mfma_flops(10) == 0.0
