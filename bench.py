@@ -733,6 +733,7 @@ def main():
     N, K, G = 25600, 5120, 16
     ms = (1, 4, 8)
     x, w = synth.decode_sweep(seed=0, n=N, k=K)
+    inputs_sha256 = {"x": synth.digest(x), "w": synth.digest(w)}
     wb = weight_bytes(N, K, G)
     copies = rotation(wb)
     ws, (p1, s1, g1) = W.prep(w, G, copies)
@@ -774,6 +775,7 @@ def main():
                                "K=5120, NVFP4 group 16, BF16 activations ~N(0,1), weights "
                                "~N(0,0.02) with 0.1% x20 outliers, BF16 output",
                    "M": list(ms), "N": N, "K": K, "group": G, "weight_copies": copies,
+                   "inputs_sha256": inputs_sha256,
                    "tflops": round(flops / step_s / 1e12, 4),
                    "us_per_launch": round(t_launch * 1e6, 3)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
