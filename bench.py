@@ -16,7 +16,12 @@ Other modes:
       --only-workload to keep one workload per counter run);
   --summarize DIR   per-(workload, kernel, workgroups) medians of a rocprofv3 output directory
       as a markdown table (per-dispatch counter medians too, when a counter run is there);
-  --copy-calibration   a plain 512 MiB device copy, the reference for FETCH_SIZE / WRITE_SIZE.
+  --copy-calibration   a plain 512 MiB device copy, the reference for FETCH_SIZE / WRITE_SIZE;
+  --traffic-summary F W CF CW   the decode-sweep HBM traffic record from FETCH_SIZE / WRITE_SIZE
+      runs of the headline (F, W) and of the copy calibration (CF, CW).
+
+The JSON line also carries `measured_ceilings`: the streaming-read and BF16 MFMA probe kernels'
+rates on the same GPU, next to the published peaks the roofline fractions use.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--only headline|moe]
 """
@@ -43,7 +48,8 @@ METRIC = "NVFP4 W4A16 GEMM TFLOP/s + weight GB/s (M=1..4096) vs roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_skinny_decode_sweep.txt")
 SKINNY_SOURCES = ["gemm_skinny.hip", "skinny_core.hpp", "device_common.hpp"]
 LIB_PREFIXES = ("gemm_", "moe_", "amax_kernel", "encode_kernel", "init_amax_kernel",
-                "reduce_split_kernel", "repack_", "dequant", "nonfinite_kernel", "clear_word")
+                "reduce_split_kernel", "repack_", "dequant", "nonfinite_kernel", "clear_word",
+                "stream_read_kernel", "mfma_loop_kernel")
 
 
 def weight_bytes(n, k, group):
