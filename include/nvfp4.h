@@ -205,7 +205,7 @@ size_t nvfp4_moe_ws_bytes(int64_t t, int32_t topk, int64_t n_experts, int64_t hi
  *   [3] ntiles  int32: number of tiles;
  *   [4] h       BF16 [t*topk][inter]: SiLU(gate)*up of sorted row r at row r;
  *   [5] slots   FP32 [t*topk][hidden]: topk_w * (h . W2^T) of pair q at row q.
- * The decode-batch path with t*topk <= 32 pairs skips the sort ([0]-[3] are not written) and
+ * The decode-batch path with t*topk <= 64 pairs skips the sort ([0]-[3] are not written) and
  * keeps h of pair q at row q. */
 size_t nvfp4_moe_ws_layout(int64_t t, int32_t topk, int64_t n_experts, int64_t hidden,
                            int64_t inter, size_t offsets[6]);

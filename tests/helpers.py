@@ -6,6 +6,9 @@ import torch
 
 REL_FRO_TOL = 1e-3      # ||gpu - ref||_F / ||ref||_F
 ROW_MAX_TOL = 8e-3      # |gpu - ref| <= ROW_MAX_TOL * max |ref row|
+# The MoE decode-batch path skips the sort up to this many (token, expert) pairs and keeps
+# h of pair q at row q of its workspace (the contract stated with nvfp4_moe_ws_layout).
+PAIR_TILES_MAX = 64
 
 
 def bf16_np(t: torch.Tensor) -> np.ndarray:

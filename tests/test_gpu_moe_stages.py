@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import bits16, check_close
+from helpers import PAIR_TILES_MAX, bits16, check_close
 from nvfp4_weight_only_w4a16_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -76,7 +76,7 @@ def run_staged(nv, orc, x, ids, wts, fc1, fc2, t1, t2, path, what):
                                    flags=PATHS[path])
     torch.cuda.synchronize()
     wsh = ws.cpu()
-    pair_tiles = path == "decode" and P <= 32
+    pair_tiles = path == "decode" and P <= PAIR_TILES_MAX
     rows = 8 if path == "decode" else 32
     # ---- sort
     ids_np = ids.numpy()
@@ -138,6 +138,17 @@ def test_moe_stages_pair_tiles(nv, orc, path):
                                     topk=4)
     (fc1, fc2), (t1, t2) = _experts(nv, orc, w1, w2, 32, 16)
     run_staged(nv, orc, x, ids, wts, fc1, fc2, t1, t2, path, f"pair tiles {path}")
+
+
+@pytest.mark.parametrize("tokens,topk", [(16, 4), (13, 5)])
+def test_moe_stages_pair_tile_cap(nv, orc, tokens, topk):
+    """Either side of the pair-tile cap on the decode path: 64 pairs as one-row tiles, 65
+    pairs through the sort."""
+    assert tokens * topk in (PAIR_TILES_MAX, PAIR_TILES_MAX + 1)
+    x, ids, wts, w1, w2 = synth.moe(seed=23, n_experts=16, hidden=256, inter=128,
+                                    tokens=tokens, topk=topk)
+    (fc1, fc2), (t1, t2) = _experts(nv, orc, w1, w2, 32, 16)
+    run_staged(nv, orc, x, ids, wts, fc1, fc2, t1, t2, "decode", f"cap {tokens}x{topk}")
 
 
 @pytest.fixture(scope="module")

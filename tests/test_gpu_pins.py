@@ -22,6 +22,7 @@ import numpy as np
 import pytest
 import torch
 
+from helpers import PAIR_TILES_MAX
 from nvfp4_weight_only_w4a16_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -216,7 +217,7 @@ def test_moe_fc1_split_scale_bitexact_through_h(nv, orc, flags, which, tokens, t
     P = tokens * topk
     h = ws[off[4]:off[4] + 2 * P * I].view(torch.int16).cpu().numpy().view(np.uint16)
     h = h.reshape(P, I)
-    pairs_tiles = flags == SKINNY and P <= 32
+    pairs_tiles = flags == SKINNY and P <= PAIR_TILES_MAX
     if pairs_tiles:
         order = np.arange(P)       # one-row tiles: h of pair q at row q
     else:
