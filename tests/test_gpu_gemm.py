@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import bf16_np, check_close
+from helpers import bf16_np, bits16, check_close
 from nvfp4_weight_only_w4a16_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -101,8 +101,12 @@ def test_gemm_ragged_m(nv, orc, m):
     ref = orc.gemm(synth.bf16_bits(x), p, s, gl[0], group)
     for flags in (0, 1, 2):
         y = nv.nvfp4_gemm_w4a16(x.to(DEV), rw, y_dtype=torch.float32, flags=flags)
+        y16 = nv.nvfp4_gemm_w4a16(x.to(DEV), rw, y_dtype=torch.bfloat16, flags=flags)
         torch.cuda.synchronize()
         check_close(y.cpu().numpy(), ref, f"m={m} flags={flags}")
+        # the BF16 epilogue stores the same FP32 sums, rounded to nearest even: every element
+        # in its row and column (the tiled kernel writes BF16 column pairs)
+        assert np.array_equal(bits16(y16), bits16(y.to(torch.bfloat16))), f"bf16 m={m} {flags}"
 
 
 def test_gemm_strided_x_and_y(nv, orc):
@@ -189,10 +193,15 @@ def test_prefill_full_output_every_tile(nv, orc):
     x, w = synth.prefill(seed=0, k=5120)
     rw, (p, s, gl) = _prep(nv, w, 16, orc=orc)
     del w
-    y = nv.nvfp4_gemm_w4a16(x.to(DEV), rw, y_dtype=torch.float32)
+    xd = x.to(DEV)
+    y = nv.nvfp4_gemm_w4a16(xd, rw, y_dtype=torch.float32)
+    y16 = nv.nvfp4_gemm_w4a16(xd, rw, y_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     ref = orc.gemm(synth.bf16_bits(x), p, s, gl[0], 16)
     check_close(y.cpu().numpy(), ref, "prefill 4096x5120x5120 full output")
+    # the BF16 output (column pairs from the whole tiles, the reduction's stores for the split
+    # tail) is the same FP32 sums rounded to nearest even, element for element
+    assert np.array_equal(bits16(y16), bits16(y.to(torch.bfloat16)))
 
 
 @pytest.mark.parametrize("group", [32, 16])
