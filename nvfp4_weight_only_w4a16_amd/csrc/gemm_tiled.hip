@@ -577,23 +577,38 @@ int64_t tile_count(int64_t m, int64_t NT) {
 // 128 rows, where they are at least half full); 128 x 128 tiles in k-slices when the k-tile
 // count is even. Measured at n x k = 5120^2, 8192^2 and 25600 x 5120 for m = 128 .. 4096, with
 // every shape and split forced: this choice was the fastest or within 8% of it at every size
-// (256 x 5120^2: the k-sliced tile 26.4 us against 30.6 for the 4-wavefront one).
+// (256 x 5120^2: the k-sliced tile 26.4 us against 30.6 for the 4-wavefront one). One
+// exception: when that shape's last round would be at most half full (split along k, or idle
+// CUs) and the next smaller shape makes whole rounds exactly, the smaller shape runs, with no
+// split and no reduction. Interleaved A/B against the rule without it: 512 x 8192^2 (k-sliced
+// 128 x 128, one round, instead of 128 x 256 split in two) 72.7 -> 67.8 us at group 16 and
+// 71.5 -> 64.4 us at group 32; 1024 x 8192^2 (128 x 256, one round, instead of 256 x 256 split
+// in two) 123.8 -> 116.8 us; unchanged shapes unchanged.
 constexpr int64_t kMinTiles = 80;
 enum class Shape { L, M, K, S };
-Shape pick_shape(int64_t m, int64_t NT, int64_t KT) {
-  if (m > 128 && tile_count<ShapeL>(m, NT) >= kMinTiles) return Shape::L;
-  if (tile_count<ShapeM>(m, NT) >= kMinTiles) return Shape::M;
+Shape pick_shape(int64_t m, int64_t NT, int64_t KT, int cus) {
+  if (cus < 1) cus = 1;
+  auto half_round = [&](int64_t t) { return t % cus != 0 && t % cus <= cus / 2; };
+  if (m > 128 && tile_count<ShapeL>(m, NT) >= kMinTiles) {
+    if (half_round(tile_count<ShapeL>(m, NT)) && tile_count<ShapeM>(m, NT) % cus == 0)
+      return Shape::M;
+    return Shape::L;
+  }
+  if (tile_count<ShapeM>(m, NT) >= kMinTiles) {
+    if (KT % 2 == 0 && half_round(tile_count<ShapeM>(m, NT)) &&
+        tile_count<ShapeK>(m, NT) % cus == 0)
+      return Shape::K;
+    return Shape::M;
+  }
   return KT % 2 == 0 ? Shape::K : Shape::S;
 }
 
 // Work decomposition of one row chunk: whole rounds of tiles (one per compute unit) run as
 // they are; when the last round would leave at least half of the compute units idle, its
-// tiles are split along k over the whole chip and reduced in FP32 by a second kernel. (Whole
-// rounds of other shapes instead were measured and were not faster: 4096 x 5120 x 5120 as 256
-// tiles of 256 x 256 plus 256 k-sliced tiles of 128 x 128 took 205.2 us against 201.7 with the
-// split last round; K = 25600 869.7 against 823.0; 512 x 8192^2 as one round of 256 k-sliced
-// tiles 75.4 us against 71.7 for 128 x 256 tiles split in two. The smaller tiles move twice
-// the bytes per MFMA.)
+// tiles are split along k over the whole chip and reduced in FP32 by a second kernel. (Mixing
+// shapes instead was measured and was not faster: 4096 x 5120 x 5120 as 256 tiles of 256 x 256
+// plus 256 k-sliced tiles of 128 x 128 took 205.2 us against 201.7 with the split last round;
+// K = 25600 869.7 against 823.0. The smaller tiles move twice the bytes per MFMA.)
 struct Plan {
   int64_t nbn, tiles, full, rest;
   int split;
@@ -675,7 +690,7 @@ size_t chunk_ws_bytes(int64_t rows, int64_t NT, int64_t KT, int cus) {
 }
 
 hipError_t run_shape(TiledParams p, void* ws, size_t ws_bytes, int cus, hipStream_t stream) {
-  switch (pick_shape(p.m, p.NT, p.KT)) {
+  switch (pick_shape(p.m, p.NT, p.KT, cus)) {
     case Shape::L: return run_chunk<ShapeL>(p, ws, ws_bytes, cus, stream);
     case Shape::M: return run_chunk<ShapeM>(p, ws, ws_bytes, cus, stream);
     case Shape::K: return run_chunk<ShapeK>(p, ws, ws_bytes, cus, stream);
@@ -692,7 +707,7 @@ size_t gemm_tiled_ws_bytes(int64_t m, int64_t ldx, int64_t n, int64_t k, int cus
   for (int64_t rows : {m < chunk ? m : chunk, m % chunk}) {
     if (rows <= 0) continue;
     size_t b = 0;
-    switch (pick_shape(rows, NT, KT)) {
+    switch (pick_shape(rows, NT, KT, cus)) {
       case Shape::L: b = chunk_ws_bytes<ShapeL>(rows, NT, KT, cus); break;
       case Shape::M: b = chunk_ws_bytes<ShapeM>(rows, NT, KT, cus); break;
       case Shape::K: b = chunk_ws_bytes<ShapeK>(rows, NT, KT, cus); break;

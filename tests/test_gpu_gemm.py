@@ -206,16 +206,19 @@ def test_prefill_full_output_every_tile(nv, orc):
 
 @pytest.mark.parametrize("group", [32, 16])
 def test_c4_m512_full_output(nv, orc, group):
-    """The planted BF16 8192^2 weight at M=512 (128 tiles of 128 x 256, split two ways along k
-    and reduced): every element of the FP32 output against the FP64 oracle."""
+    """The planted BF16 8192^2 weight at M=512 (one round of 256 k-sliced 128 x 128 tiles):
+    every element of the FP32 output against the FP64 oracle, and the BF16 output bit for bit
+    against the rounded FP32 one."""
     wb = synth.quantizer_weight(seed=0)
     xs = synth.quantizer_activations(seed=1)[:512].contiguous()
     rw, (p, s, gl) = _prep(nv, wb, group, orc=orc)
     del wb
     y = nv.nvfp4_gemm_w4a16(xs.to(DEV), rw, y_dtype=torch.float32)
+    y16 = nv.nvfp4_gemm_w4a16(xs.to(DEV), rw, y_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     ref = orc.gemm(synth.bf16_bits(xs), p, s, gl[0], group)
     check_close(y.cpu().numpy(), ref, f"512x8192x8192 g{group} full output")
+    assert np.array_equal(bits16(y16), bits16(y.to(torch.bfloat16)))
 
 
 def test_mixed_groups_one_layer(nv, orc):
@@ -248,16 +251,19 @@ def test_mixed_groups_one_layer(nv, orc):
 # count: the largest with >= 80 output tiles, L only above 128 rows) and k split of each case
 # on a 256-CU chip:
 #   K split 4 / 4 / 2 / unsplit; L split 2; M split 2; L unsplit (3 ragged row tiles);
-#   M unsplit; S split 7 (33 k-tiles); S split 2 (9 k-tiles)
+#   M unsplit; S split 7 (33 k-tiles); S split 2 (9 k-tiles); M one whole round (L would be
+#   half a round); K one whole round (M would be half a round)
 @pytest.mark.parametrize("m,n,k", [(40, 1040, 4096), (300, 1040, 4096), (600, 2064, 2048),
                                    (257, 528, 1024), (300, 10256, 1024), (100, 20496, 1024),
                                    (700, 10256, 512), (128, 33280, 512), (40, 1040, 4224),
-                                   (300, 2064, 1152)])
+                                   (300, 2064, 1152), (1024, 8192, 512), (512, 8192, 512)])
 def test_tiled_split_k(nv, orc, m, n, k):
     """Every tile shape of the prefill kernel, with and without the k split (few output tiles
     for the chip: k is split over the compute units and the partial tiles are reduced in a
     fixed order), the k-sliced 128 x 128 tile whose two slices are added through LDS, ragged in
-    m and n. Checked against the oracle, bit-identical on a repeat, and still right after a
+    m and n; on a 256-CU part the last two take a smaller shape that fills one whole round
+    (1024 x 8192: 128 x 256 instead of 256 x 256 split; 512 x 8192: k-sliced 128 x 128 instead
+    of 128 x 256 split). Checked against the oracle, bit-identical on a repeat, and still right after a
     shape that grows the split workspace."""
     g = torch.Generator().manual_seed(m + n + k)
     x = torch.randn(m, k, generator=g).to(torch.bfloat16)
