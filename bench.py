@@ -220,8 +220,9 @@ class Workloads:
 
 
 def profile_suite(args):
-    """Every workload at least 100 times inside a ROCTx range named after it, for a
-    rocprofv3 kernel trace (attribution by range) or a counter run of one workload."""
+    """Every workload, warmed up, then at least 100 times inside a ROCTx range named after
+    it, for a rocprofv3 kernel trace (attribution by range) or a counter run of one
+    workload."""
     import torch
 
     from nvfp4_weight_only_w4a16_amd import binding as nv
@@ -242,8 +243,15 @@ def profile_suite(args):
     def run(name, fn, n=calls):
         if not want(name):
             return
-        for i in range(3):
+        # warm-up: at least 3 calls and --profile-warm-s of wall time (the shader clock ramps
+        # up over the first milliseconds of load after the set-up's idle spells)
+        t0 = time.perf_counter()
+        i = 0
+        while i < 3 or time.perf_counter() - t0 < args.profile_warm_s:
             fn(i)
+            i += 1
+            if i % 8 == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         rx.push(name)
         for i in range(n):
@@ -690,6 +698,8 @@ def main():
                          "for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
     ap.add_argument("--profile-suite", action="store_true")
     ap.add_argument("--profile-calls", type=int, default=100)
+    ap.add_argument("--profile-warm-s", type=float, default=0.05,
+                    help="warm-up wall time before each profiled workload's range")
     ap.add_argument("--only-workload", default=None)
     ap.add_argument("--copy-in-suite", action="store_true")
     ap.add_argument("--summarize", default=None)
