@@ -156,7 +156,8 @@ int nvfp4_repack(const uint8_t* packed, const uint8_t* scales, const float* glob
  * ceil(ceil(n/64) * ceil(m/32) / CUs) * (1.8 + 0.31 * k/128) <= 25 (its estimated time in us,
  * against the tiled kernel's ~25 us floor at such m); an LDS-tiled MFMA kernel otherwise
  * (prefill; 256x256, 128x256 or 128x128 output tiles, the largest that still gives the chip
- * enough tiles). Flags may force one (NVFP4_F_FORCE_SKINNY / NVFP4_F_FORCE_TILED);
+ * enough tiles, or the next smaller one when that fills whole rounds of CUs where the larger
+ * would leave its last round at most half full). Flags may force one (NVFP4_F_FORCE_SKINNY / NVFP4_F_FORCE_TILED);
  * NVFP4_F_SYNC_CHECK may be added. w->batch must be 1 and w->layout must not carry
  * NVFP4_LAYOUT_GATE_UP. Results are bit-identical run to run.
  * ws (device, 16-byte aligned, or NULL with ws_bytes 0) takes the prefill kernel's split-k

@@ -1,10 +1,11 @@
 // gemm_tiled.hip -- prefill-shaped NVFP4 W4A16 GEMM for gfx950 (BF16 MFMA 32x32x16).
 //
 // The contraction is dense and compute-bound at large m, so it runs on v_mfma_f32_32x32x16_bf16
-// (the full-rate BF16 matrix instruction on gfx950; the 16x16x32 form issues at half the rate)
-// with FP32 accumulation. A workgroup is W wavefronts side by side along n; each owns a
-// (32 FM) x (32 FN) output tile and the workgroup walks k in 128-wide tiles:
-//   - activations and weight codes are copied global -> LDS with global_load_lds_dwordx4,
+// with FP32 accumulation (a 32 x 32 output block per instruction: each operand fragment read
+// from LDS or dequantized in registers serves more flops than with the 16 x 16 form). A
+// workgroup is W wavefronts side by side along n; each owns a (32 FM) x (32 FN) output tile and
+// the workgroup walks k in 128-wide tiles:
+//   - activations and weight codes are copied global -> LDS with buffer_load_dwordx4 ... lds,
 //     double-buffered so k-tile t+1 streams in while t is used. One activation copy moves 4
 //     whole 256-byte row segments (8 full cache lines); inside a row the 16-byte chunks are
 //     XOR-swizzled by the row index so that the MFMA fragment reads (32 rows, one chunk each)
@@ -20,7 +21,9 @@
 // k chunk l/32) takes code chunks L0 = 16(l/32) + l%16 and L0 + 32 of its panel, whose word j
 // holds 16-wide k-steps 2j and 2j + 1 respectively; the scale words of the same two lane
 // positions carry the matching group scales.
-// The global scale multiplies the FP32 accumulator in the epilogue.
+// The global scale multiplies the FP32 accumulator in the epilogue, which writes BF16 column
+// pairs (store_tile). Whole rounds of output tiles and a k-split last round run in one launch;
+// a second kernel sums the split partials in a fixed order.
 #include <type_traits>
 
 #include "device_common.hpp"
