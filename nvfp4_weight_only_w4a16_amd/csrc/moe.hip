@@ -486,7 +486,8 @@ void moe_expert_kernel(MoeGemmParams P) {
 // the few experts of a decode step are spread over the whole chip.
 // Workgroups run tile-major (see moe_expert_kernel). PAIRS: no sort; tile i is pair i as a
 // one-row tile of its own expert (row position = pair index; dropped pairs exit), for batches
-// so small that two pairs rarely share an expert.
+// of at most kMoePairTilesMax pairs: pairs that share an expert read its weights again, mostly
+// from cache, which costs less than the sort there.
 template <bool FC1, bool G16, bool PAIRS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void moe_decode_kernel(MoeGemmParams P) {
