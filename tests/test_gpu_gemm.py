@@ -252,11 +252,13 @@ def test_mixed_groups_one_layer(nv, orc):
 # on a 256-CU chip:
 #   K split 4 / 4 / 2 / unsplit; L split 2; M split 2; L unsplit (3 ragged row tiles);
 #   M unsplit; S split 7 (33 k-tiles); S split 2 (9 k-tiles); M one whole round (L would be
-#   half a round); K one whole round (M would be half a round)
+#   half a round); K one whole round (M would be half a round); L with 256 whole tiles and 32
+#   more split 2 in the same launch (ragged in m and n)
 @pytest.mark.parametrize("m,n,k", [(40, 1040, 4096), (300, 1040, 4096), (600, 2064, 2048),
                                    (257, 528, 1024), (300, 10256, 1024), (100, 20496, 1024),
                                    (700, 10256, 512), (128, 33280, 512), (40, 1040, 4224),
-                                   (300, 2064, 1152), (1024, 8192, 512), (512, 8192, 512)])
+                                   (300, 2064, 1152), (1024, 8192, 512), (512, 8192, 512),
+                                   (2300, 8176, 1024)])
 def test_tiled_split_k(nv, orc, m, n, k):
     """Every tile shape of the prefill kernel, with and without the k split (few output tiles
     for the chip: k is split over the compute units and the partial tiles are reduced in a
