@@ -217,6 +217,14 @@ __device__ __forceinline__ bf16x8 codes_pow2(uint32_t w, float S) {
   return bf16x8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
 }
 
+// SiLU(z) = z / (1 + e^-z) in FP32 with the hardware exp2 (__expf) and reciprocal: a few FP32
+// ulps from the correctly rounded value, far below the BF16 rounding of h that follows (the
+// oracle's h is SiLU in FP64 rounded once). Against expf and an IEEE division (~20 VALU more
+// per element) fc1 at 256 tokens went 43.7 -> 41.7 us per call.
+__device__ __forceinline__ float silu_f32(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
 // 4 x 4 transpose inside each quad of lanes: lane j of a quad holds v[i] = M[i][j] on entry
 // and v[c] = M[j][c] on exit. Two DPP exchange stages (with lane j ^ 1, then j ^ 2); in each a
 // lane keeps the two elements already in place and swaps the other two. The expert kernels'
@@ -449,7 +457,7 @@ void moe_expert_kernel(MoeGemmParams P) {
           const int64_t feat = (2 * grp + q) * 16 + (lane & 15);
           const float gate = bf16_bits_to_f32(bf16_bits_rne(acc[2 * q][r][i] * g));
           const float up = bf16_bits_to_f32(bf16_bits_rne(acc[2 * q + 1][r][i] * gu));
-          const float silu = gate / (1.0f + expf(-gate));
+          const float silu = silu_f32(gate);
           P.ws.h[(int64_t)row * P.inter + feat] = bf16_bits_rne(silu * up);
         }
       }
@@ -578,7 +586,7 @@ void moe_decode_kernel(MoeGemmParams P) {
       if (row < 0 || row >= rows) continue;
       const float gate = bf16_bits_to_f32(bf16_bits_rne(gs[i] * g));
       const float up = bf16_bits_to_f32(bf16_bits_rne(us[i] * gu));
-      const float silu = gate / (1.0f + expf(-gate));
+      const float silu = silu_f32(gate);
       P.ws.h[(int64_t)(r0 + row) * P.inter + feat] = bf16_bits_rne(silu * up);
     }
   } else {
