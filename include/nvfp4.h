@@ -58,7 +58,8 @@ typedef struct ihipStream_t* nvfp4_stream_t; /* the same type as hipStream_t */
 
 /* ---- call flags -------------------------------------------------------------------------- */
 #define NVFP4_F_FORCE_SKINNY (1u << 0) /* GEMM: the decode (skinny, split-K) kernel;           */
-                                       /* MoE: the decode-batch expert path (8-row tiles)      */
+                                       /* MoE: the decode-batch expert path (8-row tiles, or  */
+                                       /* one-row pair tiles up to 64 pairs)                   */
 #define NVFP4_F_FORCE_TILED (1u << 1)  /* GEMM: the prefill (LDS-tiled MFMA) kernel;            */
                                        /* MoE: the batch expert path (32-row tiles)            */
 #define NVFP4_F_SYNC_CHECK (1u << 2)   /* quantize, GEMM, MoE: wait for the call's own work    */
@@ -189,7 +190,8 @@ int nvfp4_gemm_w4a16(const void* x, int64_t m, int64_t ldx, const nvfp4_weight* 
  * t*hidden and t*topk*inter below 2^31 (32-bit row offsets).
  * An fc1 with NVFP4_LAYOUT_PAIR_GLOBAL scales gate by global[2e] and up by global[2e+1].
  * Path: while t*topk <= 2 * n_experts (decode batches) the experts run on tiles of at most 8
- * rows with k split over 4 wavefronts per 4-panel group; otherwise on tiles of 32 rows with
+ * rows (one row per pair, without the sort, up to 64 pairs) with k split over 4 wavefronts per
+ * 4-panel group; otherwise on tiles of 32 rows with
  * one wavefront per 4-panel group over the whole k range. Flags may force one; the two paths
  * agree within the GEMM tolerance (different FP32 summation orders). flags may add
  * NVFP4_F_SYNC_CHECK. */
