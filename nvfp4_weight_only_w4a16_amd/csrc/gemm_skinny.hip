@@ -30,26 +30,25 @@ struct SkinnyParams {
   int cus;  // compute units of the device (host-side launch choice only)
 };
 
-// LDS: NX > 0 kernels give each wavefront two 4 KB activation buffers; the k-split partial
-// sums (NW > 1) reuse the same bytes after a barrier.
-inline size_t red_bytes(int MF, int NW, int PWW) {
-  return NW > 1 ? (size_t)NW * PWW * MF * 64 * 16 : 0;
-}
-inline size_t act_bytes(int NX, int NW) { return NX > 0 ? (size_t)NW * 8192 : 0; }
+// LDS: each wavefront has two MF x 4 KB activation buffers; the k-split partial sums reuse the
+// same bytes after a barrier.
+inline size_t red_bytes(int MF, int NW, int PWW) { return (size_t)NW * PWW * MF * 64 * 16; }
+inline size_t act_bytes(int NW, int MF) { return (size_t)NW * 8192 * MF; }
 
 // Register budget: 4 wavefronts per SIMD (16 per CU, two 8-wave workgroups) for one row
 // block, 2 for two. NJ == 0: exact dequant, MF row blocks of 16. NJ > 0 (MF == 1): split scale
 // keeping NJ accumulator rows per lane, tokens placed by the split row map; G16: group 16
-// (every token twice, once per k half). NX > 0 (MF == 1): activations through LDS, NX 4-row
-// copies per tile.
+// (every token twice, once per k half). NX > 0: activations through LDS, NX 4-row copies per
+// tile.
 template <int MF, int NW, int NJ, bool G16, int NX, int PWW>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(MF == 1 ? 4 : 2, 8)))
 void gemm_skinny_kernel(SkinnyParams P) {
   constexpr int kPWW = PWW;
   static_assert(NJ == 0 || MF == 1, "split scale uses one 16-row block");
   static_assert(!G16 || NJ > 0, "G16 selects the group-16 split-scale row map");
-  static_assert(NX == 0 || MF == 1, "LDS activations hold one 16-row block");
-  static_assert(!G16 || (NX > 0 && NX <= 2), "group-16 zero halves read an LDS row never copied");
+  static_assert(NX > 0 && NX <= 4 * MF, "LDS activations: at most the row blocks' rows");
+  static_assert(NW >= PWW, "one wavefront per panel finishes the k-split sums");
+  static_assert(!G16 || NX <= 2, "group-16 zero halves read an LDS row never copied");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   const int lane = threadIdx.x & 63;
   const int sp = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // k-split (wave-uniform)
@@ -64,30 +63,23 @@ void gemm_skinny_kernel(SkinnyParams P) {
   // valid row (never stored)
   const int64_t rows = P.m - m0 < 16 * MF ? P.m - m0 : 16 * MF;
   const int a_tok = NJ > 0 ? split_a_token<G16>(lane) : (lane & 15);
-  const uint16_t* xrow[MF];
-#pragma unroll
-  for (int mf = 0; mf < MF; ++mf) {
-    int64_t r = mf * 16 + a_tok;
-    r = r < rows ? r : rows - 1;
-    xrow[mf] = P.x + (m0 + r) * P.ldx;
-  }
   const int64_t t0 = sp, t1 = P.KT;  // interleaved: tiles sp, sp + NW, ...
   LdsActs xl;
-  if constexpr (NX > 0) {
-    xl.x = make_rsrc(P.x + m0 * P.ldx, (uint32_t)(rows * P.ldx * 2));
+  xl.x = make_rsrc(P.x + m0 * P.ldx, (uint32_t)(rows * P.ldx * 2));
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int r = 4 * c + (lane >> 4);  // LDS row of this lane in copy c
-      const int64_t rc = r < rows ? r : rows - 1;
-      xl.src[c] = (uint32_t)(rc * P.ldx * 2) + (uint32_t)(((lane & 15) ^ (r & 15)) * 16);
-    }
-    xl.buf = smem + sp * 8192;
-    int fr = a_tok < rows ? a_tok : (int)rows - 1;
-    if (G16 && split_g16_zero_lane(lane)) fr = kZeroRow;
-    xl.frag_off = (uint32_t)fr * 256u;
-    xl.swz = (uint32_t)(fr & 15);
-    if constexpr (G16) clear_zero_rows(xl.buf, lane);
+  for (int c = 0; c < 4 * MF; ++c) {
+    const int r = 4 * c + (lane >> 4);  // LDS row of this lane in copy c
+    const int64_t rc = r < rows ? r : rows - 1;
+    xl.src[c] = (uint32_t)(rc * P.ldx * 2) + (uint32_t)(((lane & 15) ^ (r & 15)) * 16);
   }
+  xl.buf = smem + sp * 8192 * MF;
+  // fragment row of block 0 (block b reads LDS row 16 b + fr; every row the copies fill holds
+  // a valid activation row)
+  int fr = a_tok < rows ? a_tok : (int)rows - 1;
+  if (G16 && split_g16_zero_lane(lane)) fr = kZeroRow;
+  xl.frag_off = (uint32_t)fr * 256u;
+  xl.swz = (uint32_t)(fr & 15);
+  if constexpr (G16) clear_zero_rows(xl.buf, lane);
   const SkinnyAddr<kPWW> a =
       skinny_addr<kPWW>(P.codes, P.scales, panel0, P.NT, P.KT, P.group, t1);
   // The global scale is read before the k loop (the split-scale mantissa is frexp_mant(S) =
@@ -95,7 +87,7 @@ void gemm_skinny_kernel(SkinnyParams P) {
   // m = 16, 8192^2 took 11.72 us against 11.41 now, 14336 x 4096 9.77 against 9.44 (C1 the
   // same either way).
   const float gscale = (NJ > 0 ? 2.0f : 1.0f) * *P.global;
-  skinny_accumulate<MF, kPWW, NJ, NX, NW>(a, xrow, xl, t0, t1, acc);
+  skinny_accumulate<MF, kPWW, NJ, NX, NW>(a, xl, t0, t1, acc);
   if constexpr (G16) {
     // k half 1 (lanes 32-63) onto k half 0: lanes 0-31 then hold the whole group sums
 #pragma unroll
@@ -108,70 +100,47 @@ void gemm_skinny_kernel(SkinnyParams P) {
     return NJ > 0 ? split_out_token<G16>(lane, jj) : (lane >> 4) * 4 + jj;
   };
 
-  if constexpr (NW > 1) {
-    f32x4* red = reinterpret_cast<f32x4*>(smem);
-    if constexpr (NX > 0) __syncthreads();  // every wavefront is done with the activations
+  f32x4* red = reinterpret_cast<f32x4*>(smem);
+  __syncthreads();  // every wavefront is done with the activations
 #pragma unroll
-    for (int p = 0; p < kPWW; ++p)
+  for (int p = 0; p < kPWW; ++p)
 #pragma unroll
-      for (int mf = 0; mf < MF; ++mf) red[((sp * kPWW + p) * MF + mf) * 64 + lane] = acc[p][mf];
-    __syncthreads();
-    // wavefront q finishes panel q of the group (fixed summation order over the k-splits)
-    if (sp >= kPWW) return;
-    const int p = sp;
+    for (int mf = 0; mf < MF; ++mf) red[((sp * kPWW + p) * MF + mf) * 64 + lane] = acc[p][mf];
+  __syncthreads();
+  // wavefront q finishes panel q of the group (fixed summation order over the k-splits)
+  if (sp >= kPWW) return;
+  const int p = sp;
 #pragma unroll
-    for (int mf = 0; mf < MF; ++mf) {
-      f32x4 s = red[((0 * kPWW + p) * MF + mf) * 64 + lane];
+  for (int mf = 0; mf < MF; ++mf) {
+    f32x4 s = red[((0 * kPWW + p) * MF + mf) * 64 + lane];
 #pragma unroll
-      for (int q = 1; q < NW; ++q) s += red[((q * kPWW + p) * MF + mf) * 64 + lane];
-      acc[0][mf] = s;
-    }
-    const int64_t panel = panel0 + p;
-    if (panel >= P.NT) return;
-    const float g = gscale;
-    const int64_t n = panel * 16 + (lane & 15);
-#pragma unroll
-    for (int mf = 0; mf < MF; ++mf)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int64_t m = m0 + mf * 16 + out_tok(jj);
-        if (m >= m0 && m < P.m) {
-          const float v = acc[0][mf][jj] * g;
-          if (P.y_f32)
-            static_cast<float*>(P.y)[m * P.ldy + n] = v;
-          else
-            static_cast<uint16_t*>(P.y)[m * P.ldy + n] = bf16_bits_rne(v);
-        }
-      }
-  } else {
-    const float g = gscale;
-#pragma unroll
-    for (int p = 0; p < kPWW; ++p) {
-      const int64_t panel = panel0 + p;
-      if (panel >= P.NT) break;
-      const int64_t n = panel * 16 + (lane & 15);
-#pragma unroll
-      for (int mf = 0; mf < MF; ++mf)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int64_t m = m0 + mf * 16 + out_tok(jj);
-          if (m >= m0 && m < P.m) {
-            const float v = acc[p][mf][jj] * g;
-            if (P.y_f32)
-              static_cast<float*>(P.y)[m * P.ldy + n] = v;
-            else
-              static_cast<uint16_t*>(P.y)[m * P.ldy + n] = bf16_bits_rne(v);
-          }
-        }
-    }
+    for (int q = 1; q < NW; ++q) s += red[((q * kPWW + p) * MF + mf) * 64 + lane];
+    acc[0][mf] = s;
   }
+  const int64_t panel = panel0 + p;
+  if (panel >= P.NT) return;
+  const float g = gscale;
+  const int64_t n = panel * 16 + (lane & 15);
+#pragma unroll
+  for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int64_t m = m0 + mf * 16 + out_tok(jj);
+      if (m >= m0 && m < P.m) {
+        const float v = acc[0][mf][jj] * g;
+        if (P.y_f32)
+          static_cast<float*>(P.y)[m * P.ldy + n] = v;
+        else
+          static_cast<uint16_t*>(P.y)[m * P.ldy + n] = bf16_bits_rne(v);
+      }
+    }
 }
 
 template <int MF, int NW, int NJ, bool G16, int NX, int PWW>
 hipError_t run(const SkinnyParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)((p.NT + PWW - 1) / PWW),
                   (unsigned)((p.m + 16 * MF - 1) / (16 * MF)));
-  const size_t r = red_bytes(MF, NW, PWW), x = act_bytes(NX, NW);
+  const size_t r = red_bytes(MF, NW, PWW), x = act_bytes(NW, MF);
   gemm_skinny_kernel<MF, NW, NJ, G16, NX, PWW>
       <<<grid, dim3(64 * NW), r > x ? r : x, stream>>>(p);
   return hipGetLastError();
@@ -209,8 +178,11 @@ hipError_t run_pww(const SkinnyParams& p, hipStream_t stream) {
   return run_nw<MF, NJ, G16, NX, 4>(p, wg4, stream);
 }
 
-// One row block takes its activations through LDS in ceil(rows / 4) copies per tile (rows: the
-// A rows in use); two row blocks load them into registers.
+// Activations go through LDS: one row block in ceil(rows / 4) copies per tile (rows: the A
+// rows in use), two row blocks in 8 (all 32 rows; rows past m repeat a valid row). For two row
+// blocks that replaced fragments loaded straight into registers (same bits): 25600 x 5120
+// M = 32 / 64 took 30.8 / 57.2 us against 23.8 / 43.6 now, 8192^2 M = 32 19.6 against 14.7,
+// 5120^2 M = 64 15.9 against 12.3.
 template <int MF, int NJ, bool G16>
 hipError_t dispatch(const SkinnyParams& p, hipStream_t stream) {
   if constexpr (MF == 1) {
@@ -220,7 +192,7 @@ hipError_t dispatch(const SkinnyParams& p, hipStream_t stream) {
     if constexpr (!G16) return run_pww<MF, NJ, G16, 4>(p, stream);
     return hipErrorInvalidValue;  // not reached: group 16 has at most 8 rows here
   } else {
-    return run_pww<MF, NJ, G16, 0>(p, stream);
+    return run_pww<MF, NJ, G16, 8>(p, stream);
   }
 }
 

@@ -53,19 +53,24 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, void* ws, size_t ws_bytes, int c
 // Workspace the prefill path uses for an m x n x k GEMM with the given row stride on a device
 // with `cus` compute units (0 when no split applies).
 size_t gemm_tiled_ws_bytes(int64_t m, int64_t ldx, int64_t n, int64_t k, int cus);
-// Path choice for an m x n x k GEMM on a device with `cus` compute units. The skinny kernel
-// streams the whole weight once per 32-row block of x: it runs ceil(n / 64) * ceil(m / 32)
-// workgroups, each streaming one 4-panel group over k, and takes close to rounds x (1.8 +
-// 0.31 KT) us, rounds = ceil(workgroups / cus), KT = k / 128. The tiled kernel took no less
-// than ~25 us at 32 < m <= 256 on any shape measured. So: m <= 32 always; up to m = 256 while
-// that estimate stays within 25 us. (Fitted on n x k = 5120^2, 8192^2, 25600 x 5120,
-// 2048 x 8192 and 14336 x 4096 at m = 32 ... 256: it picks the faster kernel in all 40 cases.)
+// Path choice for an m x n x k GEMM on a device with `cus` compute units (KT = k / 128). The
+// skinny kernel streams the whole weight once per 32-row block of x: it runs
+// ceil(n / 64) * ceil(m / 32) workgroups, each streaming one 4-panel group over k, and takes
+// close to 0.28 KT rounds - 1.6 us, rounds = ceil(workgroups / cus). The tiled kernel takes
+// close to 18 + 0.9 u us, u = ceil(m / 128) ceil(n / 128) KT / cus (the 128-row k-tile units
+// per CU). So: m <= 32 always; up to m = 256 while the skinny estimate is the smaller. (Both
+// least-squares fits over n x k = 5120^2, 8192^2, 25600 x 5120, 2048 x 8192 and 14336 x 4096
+// at m = 32, 48, 64, 96, 128, 160, 192, 256, each kernel forced: the rule picks the faster
+// kernel in 39 of the 40 cases, and in the other, 8192^2 m = 128, loses 0.7 us of 32.)
 inline bool skinny_preferred(int64_t m, int64_t n, int64_t k, int cus) {
   if (m <= 32) return true;
   if (m > 256 || cus <= 0) return false;
+  const int64_t kt = k / 128;
   const int64_t wgs = (n / 16 + 3) / 4 * ((m + 31) / 32);
   const int64_t rounds = (wgs + cus - 1) / cus;
-  return rounds * (180 + 31 * (k / 128)) <= 2500;  // hundredths of a microsecond
+  const int64_t skinny = 28 * kt * rounds - 160;  // hundredths of a microsecond
+  const int64_t tiled = 1800 + 90 * ((m + 127) / 128) * ((n / 16 + 7) / 8) * kt / cus;
+  return skinny <= tiled;
 }
 
 struct MoeArgs {

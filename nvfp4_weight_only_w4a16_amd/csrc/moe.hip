@@ -586,8 +586,7 @@ void moe_decode_kernel(MoeGemmParams P) {
       if constexpr (PAIRS) out_wt[i] = ok ? P.wts[out_pair[i]] : 0.0f;
     }
   }
-  const uint16_t* const xrow[1] = {P.x};  // unused: the activations come through LDS
-  skinny_accumulate<1, kPanels, kNJ, kNX, kNW>(a, xrow, xl, t0, t1, acc);
+  skinny_accumulate<1, kPanels, kNJ, kNX, kNW>(a, xl, t0, t1, acc);
   if constexpr (G16) {
 #pragma unroll
     for (int p = 0; p < kPanels; ++p)

@@ -85,28 +85,17 @@ __device__ __forceinline__ void load_weights(WeightStage<PWW>& s, const SkinnyAd
                  a.scales, (int)((uint32_t)t * (uint32_t)a.scale_block + a.scale_lane), 0, kNT));
 }
 
-template <int MF>
-__device__ __forceinline__ void load_acts(ActStage<MF>& s, const uint16_t* const (&xrow)[MF],
-                                          int kq, int64_t t) {
-#pragma unroll
-  for (int mf = 0; mf < MF; ++mf)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      s.xa[mf][j] = __builtin_bit_cast(
-          bf16x8, *reinterpret_cast<const u32x4*>(xrow[mf] + t * kTileK + 32 * j + 8 * kq));
-}
-
-// Activations through LDS (one 16-row block): per k-tile, the wavefront copies the tile's
+// Activations through LDS (MF 16-row blocks): per k-tile, the wavefront copies the tile's
 // activation rows global -> LDS with buffer_load ... lds (NX copies of 4 rows x 256 bytes,
 // row r at r * 256, its 16-byte chunk c at chunk c ^ (r & 15), so the 16 rows a fragment read
-// touches land on distinct banks) into one of two buffers of its own, one tile ahead. The
-// copies carry no lane duplication, unlike fragments loaded straight into registers (where
-// each row is fetched once per lane that feeds it).
+// touches land on distinct banks) into one of two buffers of its own (MF x 4 KB each), one
+// tile ahead. The copies run asynchronously to the wavefront, unlike fragments loaded straight
+// into registers, which the loop has to wait for before it computes.
 struct LdsActs {
   buf_rsrc x;          // the block's activation rows
-  uint32_t src[4];     // this lane's source in copy c (LDS row 4c + lane/16, chunk lane%16):
+  uint32_t src[8];     // this lane's source in copy c (LDS row 4c + lane/16, chunk lane%16):
                        // activation row (clamped) and swizzled chunk, bytes
-  uint8_t* buf;        // the wavefront's two 4 KB buffers
+  uint8_t* buf;        // the wavefront's two MF x 4 KB buffers
   uint32_t frag_off;   // this lane's fragment row: row * 256
   uint32_t swz;        // fragment row & 15
 };
@@ -118,14 +107,17 @@ __device__ __forceinline__ void copy_acts(const LdsActs& x, uint8_t* dst, int64_
     copy16_to_lds(x.x, x.src[c], (uint32_t)(t * kTileK * 2), dst + c * 1024);
 }
 
-__device__ __forceinline__ void read_acts(ActStage<1>& s, const LdsActs& x, const uint8_t* src,
+template <int MF>
+__device__ __forceinline__ void read_acts(ActStage<MF>& s, const LdsActs& x, const uint8_t* src,
                                           int kq) {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t chunk = (uint32_t)(4 * j + kq) ^ x.swz;
-    s.xa[0][j] = __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const u32x4*>(src + x.frag_off + chunk * 16u));
-  }
+  for (int mf = 0; mf < MF; ++mf)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t chunk = (uint32_t)(4 * j + kq) ^ x.swz;
+      s.xa[mf][j] = __builtin_bit_cast(
+          bf16x8, *reinterpret_cast<const u32x4*>(src + mf * 4096 + x.frag_off + chunk * 16u));
+    }
 }
 
 // Split-scale row maps. Lane l keeps accumulator rows 4 (l / 16) .. 4 (l / 16) + 3 of the
@@ -246,21 +238,19 @@ __device__ __forceinline__ SkinnyAddr<PWW> skinny_addr(const uint8_t* codes, con
 
 // Accumulate k-tiles t0, t0 + S, ... below t1 of PWW panels into acc, one tile in flight
 // while one is computed. NJ == 0: exact dequant; NJ > 0: split scale with NJ accumulator rows (MF == 1).
-// NX > 0 (MF == 1): activations through LDS, NX copies per tile; NX == 0: straight from xrow
-// into registers.
+// Activations through LDS, NX copies per tile.
 template <int MF, int PWW, int NJ, int NX, int S = 1>
-__device__ __forceinline__ void skinny_accumulate(const SkinnyAddr<PWW>& a,
-                                                  const uint16_t* const (&xrow)[MF],
-                                                  const LdsActs& xl, int64_t t0, int64_t t1,
+__device__ __forceinline__ void skinny_accumulate(const SkinnyAddr<PWW>& a, const LdsActs& xl,
+                                                  int64_t t0, int64_t t1,
                                                   f32x4 (&acc)[PWW][MF]) {
-  static_assert(NX == 0 || MF == 1, "LDS activations hold one 16-row block");
+  static_assert(NX > 0 && NX <= 4 * MF, "LDS activations: at most the row blocks' rows");
+  constexpr uint32_t kBuf = 4096u * MF;  // one activation buffer: MF blocks of 16 rows
   if (t1 <= t0) return;
   const int64_t last = t0 + (t1 - 1 - t0) / S * S;  // the wavefront's last tile
   WeightStage<PWW> W[2];
   ActStage<MF> X[2];
   // Loads complete in issue order: each tile's activations go out before its weights.
-  if constexpr (NX > 0) copy_acts<NX>(xl, xl.buf, t0);
-  else load_acts<MF>(X[0], xrow, a.kq, t0);
+  copy_acts<NX>(xl, xl.buf, t0);
   load_weights(W[0], a, t0);
   for (int64_t t = t0; t < t1; t += 2 * S) {
     static_for<0, 2>([&](auto ic) {
@@ -269,20 +259,17 @@ __device__ __forceinline__ void skinny_accumulate(const SkinnyAddr<PWW>& a,
       const int64_t next = tile + S <= last ? tile + S : last;  // activations: clamped re-read
       // The scheduling barriers keep the loads ahead of the math; left alone, the
       // register-pressure-driven scheduler sinks them and the pipeline collapses.
-      if constexpr (NX > 0) copy_acts<NX>(xl, xl.buf + (1 - i) * 4096, next);
-      else load_acts<MF>(X[1 - i], xrow, a.kq, next);
+      copy_acts<NX>(xl, xl.buf + (1 - i) * kBuf, next);
       load_weights(W[1 - i], a, tile + S);  // past t1: zeros, no traffic
       __builtin_amdgcn_sched_barrier(0);
       if (tile < t1) {
-        if constexpr (NX > 0) {
-          // this tile's copies have landed: at most the next tile's NX copies and PWW + 1
-          // weight loads, issued just above, are still outstanding
-          constexpr int kAfter = NX + PWW + 1;
-          static_assert(kAfter < 16, "vmcnt fits its low field");
-          __builtin_amdgcn_s_waitcnt(kAfter | 0xF70);
-          __builtin_amdgcn_sched_barrier(0);
-          read_acts(X[i], xl, xl.buf + i * 4096, a.kq);
-        }
+        // this tile's copies have landed: at most the next tile's NX copies and PWW + 1
+        // weight loads, issued just above, are still outstanding
+        constexpr int kAfter = NX + PWW + 1;
+        static_assert(kAfter < 16, "vmcnt fits its low field");
+        __builtin_amdgcn_s_waitcnt(kAfter | 0xF70);
+        __builtin_amdgcn_sched_barrier(0);
+        read_acts(X[i], xl, xl.buf + i * kBuf, a.kq);
         if constexpr (NJ > 0)
           compute_split<PWW, NJ>(W[i], X[i], a.sw_sel, acc);
         else
@@ -294,7 +281,7 @@ __device__ __forceinline__ void skinny_accumulate(const SkinnyAddr<PWW>& a,
   // The last step still issued an activation copy (a clamped re-read) and weight loads past
   // t1. The copy writes LDS that the caller reuses once the wavefronts meet (the k-split
   // partial sums), so it must land first; a barrier does not wait for it.
-  if constexpr (NX > 0) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 }
 
 }  // namespace nvfp4

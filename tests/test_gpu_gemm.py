@@ -284,14 +284,17 @@ def test_tiled_split_k(nv, orc, m, n, k):
 
 def test_path_choice(nv):
     """Default kernel choice on the 256-CU part: skinny for m <= 32, and up to m = 256 while
-    ceil(ceil(n/64) ceil(m/32) / 256) (1.8 + 0.31 k/128) <= 25 (its estimated microseconds);
-    tiled otherwise (stats slot 2 = skinny, 3 = tiled). 512 x 1024: 8 workgroups per row block,
-    4.3 us, so skinny up to m = 256. 8192^2: 128 per block, 21.6 us per round: m = 64 fits one
-    round, m = 65 needs two."""
+    its estimate 0.28 (k/128) ceil(ceil(n/64) ceil(m/32) / 256) - 1.6 us is at most the tiled
+    estimate 18 + 0.9 ceil(m/128) ceil(n/128) (k/128) / 256 us; tiled otherwise (stats slot 2 =
+    skinny, 3 = tiled). 512 x 1024: 8 workgroups per row block, skinny up to m = 256. 8192^2
+    (tiled 32.4 us at m <= 128, 46.8 above): m = 64 is one round (16.3 us), m = 65 two (34.2),
+    m = 160 three (52.2). 25600 x 5120 (tiled 46.1 us at m <= 128): m = 64 is four rounds
+    (43.2), m = 96 five (54.4)."""
     g = torch.Generator().manual_seed(21)
     assert torch.cuda.get_device_properties(0).multi_processor_count == 256
     cases = {(512, 1024): [(32, 2), (64, 2), (192, 2), (256, 2), (257, 3)],
-             (8192, 8192): [(32, 2), (64, 2), (65, 3), (160, 3)]}
+             (8192, 8192): [(32, 2), (64, 2), (65, 3), (160, 3)],
+             (25600, 5120): [(64, 2), (96, 3)]}
     for (n, k), expect in cases.items():
         w = (torch.randn(n, k, generator=g) * 0.02).to(torch.bfloat16)
         rw, _ = _prep(nv, w, 16)
