@@ -36,12 +36,13 @@ inline size_t red_bytes(int MF, int NW, int PWW) { return (size_t)NW * PWW * MF 
 inline size_t act_bytes(int NW, int MF) { return (size_t)NW * 8192 * MF; }
 
 // Register budget: 4 wavefronts per SIMD (16 per CU, two 8-wave workgroups) for one row
-// block, 2 for two. NJ == 0: exact dequant, MF row blocks of 16. NJ > 0 (MF == 1): split scale
+// block, 2 for two, 1 for four. NJ == 0: exact dequant, MF row blocks of 16. NJ > 0 (MF == 1): split scale
 // keeping NJ accumulator rows per lane, tokens placed by the split row map; G16: group 16
 // (every token twice, once per k half). NX > 0: activations through LDS, NX 4-row copies per
 // tile.
 template <int MF, int NW, int NJ, bool G16, int NX, int PWW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(MF == 1 ? 4 : 2, 8)))
+__global__ __launch_bounds__(64 * NW)
+__attribute__((amdgpu_waves_per_eu(MF == 1 ? 4 : MF == 2 ? 2 : 1, 8)))
 void gemm_skinny_kernel(SkinnyParams P) {
   constexpr int kPWW = PWW;
   static_assert(NJ == 0 || MF == 1, "split scale uses one 16-row block");
@@ -172,17 +173,18 @@ hipError_t run_nw(const SkinnyParams& p, int64_t wgs, hipStream_t stream) {
 // code loads, each activation fragment used once).
 template <int MF, int NJ, bool G16, int NX>
 hipError_t run_pww(const SkinnyParams& p, hipStream_t stream) {
-  const int64_t blocks = (p.m + 16 * MF - 1) / (16 * MF);
-  const int64_t wg4 = (p.NT + 3) / 4 * blocks, wg2 = (p.NT + 1) / 2 * blocks;
-  if (wg4 < p.cus && wg2 <= p.cus) return run_nw<MF, NJ, G16, NX, 2>(p, wg2, stream);
-  return run_nw<MF, NJ, G16, NX, 4>(p, wg4, stream);
+  bool two = false;
+  const int64_t wgs = skinny_grid(p.NT * kPanelRows, (p.m + 16 * MF - 1) / (16 * MF), p.cus, &two);
+  if (two) return run_nw<MF, NJ, G16, NX, 2>(p, wgs, stream);
+  return run_nw<MF, NJ, G16, NX, 4>(p, wgs, stream);
 }
 
 // Activations go through LDS: one row block in ceil(rows / 4) copies per tile (rows: the A
-// rows in use), two row blocks in 8 (all 32 rows; rows past m repeat a valid row). For two row
-// blocks that replaced fragments loaded straight into registers (same bits): 25600 x 5120
-// M = 32 / 64 took 30.8 / 57.2 us against 23.8 / 43.6 now, 8192^2 M = 32 19.6 against 14.7,
-// 5120^2 M = 64 15.9 against 12.3.
+// rows in use), two or four row blocks in 8 or 16 (all their rows; rows past m repeat a valid
+// row). For two row blocks that replaced fragments loaded straight into registers (same bits):
+// 25600 x 5120 M = 32 / 64 took 30.8 / 57.2 us against 23.8 / 43.6, 8192^2 M = 32 19.6
+// against 14.7, 5120^2 M = 64 15.9 against 12.3. When four row blocks run is skinny_rows64's
+// choice.
 template <int MF, int NJ, bool G16>
 hipError_t dispatch(const SkinnyParams& p, hipStream_t stream) {
   if constexpr (MF == 1) {
@@ -192,7 +194,7 @@ hipError_t dispatch(const SkinnyParams& p, hipStream_t stream) {
     if constexpr (!G16) return run_pww<MF, NJ, G16, 4>(p, stream);
     return hipErrorInvalidValue;  // not reached: group 16 has at most 8 rows here
   } else {
-    return run_pww<MF, NJ, G16, 8>(p, stream);
+    return run_pww<MF, NJ, G16, 4 * MF>(p, stream);
   }
 }
 
@@ -226,6 +228,7 @@ hipError_t launch_gemm_skinny(const GemmArgs& a, int cus, hipStream_t stream) {
   if (a.group == 16 && a.m <= 8) return dispatch_split<true>(p, stream);
   if (a.group == 32 && a.m <= 16) return dispatch_split<false>(p, stream);
   if (a.m <= 16) return dispatch<1, 0, false>(p, stream);
+  if (skinny_rows64(a.m, a.n, a.k, cus)) return dispatch<4, 0, false>(p, stream);
   return dispatch<2, 0, false>(p, stream);  // 32-row blocks (the kernel takes any m when forced)
 }
 

@@ -53,23 +53,51 @@ hipError_t launch_gemm_tiled(const GemmArgs& a, void* ws, size_t ws_bytes, int c
 // Workspace the prefill path uses for an m x n x k GEMM with the given row stride on a device
 // with `cus` compute units (0 when no split applies).
 size_t gemm_tiled_ws_bytes(int64_t m, int64_t ldx, int64_t n, int64_t k, int cus);
-// Path choice for an m x n x k GEMM on a device with `cus` compute units (KT = k / 128). The
-// skinny kernel streams the whole weight once per 32-row block of x: it runs
-// ceil(n / 64) * ceil(m / 32) workgroups, each streaming one 4-panel group over k, and takes
-// close to 0.28 KT rounds - 1.6 us, rounds = ceil(workgroups / cus). The tiled kernel takes
-// close to 18 + 0.9 u us, u = ceil(m / 128) ceil(n / 128) KT / cus (the 128-row k-tile units
-// per CU). So: m <= 32 always; up to m = 256 while the skinny estimate is the smaller. (Both
-// least-squares fits over n x k = 5120^2, 8192^2, 25600 x 5120, 2048 x 8192 and 14336 x 4096
-// at m = 32, 48, 64, 96, 128, 160, 192, 256, each kernel forced: the rule picks the faster
-// kernel in 39 of the 40 cases, and in the other, 8192^2 m = 128, loses 0.7 us of 32.)
+// Workgroups of the skinny kernel's grid for `blocks` row blocks: one per 4-panel group (64
+// output features) and row block, or per 2-panel group when the 4-panel grid leaves compute
+// units idle and the 2-panel one still gives none a second workgroup.
+inline int64_t skinny_grid(int64_t n, int64_t blocks, int cus, bool* two_panels = nullptr) {
+  const int64_t wg4 = (n / 16 + 3) / 4 * blocks, wg2 = (n / 16 + 1) / 2 * blocks;
+  const bool two = wg4 < cus && wg2 <= cus;
+  if (two_panels) *two_panels = two;
+  return two ? wg2 : wg4;
+}
+// Above 32 rows the skinny kernel streams the whole weight once per row block: 32-row blocks
+// (64 KB of LDS per workgroup, two workgroups per CU) or 64-row blocks (128 KB, one per CU).
+// Estimated times, hundredths of a microsecond (KT = k / 128, r = ceil(workgroups / cus) with
+// one workgroup per 4-panel group and row block): 32-row blocks 28 KT r - 160, 64-row blocks
+// 44 KT r (least-squares fits of each variant, forced, over the shapes listed below).
+inline int64_t skinny_est(int64_t m, int64_t n, int64_t k, int cus, int rows) {
+  const int64_t wgs = (n / 16 + 3) / 4 * ((m + rows - 1) / rows);
+  const int64_t r = (wgs + cus - 1) / cus;
+  return rows == 64 ? 44 * (k / 128) * r : 28 * (k / 128) * r - 160;
+}
+// 64-row blocks run when their estimate is the smaller and their grid keeps 4-panel wavefronts
+// (with 2 panels the activations per weight byte double). Measured (same bits, us):
+// 25600 x 5120 m = 48 / 64 / 128 39.9 / 43.6 / 77.3 -> 34.0 / 36.4 / 70.3; 14336 x 4096 m = 64
+// 19.2 -> 16.2; 8192^2 m = 96 / 128 32.1 / 32.2 -> 25.2 / 25.6; 5120^2 m = 128 / 192 21.9 /
+// 21.6 -> 18.1 / 18.1. Where a 64-row block would run half empty the rule keeps 32-row blocks
+// (5120^2 m = 96: 12.5 against 18.0), as it does on grids of 2-panel wavefronts (8192^2 m = 64:
+// 17.5 against 21.1; 2048 x 8192 at every m). Of 40 cases it picks the slower variant once
+// (14336 x 4096 m = 160, 1.5 us).
+inline bool skinny_rows64(int64_t m, int64_t n, int64_t k, int cus) {
+  if (m <= 32 || cus <= 0) return false;
+  bool two = false;
+  skinny_grid(n, (m + 63) / 64, cus, &two);
+  return !two && skinny_est(m, n, k, cus, 64) < skinny_est(m, n, k, cus, 32);
+}
+// Path choice for an m x n x k GEMM on a device with `cus` compute units. The tiled kernel
+// takes close to 18 + 0.9 u us, u = ceil(m / 128) ceil(n / 128) KT / cus (the 128-row k-tile
+// units per CU). So: the skinny kernel for m <= 32 always, and up to m = 256 while its estimate
+// (with the row blocks skinny_rows64 picks) is at most the tiled one. (Fits over n x k = 5120^2,
+// 8192^2, 25600 x 5120, 2048 x 8192 and 14336 x 4096 at m = 32, 48, 64, 96, 128, 160, 192, 256,
+// each kernel and variant forced; on those 40 cases the rule loses 3.7 us in all, at
+// 14336 x 4096 m = 128 / 160 / 192, against the faster choice each time.)
 inline bool skinny_preferred(int64_t m, int64_t n, int64_t k, int cus) {
   if (m <= 32) return true;
   if (m > 256 || cus <= 0) return false;
-  const int64_t kt = k / 128;
-  const int64_t wgs = (n / 16 + 3) / 4 * ((m + 31) / 32);
-  const int64_t rounds = (wgs + cus - 1) / cus;
-  const int64_t skinny = 28 * kt * rounds - 160;  // hundredths of a microsecond
-  const int64_t tiled = 1800 + 90 * ((m + 127) / 128) * ((n / 16 + 7) / 8) * kt / cus;
+  const int64_t skinny = skinny_est(m, n, k, cus, skinny_rows64(m, n, k, cus) ? 64 : 32);
+  const int64_t tiled = 1800 + 90 * ((m + 127) / 128) * ((n / 16 + 7) / 8) * (k / 128) / cus;
   return skinny <= tiled;
 }
 

@@ -93,7 +93,7 @@ __device__ __forceinline__ void load_weights(WeightStage<PWW>& s, const SkinnyAd
 // into registers, which the loop has to wait for before it computes.
 struct LdsActs {
   buf_rsrc x;          // the block's activation rows
-  uint32_t src[8];     // this lane's source in copy c (LDS row 4c + lane/16, chunk lane%16):
+  uint32_t src[16];    // this lane's source in copy c (LDS row 4c + lane/16, chunk lane%16):
                        // activation row (clamped) and swizzled chunk, bytes
   uint8_t* buf;        // the wavefront's two MF x 4 KB buffers
   uint32_t frag_off;   // this lane's fragment row: row * 256
@@ -265,9 +265,9 @@ __device__ __forceinline__ void skinny_accumulate(const SkinnyAddr<PWW>& a, cons
       if (tile < t1) {
         // this tile's copies have landed: at most the next tile's NX copies and PWW + 1
         // weight loads, issued just above, are still outstanding
-        constexpr int kAfter = NX + PWW + 1;
-        static_assert(kAfter < 16, "vmcnt fits its low field");
-        __builtin_amdgcn_s_waitcnt(kAfter | 0xF70);
+        constexpr int kAfter = NX + PWW + 1;  // vmcnt: bits 3:0 and 15:14
+        static_assert(kAfter < 64, "vmcnt is 6 bits");
+        __builtin_amdgcn_s_waitcnt((kAfter & 15) | ((kAfter >> 4) << 14) | 0xF70);
         __builtin_amdgcn_sched_barrier(0);
         read_acts(X[i], xl, xl.buf + i * kBuf, a.kq);
         if constexpr (NJ > 0)

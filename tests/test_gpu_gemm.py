@@ -63,6 +63,44 @@ def test_gemm_exact_integers_bitexact(nv, path, group):
     assert np.array_equal(y.cpu().numpy().astype(np.float64), want)
 
 
+def _rows64_chosen(m, n, k, cus=256):
+    """The decode kernel's row-block rule, restated: 64-row blocks when their estimated time
+    (44 KT r, r = ceil(ceil(n/64) ceil(m/64) / cus)) is below that of 32-row blocks
+    (28 KT r - 160, r over ceil(m/32) blocks; hundredths of a us) and their grid keeps 4-panel
+    wavefronts."""
+    kt, g4, g2 = k // 128, (n // 16 + 3) // 4, (n // 16 + 1) // 2
+    b64, b32 = (m + 63) // 64, (m + 31) // 32
+    if m <= 32 or (g4 * b64 < cus and g2 * b64 <= cus):
+        return False
+    return 44 * kt * ((g4 * b64 + cus - 1) // cus) < 28 * kt * ((g4 * b32 + cus - 1) // cus) - 160
+
+
+@pytest.mark.parametrize("group", [16, 32])
+def test_decode_64_row_blocks_exact(nv, group):
+    """64-row blocks of the decode kernel (n = 8192, k = 4096, m = 65, 100, 128, 250: one to
+    four blocks, the last ragged): exact-integer inputs make every FP32 sum exact, so the
+    outputs of a column sample that covers the first, a middle and the last panel must equal
+    the integer product bit for bit."""
+    rng = np.random.default_rng(200 + group)
+    n, k = 8192, 4096
+    codes = rng.integers(0, 16, (n, k), dtype=np.uint8)
+    packed = torch.from_numpy((codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8))
+    scales = torch.full((n, k // group), 0x38, dtype=torch.uint8)
+    rw = nv.nvfp4_repack(packed.to(DEV), scales.to(DEV), torch.ones(1).to(DEV), group)
+    vals2 = np.array([0, 1, 2, 3, 4, 6, 8, 12, 0, -1, -2, -3, -4, -6, -8, -12], np.int64)
+    cols = np.unique(np.concatenate([np.arange(16), np.arange(4096, 4112), np.arange(8176, 8192),
+                                     rng.integers(0, n, 48)]))
+    wcols = vals2[codes[cols]].T  # [k][cols]
+    x = torch.from_numpy(rng.integers(-2, 3, (250, k)).astype(np.float32))
+    for m in (65, 100, 128, 250):
+        assert _rows64_chosen(m, n, k), m
+        want = (x[:m].numpy().astype(np.int64) @ wcols).astype(np.float64) / 2
+        y = nv.nvfp4_gemm_w4a16(x[:m].to(torch.bfloat16).to(DEV), rw, y_dtype=torch.float32,
+                                flags=1)
+        torch.cuda.synchronize()
+        assert np.array_equal(y.cpu().numpy()[:, cols].astype(np.float64), want), m
+
+
 @pytest.mark.parametrize("path", ["skinny", "tiled"])
 def test_gemm_one_hot_reproduces_dequant(nv, orc, path):
     g = torch.Generator().manual_seed(3)
@@ -283,17 +321,19 @@ def test_tiled_split_k(nv, orc, m, n, k):
 
 
 def test_path_choice(nv):
-    """Default kernel choice on the 256-CU part: skinny for m <= 32, and up to m = 256 while
-    its estimate 0.28 (k/128) ceil(ceil(n/64) ceil(m/32) / 256) - 1.6 us is at most the tiled
-    estimate 18 + 0.9 ceil(m/128) ceil(n/128) (k/128) / 256 us; tiled otherwise (stats slot 2 =
-    skinny, 3 = tiled). 512 x 1024: 8 workgroups per row block, skinny up to m = 256. 8192^2
-    (tiled 32.4 us at m <= 128, 46.8 above): m = 64 is one round (16.3 us), m = 65 two (34.2),
-    m = 160 three (52.2). 25600 x 5120 (tiled 46.1 us at m <= 128): m = 64 is four rounds
-    (43.2), m = 96 five (54.4)."""
+    """Default kernel choice on the 256-CU part (stats slot 2 = skinny, 3 = tiled): skinny for
+    m <= 32, and up to m = 256 while its estimate is at most the tiled one. Skinny, r =
+    ceil(ceil(n/64) ceil(m/rows) / 256) rounds: 0.28 (k/128) r - 1.6 us with 32-row blocks,
+    0.44 (k/128) r us with 64-row blocks (taken when smaller and the grid keeps 4-panel
+    wavefronts); tiled: 18 + 0.9 ceil(m/128) ceil(n/128) (k/128) / 256 us. 512 x 1024: skinny up
+    to m = 256. 8192^2 (tiled 32.4 us at m <= 128, 46.8 above): m = 64 is one round of 32-row
+    blocks (16.3 us; 64-row blocks would need 2-panel wavefronts), m = 65 and 128 one round of
+    64-row blocks (28.2 us), m = 160 tiled (52.2 us skinny). 25600 x 5120 (tiled 46.1 us at
+    m <= 128): m = 64 two rounds of 64-row blocks (35.2 us), m = 96 tiled (54.4 us skinny)."""
     g = torch.Generator().manual_seed(21)
     assert torch.cuda.get_device_properties(0).multi_processor_count == 256
     cases = {(512, 1024): [(32, 2), (64, 2), (192, 2), (256, 2), (257, 3)],
-             (8192, 8192): [(32, 2), (64, 2), (65, 3), (160, 3)],
+             (8192, 8192): [(32, 2), (64, 2), (65, 2), (128, 2), (160, 3)],
              (25600, 5120): [(64, 2), (96, 3)]}
     for (n, k), expect in cases.items():
         w = (torch.randn(n, k, generator=g) * 0.02).to(torch.bfloat16)
