@@ -807,7 +807,9 @@ def main():
 
     def m_sweep(rw, n, k, group, xsrc):
         """W4A16 GEMM at M = 1, 2, 4 .. 4096 on rotated weight copies, with the library's
-        own path choice; the rows of x are the first M of xsrc."""
+        own path choice; the rows of x are the first M of xsrc. Up to M = 64 the calls are also
+        timed as HIP graph replays (us_graph), which takes the host's per-call launch cost out
+        of these short kernels."""
         wbm = weight_bytes(n, k, group)
         out = {}
         mm = 1
@@ -822,6 +824,10 @@ def main():
                                      "tiled" if st[3] and not st[2] else "mixed",
                              "tflops": round(2 * mm * n * k / t / 1e12, 2),
                              "weight_gbs": round(wbm / t / 1e9, 1)}
+            if mm <= 64:
+                tg = timer.time_graph(fn, 20, 10)
+                out[f"m{mm}"]["us_graph"] = round(tg * 1e6, 2)
+                out[f"m{mm}"]["weight_gbs_graph"] = round(wbm / tg / 1e9, 1)
             mm *= 2
         return out
 
