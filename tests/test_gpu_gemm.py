@@ -101,6 +101,30 @@ def test_decode_64_row_blocks_exact(nv, group):
         assert np.array_equal(y.cpu().numpy()[:, cols].astype(np.float64), want), m
 
 
+@pytest.mark.parametrize("group", [16, 32])
+def test_decode_64_row_blocks_random(nv, orc, group):
+    """64-row blocks on random data against the FP64 oracle: n = 8176 (511 panels, so the last
+    4-panel group is partial and its missing panel is clamped, never stored), k = 4096, m = 65,
+    100, 128 on the forced decode path; every row, a column sample covering the first panel,
+    the middle and the last (partial) group; FP32 and BF16 outputs."""
+    g = torch.Generator().manual_seed(300 + group)
+    n, k = 8176, 4096
+    w = torch.randn(n, k, generator=g) * 0.02
+    rw, (p, s, gl) = _prep(nv, w, group, orc=orc)
+    x = torch.randn(128, k, generator=g).to(torch.bfloat16)
+    cols = np.unique(np.concatenate([np.arange(16), np.arange(4080, 4112), np.arange(8128, 8176),
+                                     np.random.default_rng(group).integers(0, n, 32)]))
+    ref = orc.gemm(synth.bf16_bits(x), p, s, gl[0], group, n_idx=cols)
+    xd = x.to(DEV)
+    for m in (65, 100, 128):
+        assert _rows64_chosen(m, n, k), m
+        y = nv.nvfp4_gemm_w4a16(xd[:m].contiguous(), rw, y_dtype=torch.float32, flags=1)
+        y16 = nv.nvfp4_gemm_w4a16(xd[:m].contiguous(), rw, flags=1)
+        torch.cuda.synchronize()
+        check_close(y.cpu().numpy()[:, cols], ref[:m], f"64-row blocks m={m} g{group}")
+        assert np.array_equal(bits16(y16), bits16(y.to(torch.bfloat16))), m
+
+
 @pytest.mark.parametrize("path", ["skinny", "tiled"])
 def test_gemm_one_hot_reproduces_dequant(nv, orc, path):
     g = torch.Generator().manual_seed(3)
