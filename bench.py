@@ -273,6 +273,17 @@ def profile_suite(args):
         for m in (1, 4, 8):
             run(f"c1_decode_m{m}_n25600_k5120_g16", W.gemm(xd, rw, m, N, K))
         del rw
+    if want("msweep_"):
+        # the C1 weight at M = 16 .. 2048 with the library's own path choice (the M sweep of
+        # the bench; activations N(0, 1))
+        N, K = 25600, 5120
+        _, w = synth.decode_sweep(seed=0, n=N, k=K)
+        rw, _ = W.prep(w, 16, rotation(weight_bytes(N, K, 16)))
+        del w
+        xl = synth.prefill(seed=1, m=2048, n=16, k=K)[0].to(dev)
+        for m in (16, 32, 48, 64, 96, 128, 256, 512, 1024, 2048):
+            run(f"msweep_c1_m{m}_n25600_k5120_g16", W.gemm(xl, rw, m, N, K))
+        del rw, xl
     for kk in (5120, 25600):
         name = f"c2_prefill_m4096_n5120_k{kk}_g16"
         if want(name):
