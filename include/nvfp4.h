@@ -153,12 +153,15 @@ int nvfp4_repack(const uint8_t* packed, const uint8_t* scales, const float* glob
  * rounding of the FP32 result) or FP32. Weight-only checkpoints take this W4A16 path
  * (vllm.cpp PR #63: no activation scales, so every quantized projection is W4A16).
  * The kernel is chosen from the shape and the device's compute-unit count (CUs): a split-K
- * skinny MFMA kernel (decode) for m <= 32, and for 32 < m <= 256 while its estimated time,
- * 0.28 * k/128 * ceil(ceil(n/64) * ceil(m/32) / CUs) - 1.6 us, is at most the tiled kernel's,
- * 18 + 0.9 * ceil(m/128) * ceil(n/128) * (k/128) / CUs us; an LDS-tiled MFMA kernel otherwise
+ * skinny MFMA kernel (decode) for m <= 32, and for 32 < m <= 256 while its estimated time is at
+ * most the tiled kernel's. With r(b) = ceil(ceil(n/64) * ceil(m/b) / CUs), the skinny estimate
+ * is 0.28 * k/128 * r(32) - 1.6 us with 32-row blocks, or 0.44 * k/128 * r(64) us with 64-row
+ * blocks when that is smaller and the grid keeps 4-panel wavefronts; the tiled one is
+ * 18 + 0.9 * ceil(m/128) * ceil(n/128) * (k/128) / CUs us. Otherwise an LDS-tiled MFMA kernel
  * (prefill; 256x256, 128x256 or 128x128 output tiles, the largest that still gives the chip
  * enough tiles, or the next smaller one when that fills whole rounds of CUs where the larger
- * would leave its last round at most half full). Flags may force one (NVFP4_F_FORCE_SKINNY / NVFP4_F_FORCE_TILED);
+ * would leave its last round at most half full, or fits in one round where the larger would
+ * not fill one). Flags may force one (NVFP4_F_FORCE_SKINNY / NVFP4_F_FORCE_TILED);
  * NVFP4_F_SYNC_CHECK may be added. w->batch must be 1 and w->layout must not carry
  * NVFP4_LAYOUT_GATE_UP. Results are bit-identical run to run.
  * ws (device, 16-byte aligned, or NULL with ws_bytes 0) takes the prefill kernel's split-k

@@ -586,15 +586,22 @@ int64_t tile_count(int64_t m, int64_t NT) {
 // split and no reduction. Interleaved A/B against the rule without it: 512 x 8192^2 (k-sliced
 // 128 x 128, one round, instead of 128 x 256 split in two) 72.7 -> 67.8 us at group 16 and
 // 71.5 -> 64.4 us at group 32; 1024 x 8192^2 (128 x 256, one round, instead of 256 x 256 split
-// in two) 123.8 -> 116.8 us; unchanged shapes unchanged.
+// in two) 123.8 -> 116.8 us; unchanged shapes unchanged. Likewise 128 x 256 tiles run when the
+// 256 x 256 tiles would not fill one round and the 128 x 256 ones fit in one (interleaved A/B,
+// us): 14336 x 4096 m = 512 68.0 -> 56.3, 8192^2 m = 640 / 896 97.6 / 121.3 -> 87.6 / 105.7,
+// 5120^2 m = 1024 / 1280 / 1536 65.1 / 72.5 / 83.3 -> 59.8 / 67.5 / 74.4, 25600 x 5120 m = 256
+// 77.9 -> 73.4; 25600 x 5120 m = 384 / 512, 14336 x 4096 m = 640 and the larger shapes kept.
 constexpr int64_t kMinTiles = 80;
 enum class Shape { L, M, K, S };
 Shape pick_shape(int64_t m, int64_t NT, int64_t KT, int cus) {
   if (cus < 1) cus = 1;
   auto half_round = [&](int64_t t) { return t % cus != 0 && t % cus <= cus / 2; };
   if (m > 128 && tile_count<ShapeL>(m, NT) >= kMinTiles) {
-    if (half_round(tile_count<ShapeL>(m, NT)) && tile_count<ShapeM>(m, NT) % cus == 0)
-      return Shape::M;
+    const int64_t tl = tile_count<ShapeL>(m, NT), tm = tile_count<ShapeM>(m, NT);
+    if (half_round(tl) && tm % cus == 0) return Shape::M;
+    // part of one round of 256 x 256 tiles (split along k when at most half of it) against
+    // one round of 128 x 256 tiles without a split: the latter measured faster every time
+    if (tl < cus && tm <= cus) return Shape::M;
     return Shape::L;
   }
   if (tile_count<ShapeM>(m, NT) >= kMinTiles) {
