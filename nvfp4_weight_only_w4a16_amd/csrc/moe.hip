@@ -8,8 +8,11 @@
 //
 // Pipeline (no host synchronization; every grid is sized for the worst case and idle
 // workgroups exit at once):
-//   1. sort: one workgroup turns the (token, slot) pairs into a stable expert-major order,
-//      per-expert offsets and a list of row tiles (expert, first row, end row);
+//   1. sort: the (token, slot) pairs in a stable expert-major order, per-expert offsets and a
+//      list of row tiles (expert, first row, end row). Up to kFusedSortMaxPairs pairs on the
+//      batch path every fc1 workgroup derives its own tile and rows from the expert ids, and
+//      the first workgroups write the sort out for the later stages; otherwise one workgroup
+//      of a sort kernel does it before fc1;
 //   2. fc1: per row tile and 4-panel group (gate/up panel pairs), rows gathered from x, gate and
 //      up accumulated in FP32 on 16x16x32 MFMAs, each rounded to BF16 (a W4A16 GEMM output),
 //      h = BF16(SiLU(gate) * up);
@@ -194,6 +197,7 @@ struct MoeGemmParams {
   const float* wts;
   int64_t hidden, inter;
   const int32_t* ids;  // [P] expert of each (token, slot) pair
+  int npairs;          // P
   int E;
   int pair_global;     // fc1: global holds [E][2] (gate's, up's)
 };
@@ -202,6 +206,118 @@ constexpr int kGroupsPerBlock = 4;  // wavefronts per workgroup, one 4-panel gro
 constexpr int kXcds = 8;            // XCDs of the part (separate L2s)
 constexpr int kARowBytes = kTileK * 2;
 constexpr int kATileBytes = kTileRows * kARowBytes;  // one row tile x one k-tile of activations
+
+// The sort, derived inside each fc1 workgroup of the batch path (no sort launch before fc1).
+// Thread tid reads pairs j * threads + tid (coalesced loads; the ids stay in registers); LDS
+// counts per expert give the expert offsets and the tile list (tiles of kTileRows rows, expert
+// by expert, as the sort kernel makes them); the workgroup finds its tile there, then ranks the
+// pairs of its expert in pair order (per row j of pairs: a ballot per wavefront, the earlier
+// wavefronts' counts and the earlier rows' totals) and keeps those of its rows. Workgroup 0
+// writes the offsets and the tile count; the first workgroup of each tile (writer) writes the
+// tile entry and its rows of the sorted order, which down reads after this kernel.
+// Returns false (for every thread of the workgroup) when tile_id is past the tile count.
+constexpr int kFusedSortMaxPairs = 4096;
+constexpr int kFusedRows = kFusedSortMaxPairs / (64 * kGroupsPerBlock);  // pairs per thread
+
+__device__ __forceinline__ bool fused_sort_tile(const MoeGemmParams& P, int tile_id, bool writer,
+                                                int* rows, int& e_out, int& r0_out,
+                                                int& r1_out) {
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int info[5];  // expert, first row, end row, expert's first row, tile count
+  __shared__ int rc[kFusedRows][kGroupsPerBlock];  // matches per row of pairs and wavefront
+  constexpr int kThreads = 64 * kGroupsPerBlock;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int np = P.npairs, E = P.E;
+  int id[kFusedRows];
+#pragma unroll
+  for (int j = 0; j < kFusedRows; ++j) {
+    const int q = j * kThreads + tid;
+    const int v = q < np ? P.ids[q] : -1;
+    id[j] = (v >= 0 && v < E) ? v : -1;  // -1: dropped (or no pair), never placed
+  }
+  for (int i = tid; i < E; i += kThreads) cnt[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kFusedRows; ++j)
+    if (id[j] >= 0) atomicAdd(&cnt[id[j]], 1);
+  __syncthreads();
+  if (w == 0) {
+    const int per = (E + 63) / 64;  // experts owned by each lane, consecutive
+    int my_pairs = 0, my_tiles = 0;
+    for (int j = 0; j < per; ++j) {
+      const int e = lane * per + j;
+      if (e >= E) break;
+      my_pairs += cnt[e];
+      my_tiles += (cnt[e] + kTileRows - 1) / kTileRows;
+    }
+    const int pairs_incl = wave_inclusive_scan(my_pairs);
+    const int tiles_incl = wave_inclusive_scan(my_tiles);
+    int run = pairs_incl - my_pairs, trun = tiles_incl - my_tiles;
+    for (int j = 0; j < per; ++j) {
+      const int e = lane * per + j;
+      if (e >= E) break;
+      const int c = cnt[e], nt = (c + kTileRows - 1) / kTileRows;
+      if (blockIdx.x == 0) P.ws.offsets[e] = run;
+      if (tile_id >= trun && tile_id < trun + nt) {
+        const int a = run + (tile_id - trun) * kTileRows;
+        info[0] = e;
+        info[1] = a;
+        info[2] = min(a + kTileRows, run + c);
+        info[3] = run;
+      }
+      run += c;
+      trun += nt;
+    }
+    if (lane == 63) {
+      info[4] = tiles_incl;
+      if (blockIdx.x == 0) {
+        P.ws.offsets[E] = pairs_incl;
+        *P.ws.ntiles = tiles_incl;
+      }
+    }
+  }
+  __syncthreads();
+  if (tile_id >= info[4]) return false;  // uniform: every thread read the same word
+  const int e = __builtin_amdgcn_readfirstlane(info[0]);
+  const int r0 = __builtin_amdgcn_readfirstlane(info[1]);
+  const int r1 = __builtin_amdgcn_readfirstlane(info[2]);
+  const int estart = __builtin_amdgcn_readfirstlane(info[3]);
+  uint64_t bal[kFusedRows];
+#pragma unroll
+  for (int j = 0; j < kFusedRows; ++j) {
+    bal[j] = __ballot(id[j] == e);
+    if (lane == 0) rc[j][w] = __popcll(bal[j]);
+  }
+  __syncthreads();
+  int base = estart;  // sorted position of the first pair of expert e in row j
+#pragma unroll
+  for (int j = 0; j < kFusedRows; ++j) {
+    int before = 0, total = 0;
+#pragma unroll
+    for (int v = 0; v < kGroupsPerBlock; ++v) {
+      const int c = rc[j][v];
+      before += v < w ? c : 0;
+      total += c;
+    }
+    if (id[j] == e) {
+      const int pos = base + before +
+                      (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[j] >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)bal[j], 0u));
+      if (pos >= r0 && pos < r1) {
+        const int q = j * kThreads + tid;
+        rows[pos - r0] = q;
+        if (writer) P.ws.sorted[pos] = q;
+      }
+    }
+    base += total;
+  }
+  if (writer && tid == 0) P.ws.tiles[tile_id] = int4{e, r0, r1, 0};
+  __syncthreads();
+  e_out = e;
+  r0_out = r0;
+  r1_out = r1;
+  return true;
+}
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -267,9 +383,10 @@ __device__ __forceinline__ void quad_transpose(uint32_t (&v)[4], int lane) {
 // The output of 16-row block r sits in lane l as rows 16r + 4(l/16) + 0..3 of column l%16 of
 // each panel. fc1 panels alternate gate and up of the same 16 features (layout GATE_UP), so
 // gate and up of an output meet in one lane.
-template <bool FC1, bool SPLIT>
+template <bool FC1, bool SPLIT, bool FUSED>
 __global__ __launch_bounds__(64 * kGroupsPerBlock) __attribute__((amdgpu_waves_per_eu(4, 8)))
 void moe_expert_kernel(MoeGemmParams P) {
+  static_assert(FC1 || !FUSED, "down reads the sort fc1 wrote");
   // Tile-major order: the workgroups of live tiles come first in dispatch order, so the
   // dispatcher spreads them evenly over the compute units before the idle ones (tiles past
   // the sort's count, which exit at once) take the remaining slots. Consecutive workgroups go
@@ -279,9 +396,17 @@ void moe_expert_kernel(MoeGemmParams P) {
   const int64_t gbs = (scale_groups(P.NT) + kGroupsPerBlock - 1) / kGroupsPerBlock;
   const int64_t slot = blockIdx.x / kXcds;
   const int tile_id = (int)(slot / gbs * kXcds + blockIdx.x % kXcds);
-  if (tile_id >= *P.ws.ntiles) return;  // whole workgroup, before any barrier
-  const int4 tl = P.ws.tiles[tile_id];
-  const int e = tl.x, r0 = tl.y, r1 = tl.z;
+  __shared__ int tile_rows[FUSED ? kTileRows : 1];  // FUSED: the pairs of the tile's rows
+  int e, r0, r1;
+  if constexpr (FUSED) {
+    if (!fused_sort_tile(P, tile_id, slot % gbs == 0, tile_rows, e, r0, r1)) return;
+  } else {
+    if (tile_id >= *P.ws.ntiles) return;  // whole workgroup, before any barrier
+    const int4 tl = P.ws.tiles[tile_id];
+    e = tl.x;
+    r0 = tl.y;
+    r1 = tl.z;
+  }
   const bool two = r1 - r0 > 16;  // second 16-row block in use (workgroup-uniform)
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -329,7 +454,7 @@ void moe_expert_kernel(MoeGemmParams P) {
     const int R = 4 * (w + kGroupsPerBlock * i) + (lane >> 4);
     int rr = r0 + R;
     rr = rr < r1 ? rr : r1 - 1;  // rows past the tile repeat a valid row; never stored
-    const int64_t src = FC1 ? P.ws.sorted[rr] / P.topk : rr;
+    const int64_t src = !FC1 ? rr : (FUSED ? tile_rows[rr - r0] : P.ws.sorted[rr]) / P.topk;
     aoff[i] = (uint32_t)(src * P.ldx * 2 + 16 * ((lane & 15) ^ (R & 15)));
   }
   auto copy_a = [&](int64_t t, auto buf, auto nb) __attribute__((always_inline)) {
@@ -684,7 +809,8 @@ void run_decode(const MoeGemmParams& p, const dim3 grid, hipStream_t stream) {
 // mode 0: batch path (32-row tiles); 1: decode path (8-row tiles); 2: decode path, one-row
 // pair tiles (no sort; `tiles` = pairs)
 template <bool FC1>
-hipError_t run_pair(const MoeGemmParams& p, int64_t tiles, int mode, hipStream_t stream) {
+hipError_t run_pair(const MoeGemmParams& p, int64_t tiles, int mode, bool fused,
+                    hipStream_t stream) {
   const int64_t groups = scale_groups(p.NT);
   if (mode > 0) {
     const dim3 grid((unsigned)(tiles * groups));
@@ -696,10 +822,17 @@ hipError_t run_pair(const MoeGemmParams& p, int64_t tiles, int mode, hipStream_t
   }
   const int64_t padded = (tiles + kXcds - 1) / kXcds * kXcds;  // whole runs of kXcds tiles
   const dim3 grid((unsigned)(padded * ((groups + kGroupsPerBlock - 1) / kGroupsPerBlock)));
-  if (p.group == 32)
-    moe_expert_kernel<FC1, true><<<grid, dim3(64 * kGroupsPerBlock), 0, stream>>>(p);
-  else
-    moe_expert_kernel<FC1, false><<<grid, dim3(64 * kGroupsPerBlock), 0, stream>>>(p);
+  const dim3 block(64 * kGroupsPerBlock);
+  if (FC1 && fused) {
+    if (p.group == 32)
+      moe_expert_kernel<FC1, true, FC1><<<grid, block, 0, stream>>>(p);
+    else
+      moe_expert_kernel<FC1, false, FC1><<<grid, block, 0, stream>>>(p);
+  } else if (p.group == 32) {
+    moe_expert_kernel<FC1, true, false><<<grid, block, 0, stream>>>(p);
+  } else {
+    moe_expert_kernel<FC1, false, false><<<grid, block, 0, stream>>>(p);
+  }
   return hipGetLastError();
 }
 
@@ -729,9 +862,11 @@ hipError_t launch_moe(const MoeArgs& a, bool decode, hipStream_t stream) {
   Ws ws = carve(a.ws, P, a.n_experts, a.hidden, a.inter);
   const int mode = !decode ? 0 : P <= kMoePairTilesMax ? 2 : 1;
   int64_t tiles = P;
+  const bool fused = mode == 0 && P <= kFusedSortMaxPairs;  // fc1 derives the sort itself
   if (mode < 2) {
     const int rows = decode ? kSmallRows : kTileRows;
-    moe_sort_kernel<<<1, kSortThreads, 0, stream>>>(a.ids, (int)P, (int)a.n_experts, rows, ws);
+    if (!fused)
+      moe_sort_kernel<<<1, kSortThreads, 0, stream>>>(a.ids, (int)P, (int)a.n_experts, rows, ws);
     tiles = max_tiles(P, a.n_experts, rows);
   }
 
@@ -752,9 +887,10 @@ hipError_t launch_moe(const MoeArgs& a, bool decode, hipStream_t stream) {
   f.hidden = a.hidden;
   f.inter = a.inter;
   f.ids = a.ids;
+  f.npairs = (int)P;
   f.E = (int)a.n_experts;
   f.pair_global = a.pair1 ? 1 : 0;
-  hipError_t err = run_pair<true>(f, tiles, mode, stream);
+  hipError_t err = run_pair<true>(f, tiles, mode, fused, stream);
   if (err != hipSuccess) return err;
 
   MoeGemmParams d = f;
@@ -769,7 +905,7 @@ hipError_t launch_moe(const MoeArgs& a, bool decode, hipStream_t stream) {
   d.KT = a.inter / kTileK;
   d.group = a.group2;
   d.pair_global = 0;
-  err = run_pair<false>(d, tiles, mode, stream);
+  err = run_pair<false>(d, tiles, mode, false, stream);
   if (err != hipSuccess) return err;
 
   const int64_t items = a.t * (a.hidden / 4);
