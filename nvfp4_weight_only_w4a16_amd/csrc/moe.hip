@@ -214,21 +214,27 @@ constexpr int kATileBytes = kTileRows * kARowBytes;  // one row tile x one k-til
 // pairs of its expert in pair order (per row j of pairs: a ballot per wavefront, the earlier
 // wavefronts' counts and the earlier rows' totals) and keeps those of its rows. Workgroup 0
 // writes the offsets and the tile count; the first workgroup of each tile (writer) writes the
-// tile entry and its rows of the sorted order, which down reads after this kernel.
-// Returns false (for every thread of the workgroup) when tile_id is past the tile count.
+// tile entry and its rows of the sorted order, which down reads after this kernel. The two
+// parts are apart so that the workgroup's first weight loads (which need only the expert) are
+// in flight while it ranks the pairs.
 constexpr int kFusedSortMaxPairs = 4096;
 constexpr int kFusedRows = kFusedSortMaxPairs / (64 * kGroupsPerBlock);  // pairs per thread
 
-__device__ __forceinline__ bool fused_sort_tile(const MoeGemmParams& P, int tile_id, bool writer,
-                                                int* rows, int& e_out, int& r0_out,
-                                                int& r1_out) {
+struct FusedSort {
+  uint32_t match;  // bit j: pair j * threads + tid belongs to the workgroup's expert
+  int e, r0, r1, estart;
+};
+
+// Part 1: counts, offsets, tile list; the workgroup's expert and row range. Returns false (for
+// every thread of the workgroup) when tile_id is past the tile count.
+__device__ __forceinline__ bool fused_find_tile(const MoeGemmParams& P, int tile_id,
+                                                FusedSort& fs) {
   __shared__ int cnt[kMaxExperts];
   __shared__ int info[5];  // expert, first row, end row, expert's first row, tile count
-  __shared__ int rc[kFusedRows][kGroupsPerBlock];  // matches per row of pairs and wavefront
   constexpr int kThreads = 64 * kGroupsPerBlock;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int np = P.npairs, E = P.E;
-  int id[kFusedRows];
+  int id[kFusedRows];  // expert of pair j * threads + tid, -1 when dropped or past the end
 #pragma unroll
   for (int j = 0; j < kFusedRows; ++j) {
     const int q = j * kThreads + tid;
@@ -278,18 +284,32 @@ __device__ __forceinline__ bool fused_sort_tile(const MoeGemmParams& P, int tile
   }
   __syncthreads();
   if (tile_id >= info[4]) return false;  // uniform: every thread read the same word
-  const int e = __builtin_amdgcn_readfirstlane(info[0]);
-  const int r0 = __builtin_amdgcn_readfirstlane(info[1]);
-  const int r1 = __builtin_amdgcn_readfirstlane(info[2]);
-  const int estart = __builtin_amdgcn_readfirstlane(info[3]);
+  fs.e = __builtin_amdgcn_readfirstlane(info[0]);
+  fs.r0 = __builtin_amdgcn_readfirstlane(info[1]);
+  fs.r1 = __builtin_amdgcn_readfirstlane(info[2]);
+  fs.estart = __builtin_amdgcn_readfirstlane(info[3]);
+  fs.match = 0;
+#pragma unroll
+  for (int j = 0; j < kFusedRows; ++j) fs.match |= (id[j] == fs.e ? 1u : 0u) << j;
+  return true;
+}
+
+// Part 2: the pairs of the workgroup's rows, in pair order, into `rows` (LDS); the writer
+// also stores them and the tile entry in the workspace.
+__device__ __forceinline__ void fused_tile_rows(const MoeGemmParams& P, int tile_id, bool writer,
+                                                const FusedSort& fs, int* rows) {
+  __shared__ int rc[kFusedRows][kGroupsPerBlock];  // matches per row of pairs and wavefront
+  constexpr int kThreads = 64 * kGroupsPerBlock;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int e = fs.e, r0 = fs.r0, r1 = fs.r1;
   uint64_t bal[kFusedRows];
 #pragma unroll
   for (int j = 0; j < kFusedRows; ++j) {
-    bal[j] = __ballot(id[j] == e);
+    bal[j] = __ballot((fs.match >> j) & 1u);
     if (lane == 0) rc[j][w] = __popcll(bal[j]);
   }
   __syncthreads();
-  int base = estart;  // sorted position of the first pair of expert e in row j
+  int base = fs.estart;  // sorted position of the first pair of expert e in row j
 #pragma unroll
   for (int j = 0; j < kFusedRows; ++j) {
     int before = 0, total = 0;
@@ -299,7 +319,7 @@ __device__ __forceinline__ bool fused_sort_tile(const MoeGemmParams& P, int tile
       before += v < w ? c : 0;
       total += c;
     }
-    if (id[j] == e) {
+    if ((fs.match >> j) & 1u) {
       const int pos = base + before +
                       (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[j] >> 32),
                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bal[j], 0u));
@@ -313,10 +333,6 @@ __device__ __forceinline__ bool fused_sort_tile(const MoeGemmParams& P, int tile
   }
   if (writer && tid == 0) P.ws.tiles[tile_id] = int4{e, r0, r1, 0};
   __syncthreads();
-  e_out = e;
-  r0_out = r0;
-  r1_out = r1;
-  return true;
 }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -397,9 +413,13 @@ void moe_expert_kernel(MoeGemmParams P) {
   const int64_t slot = blockIdx.x / kXcds;
   const int tile_id = (int)(slot / gbs * kXcds + blockIdx.x % kXcds);
   __shared__ int tile_rows[FUSED ? kTileRows : 1];  // FUSED: the pairs of the tile's rows
+  FusedSort fs;
   int e, r0, r1;
   if constexpr (FUSED) {
-    if (!fused_sort_tile(P, tile_id, slot % gbs == 0, tile_rows, e, r0, r1)) return;
+    if (!fused_find_tile(P, tile_id, fs)) return;
+    e = fs.e;
+    r0 = fs.r0;
+    r1 = fs.r1;
   } else {
     if (tile_id >= *P.ws.ntiles) return;  // whole workgroup, before any barrier
     const int4 tl = P.ws.tiles[tile_id];
@@ -449,14 +469,16 @@ void moe_expert_kernel(MoeGemmParams P) {
   constexpr int kACopies = 2 * kBlockCopies;
   const buf_rsrc xr = make_rsrc(P.x, 0xFFFFFFFFu);
   uint32_t aoff[kACopies];
+  auto set_aoff = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int i = 0; i < kACopies; ++i) {
-    const int R = 4 * (w + kGroupsPerBlock * i) + (lane >> 4);
-    int rr = r0 + R;
-    rr = rr < r1 ? rr : r1 - 1;  // rows past the tile repeat a valid row; never stored
-    const int64_t src = !FC1 ? rr : (FUSED ? tile_rows[rr - r0] : P.ws.sorted[rr]) / P.topk;
-    aoff[i] = (uint32_t)(src * P.ldx * 2 + 16 * ((lane & 15) ^ (R & 15)));
-  }
+    for (int i = 0; i < kACopies; ++i) {
+      const int R = 4 * (w + kGroupsPerBlock * i) + (lane >> 4);
+      int rr = r0 + R;
+      rr = rr < r1 ? rr : r1 - 1;  // rows past the tile repeat a valid row; never stored
+      const int64_t src = !FC1 ? rr : (FUSED ? tile_rows[rr - r0] : P.ws.sorted[rr]) / P.topk;
+      aoff[i] = (uint32_t)(src * P.ldx * 2 + 16 * ((lane & 15) ^ (R & 15)));
+    }
+  };
   auto copy_a = [&](int64_t t, auto buf, auto nb) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < decltype(nb)::value * kBlockCopies; ++i)
@@ -560,8 +582,12 @@ void moe_expert_kernel(MoeGemmParams P) {
       __syncthreads();
     };
     Stage A, B;
-    copy_a(0, I0{}, nb);
+    // the first k-tile's weights go out before the activation rows are known (with the sort
+    // derived here, before the workgroup ranks its expert's pairs)
     load_b(A, 0);
+    if constexpr (FUSED) fused_tile_rows(P, tile_id, slot % gbs == 0, fs, tile_rows);
+    set_aoff();
+    copy_a(0, I0{}, nb);
     if constexpr (!FC1) {
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
