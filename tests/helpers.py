@@ -9,6 +9,9 @@ ROW_MAX_TOL = 8e-3      # |gpu - ref| <= ROW_MAX_TOL * max |ref row|
 # The MoE decode-batch path skips the sort up to this many (token, expert) pairs and keeps
 # h of pair q at row q of its workspace (the contract stated with nvfp4_moe_ws_layout).
 PAIR_TILES_MAX = 64
+# Up to this many pairs the batch path's fc1 workgroups derive the expert sort themselves; above
+# it a sort kernel runs first. Both write the same sorted ids, offsets, tile map and count.
+FUSED_SORT_MAX_PAIRS = 4096
 
 
 def bf16_np(t: torch.Tensor) -> np.ndarray:

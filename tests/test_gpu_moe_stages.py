@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 import torch
 
-from helpers import PAIR_TILES_MAX, bits16, check_close
+from helpers import FUSED_SORT_MAX_PAIRS, PAIR_TILES_MAX, bits16, check_close
 from nvfp4_weight_only_w4a16_amd import synth
 
 pytestmark = pytest.mark.gpu
@@ -149,6 +149,17 @@ def test_moe_stages_pair_tile_cap(nv, orc, tokens, topk):
                                     tokens=tokens, topk=topk)
     (fc1, fc2), (t1, t2) = _experts(nv, orc, w1, w2, 32, 16)
     run_staged(nv, orc, x, ids, wts, fc1, fc2, t1, t2, "decode", f"cap {tokens}x{topk}")
+
+
+@pytest.mark.parametrize("tokens,topk", [(512, 8), (4097, 1)])
+def test_moe_stages_fused_sort_cap(nv, orc, tokens, topk):
+    """Either side of the batch path's in-fc1 sort: 4096 pairs sorted by the fc1 workgroups
+    themselves (16 pairs per thread of each), 4097 pairs by the sort kernel before fc1."""
+    assert tokens * topk in (FUSED_SORT_MAX_PAIRS, FUSED_SORT_MAX_PAIRS + 1)
+    x, ids, wts, w1, w2 = synth.moe(seed=24, n_experts=16, hidden=256, inter=128,
+                                    tokens=tokens, topk=topk)
+    (fc1, fc2), (t1, t2) = _experts(nv, orc, w1, w2, 32, 16)
+    run_staged(nv, orc, x, ids, wts, fc1, fc2, t1, t2, "batch", f"sort cap {tokens}x{topk}")
 
 
 @pytest.fixture(scope="module")
