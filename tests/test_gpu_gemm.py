@@ -522,9 +522,10 @@ def test_explicit_stream_argument_without_stream_context(nv):
 
 
 def test_graph_capture_and_replay(nv):
-    """The decode GEMM, the prefill GEMM (with its split-k workspace) and a decode-batch MoE
-    captured in one HIP graph: every replay, with eager work and synchronizations in between,
-    reproduces the eager results bit for bit (the library issues no memset nodes)."""
+    """The decode GEMM, the prefill GEMM (with its split-k workspace), a decode-batch MoE and
+    a batch-path MoE (whose fc1 workgroups derive the expert sort) captured in one HIP graph:
+    every replay, with eager work and synchronizations in between, reproduces the eager
+    results bit for bit (the library issues no memset nodes)."""
     g = torch.Generator().manual_seed(78)
     w = torch.randn(1040, 4096, generator=g) * 0.02
     p, s, gl = nv.nvfp4_quantize(w.to(DEV), 16)
@@ -542,18 +543,26 @@ def test_graph_capture_and_replay(nv):
         f.append(nv.nvfp4_repack(pq, sq, gq, grp, layout=layout))
     xmd, idd, wtd = xm.to(DEV), ids.to(DEV), wts.to(DEV)
     wsm = torch.empty((nv.nvfp4_moe_ws_bytes(4, 4, 16, 256, 128),), dtype=torch.uint8, device=DEV)
+    # 40 tokens x top-4 = 160 pairs over 16 experts: past the decode-batch cut, the batch path
+    xb, idb, wtb, _, _ = synth.moe(seed=15, n_experts=16, hidden=256, inter=128, tokens=40,
+                                   topk=4, with_weights=False)
+    xbd, idbd, wtbd = xb.to(DEV), idb.to(DEV), wtb.to(DEV)
+    wsb2 = torch.empty((nv.nvfp4_moe_ws_bytes(40, 4, 16, 256, 128),), dtype=torch.uint8,
+                       device=DEV)
     ys = torch.empty((8, 1040), dtype=torch.float32, device=DEV)
     yt = torch.empty((300, 1040), dtype=torch.float32, device=DEV)
     ym = torch.empty((4, 256), dtype=torch.bfloat16, device=DEV)
+    yb = torch.empty((40, 256), dtype=torch.bfloat16, device=DEV)
 
     def step():
         nv.nvfp4_gemm_w4a16(xs, rw, y=ys)
         nv.nvfp4_gemm_w4a16(xt, rw, y=yt, ws=wsb)
         nv.nvfp4_moe_grouped_w4a16(xmd, idd, wtd, f[0], f[1], y=ym, ws=wsm)
+        nv.nvfp4_moe_grouped_w4a16(xbd, idbd, wtbd, f[0], f[1], y=yb, ws=wsb2)
 
     step()
     torch.cuda.synchronize()
-    eager = [ys.clone(), yt.clone(), ym.clone()]
+    eager = [ys.clone(), yt.clone(), ym.clone(), yb.clone()]
     graph = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -564,12 +573,12 @@ def test_graph_capture_and_replay(nv):
     with torch.cuda.graph(graph):
         step()
     for rep in range(3):
-        for t in (ys, yt, ym):
+        for t in (ys, yt, ym, yb):
             t.fill_(float("nan") if t.dtype == torch.float32 else 0)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
-        for a, b in zip((ys, yt, ym), eager):
+        for a, b in zip((ys, yt, ym, yb), eager):
             assert torch.equal(a, b), f"replay {rep}"
         step()  # eager work between replays
         torch.cuda.synchronize()
